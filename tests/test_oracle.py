@@ -1,0 +1,305 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-worked examples, brute force with a different formula, closed forms, special
+cases that reduce to library routines (torch SDPA, logsumexp), and invariants
+(dense equality for short contexts, independence from the slice count P).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_qsa_amd.inputs import Workload, make_inputs
+from tests.helpers import oracle_arrays, oracle_decode
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "handworked_indexer.json")
+
+
+# ----------------------------------------------------------------- golden, hand-worked
+
+def _golden_case(case):
+    idx = np.full((case["num_pages"], 64, 4, 64), case["filler"], dtype=np.int8)
+    pt = np.array(case["page_table"], dtype=np.int32)
+    L = case["length"]
+    logical = np.zeros((len(pt) * 64, 4, 64), dtype=np.int8)
+    for t, h, d, v in case.get("key_entries", []):
+        logical[t, h, d] = v
+    rule = case.get("key_entries_rule")
+    if rule:
+        logical[rule["tokens"][0]: rule["tokens"][1], rule["head"], rule["dim"]] = rule["value"]
+    logical[L:] = 127
+    for p, phys in enumerate(pt):
+        idx[phys] = logical[p * 64:(p + 1) * 64]
+    q_idx = np.zeros((4, 64), dtype=np.int8)
+    for h, d, v in case["q_idx"]:
+        q_idx[h, d] = v
+    return q_idx, idx, pt, L
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_golden_scores_and_selection(case):
+    q_idx, idx, pt, L = _golden_case(case)
+    s = oracle.index_scores(q_idx, idx, pt, L)
+    assert s.tolist() == case["scores"]
+    for k, kept in case["kept"].items():
+        assert oracle.select_blocks(s, int(k)).tolist() == kept
+    if "tokens_k2" in case:
+        assert oracle.kept_tokens(oracle.select_blocks(s, 2), L).tolist() == case["tokens_k2"]
+
+
+def test_golden_attention_mean_of_kept_values():
+    g = json.load(open(GOLDEN))
+    case = g["cases"][0]
+    q_idx, idx, pt, L = _golden_case(case)
+    kc = np.full((idx.shape[0], 64, 1, 128), np.nan)
+    vc = np.full((idx.shape[0], 64, 1, 128), np.nan)
+    kc[pt[0], :L] = 0.0
+    vc[pt[0], :L] = 0.0
+    vc[pt[0], :L, 0, 0] = np.arange(L)
+    vc[pt[0], :L, 0, 1] = 1.0
+    q = np.zeros((2, 128))
+    q[0, 0], q[1, 3] = 1.0, -2.0
+    for k, ref, n in ((2, g["attention"]["k2"], 6), (512, g["attention"]["k512"], 10)):
+        r = oracle.decode_request(q, q_idx, idx, kc, vc, pt, L, P=2, scale=1 / math.sqrt(128), k=k)
+        for h in range(2):
+            assert r["out"][h, 0] == pytest.approx(ref["mean_dim0"], abs=1e-14)
+            assert r["out"][h, 1] == pytest.approx(ref["mean_dim1"], abs=1e-14)
+            assert np.all(r["out"][h, 2:] == 0.0)
+            assert r["lse"][h] == pytest.approx(math.log(n), abs=1e-14)
+        assert r["ranges"] == [tuple(x) for x in g["attention"]["slices_P2"]["ranges"]]
+        assert np.all(r["o_part"][1] == 0) and np.all(np.isneginf(r["lse_part"][1]))
+
+
+# ------------------------------------------------------------ indexer: brute force
+
+def _brute_scores(q_idx, idx_cache, page_table_row, L):
+    """Per-token dot products summed over each block: a different formula from
+    pool-then-dot, equal to it by distributivity of integer arithmetic."""
+    qi = [[int(v) for v in row] for row in q_idx]
+    out = []
+    for j in range((L + 3) // 4):
+        total = 0
+        for t in range(4 * j, min(4 * j + 4, L)):
+            row = idx_cache[int(page_table_row[t // 64]), t % 64]
+            for h in range(4):
+                total += sum(qi[h][d] * int(row[h, d]) for d in range(64))
+        out.append(total)
+    return out
+
+
+@pytest.mark.parametrize("lens", [(1, 3), (5, 64), (65, 130), (257, 200)])
+def test_scores_brute_force(lens):
+    w = Workload("t", len(lens), ("list",) + tuple(lens), 16, 2, 1)
+    x = make_inputs(w, seed=11)
+    a = oracle_arrays(x)
+    for b, L in enumerate(lens):
+        got = oracle.index_scores(a["q_idx"][b], a["idx_cache"], a["page_table"][b], L)
+        assert got.tolist() == _brute_scores(a["q_idx"][b], a["idx_cache"], a["page_table"][b], L)
+
+
+def test_scores_closed_form_constant_keys():
+    c, e, L = -7, 3, 10
+    idx = np.full((1, 64, 4, 64), c, dtype=np.int8)
+    idx[0, L:] = 127
+    q_idx = np.full((4, 64), e, dtype=np.int8)
+    s = oracle.index_scores(q_idx, idx, np.array([0]), L)
+    n_valid = [4, 4, 2]
+    assert s.tolist() == [n * c * e * 256 for n in n_valid]
+
+
+def test_scores_zero_query_and_planted_block():
+    rng = np.random.default_rng(3)
+    idx = rng.integers(-127, 128, size=(2, 64, 4, 64), dtype=np.int8)
+    q0 = np.zeros((4, 64), dtype=np.int8)
+    assert np.all(oracle.index_scores(q0, idx, np.array([1, 0]), 100) == 0)
+    q = rng.integers(-127, 128, size=(4, 64), dtype=np.int8)
+    idx[1, 8:12] = q          # logical page 0 is physical page 1: block 2 planted
+    s = oracle.index_scores(q, idx, np.array([1, 0]), 100)
+    assert s[2] == 4 * int((q.astype(np.int64) ** 2).sum())
+
+
+def test_score_extremes_fit_int32():
+    idx = np.full((1, 64, 4, 64), -128, dtype=np.int8)
+    q = np.full((4, 64), -128, dtype=np.int8)
+    assert oracle.index_scores(q, idx, np.array([0]), 64)[0] == 4 * 256 * 128 * 128
+
+
+# ------------------------------------------------------------------------ selection
+
+def _brute_select(scores, k):
+    """Selection sort: repeatedly take the highest remaining score, lowest index first."""
+    left = list(range(len(scores)))
+    kept = []
+    for _ in range(min(k, len(scores))):
+        best = left[0]
+        for j in left:
+            if scores[j] > scores[best]:
+                best = j
+        kept.append(best)
+        left.remove(best)
+    return sorted(kept)
+
+
+def test_select_all_ties_keeps_lowest_indices():
+    assert oracle.select_blocks(np.zeros(1000, dtype=np.int64)).tolist() == list(range(512))
+
+
+def test_select_monotone_scores_pin_direction():
+    inc = np.arange(2000, dtype=np.int64)
+    assert oracle.select_blocks(inc).tolist() == list(range(1488, 2000))
+    assert oracle.select_blocks(-inc).tolist() == list(range(512))
+
+
+def test_select_keeps_everything_when_few_blocks():
+    s = np.random.default_rng(0).integers(-5, 5, 300)
+    assert oracle.select_blocks(s).tolist() == list(range(300))
+
+
+@pytest.mark.parametrize("n,k,span", [(513, 512, 3), (700, 7, 4), (1500, 512, 50), (900, 1, 2)])
+def test_select_brute_force_with_ties(n, k, span):
+    s = np.random.default_rng(n + k).integers(-span, span + 1, n)
+    assert oracle.select_blocks(s, k).tolist() == _brute_select(s.tolist(), k)
+
+
+def test_select_finds_planted_blocks():
+    w = Workload("t", 2, ("fixed", 8192), 16, 2, 2, paging="identity", planted=512)
+    x = make_inputs(w, seed=5)
+    a = oracle_arrays(x)
+    for b in range(2):
+        s = oracle.index_scores(a["q_idx"][b], a["idx_cache"], a["page_table"][b], 8192)
+        assert oracle.select_blocks(s).tolist() == x.planted[b]
+
+
+# ------------------------------------------------------------------------ attention
+
+def _sdpa(q, k_rows, v_rows, scale):
+    """torch SDPA in float64 on the CPU, K/V repeated per query-head group."""
+    Hq = q.shape[0]
+    group = Hq // k_rows.shape[1]
+    kt = torch.from_numpy(k_rows).permute(1, 0, 2).repeat_interleave(group, 0)[None]
+    vt = torch.from_numpy(v_rows).permute(1, 0, 2).repeat_interleave(group, 0)[None]
+    qt = torch.from_numpy(q)[None, :, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, :, 0]
+    lse = torch.logsumexp(torch.einsum("hd,htd->ht", torch.from_numpy(q), kt[0]) * scale, dim=1)
+    return o.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("L", [1, 5, 100, 2047, 2048])
+def test_short_context_equals_dense_attention(L):
+    w = Workload("t", 1, ("list", L), 32, 4, 4)
+    x = make_inputs(w, seed=L)
+    r = oracle_decode(oracle, x)[0]
+    assert len(r["kept"]) == (L + 3) // 4          # every block kept
+    a = oracle_arrays(x)
+    kr = oracle.bf16_to_f64(oracle.request_rows(a["k_cache"], a["page_table"][0], L))
+    vr = oracle.bf16_to_f64(oracle.request_rows(a["v_cache"], a["page_table"][0], L))
+    o, lse = _sdpa(oracle.bf16_to_f64(a["q"][0]), kr, vr, x.scale)
+    np.testing.assert_allclose(r["out"], o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, rtol=0, atol=1e-12)
+
+
+def test_single_token_output_is_its_value():
+    x = make_inputs(Workload("t", 1, ("list", 1), 16, 2, 3), seed=2)
+    a = oracle_arrays(x)
+    r = oracle_decode(oracle, x)[0]
+    v0 = oracle.bf16_to_f64(a["v_cache"][a["page_table"][0, 0], 0])
+    k0 = oracle.bf16_to_f64(a["k_cache"][a["page_table"][0, 0], 0])
+    q = oracle.bf16_to_f64(a["q"][0])
+    for h in range(16):
+        assert np.array_equal(r["out"][h], v0[h // 8])
+        assert r["lse"][h] == pytest.approx(float(q[h] @ k0[h // 8]) * x.scale, abs=1e-12)
+
+
+def test_identical_keys_give_mean_of_values():
+    L, T = 37, 37
+    kc = np.tile(np.linspace(-1, 1, 128), (1, 64, 2, 1))
+    vc = np.random.default_rng(1).standard_normal((1, 64, 2, 128))
+    idx = np.zeros((1, 64, 4, 64), dtype=np.int8)
+    q = np.random.default_rng(2).standard_normal((16, 128))
+    r = oracle.decode_request(q, np.zeros((4, 64), np.int8), idx, kc, vc, np.array([0]), L, 2, 0.1)
+    for h in range(16):
+        np.testing.assert_allclose(r["out"][h], vc[0, :T, h // 8].mean(axis=0), atol=1e-13)
+        assert r["lse"][h] == pytest.approx(0.1 * float(q[h] @ kc[0, 0, h // 8]) + math.log(T), abs=1e-12)
+
+
+# ------------------------------------------------------------------- slices & merge
+
+def test_slice_ranges_table():
+    assert oracle.slice_ranges(1000, 3, 64) == [(0, 384), (384, 768), (768, 1000)]
+    assert oracle.slice_ranges(64, 4, 64) == [(0, 64), (64, 64), (64, 64), (64, 64)]
+    assert oracle.slice_ranges(4096, 1, 64) == [(0, 4096)]
+    assert oracle.slice_ranges(0, 2, 64) == [(0, 0), (0, 0)]
+    assert oracle.slice_ranges(130, 2, 64) == [(0, 128), (128, 130)]
+
+
+def test_partials_are_dense_attention_of_each_slice():
+    x = make_inputs(Workload("t", 1, ("list", 5000), 32, 4, 3), seed=9)
+    r = oracle_decode(oracle, x)[0]
+    a = oracle_arrays(x)
+    kr = oracle.bf16_to_f64(oracle.request_rows(a["k_cache"], a["page_table"][0], 5000))
+    vr = oracle.bf16_to_f64(oracle.request_rows(a["v_cache"], a["page_table"][0], 5000))
+    q = oracle.bf16_to_f64(a["q"][0])
+    for p, (lo, hi) in enumerate(r["ranges"]):
+        t = r["tokens"][(r["tokens"] >= lo) & (r["tokens"] < hi)]
+        o, lse = _sdpa(q, kr[t], vr[t], x.scale)
+        np.testing.assert_allclose(r["o_part"][p], o, atol=1e-12)
+        np.testing.assert_allclose(r["lse_part"][p], lse, atol=1e-12)
+
+
+def test_merge_independent_of_slice_count():
+    x = make_inputs(Workload("t", 2, ("list", 5000, 3001), 32, 4, 1), seed=4)
+    base = oracle_decode(oracle, x, P=1)
+    for b in range(2):
+        assert np.array_equal(base[b]["o_part"][0], base[b]["out"])
+    for P in range(2, 9):
+        r = oracle_decode(oracle, x, P=P)
+        for b in range(2):
+            np.testing.assert_allclose(r[b]["out"], base[b]["out"], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(r[b]["lse"], base[b]["lse"], rtol=0, atol=1e-12)
+            assert r[b]["kept"].tolist() == base[b]["kept"].tolist()
+
+
+def test_merge_order_and_empty_slices():
+    rng = np.random.default_rng(8)
+    o = rng.standard_normal((4, 8, 128))
+    lse = rng.standard_normal((4, 8)) * 3
+    lse[2, :3] = -np.inf
+    o[2, :3] = 0
+    ref_o, ref_l = oracle.lse_merge(o, lse)
+    perm = [3, 0, 2, 1]
+    o2, l2 = oracle.lse_merge(o[perm], lse[perm])
+    np.testing.assert_allclose(o2, ref_o, atol=1e-14)
+    np.testing.assert_allclose(l2, ref_l, atol=1e-14)
+    o3, l3 = oracle.lse_merge(np.concatenate([o, np.zeros((1, 8, 128))]),
+                              np.concatenate([lse, np.full((1, 8), -np.inf)]))
+    np.testing.assert_allclose(o3, ref_o, atol=1e-14)
+    np.testing.assert_allclose(l3, ref_l, atol=1e-14)
+
+
+def test_merged_lse_is_logsumexp_of_all_kept_scores():
+    from scipy.special import logsumexp
+    x = make_inputs(Workload("t", 1, ("list", 7777), 16, 2, 4), seed=12)
+    r = oracle_decode(oracle, x)[0]
+    a = oracle_arrays(x)
+    kr = oracle.bf16_to_f64(oracle.request_rows(a["k_cache"], a["page_table"][0], 7777))
+    q = oracle.bf16_to_f64(a["q"][0])
+    for h in range(16):
+        s = kr[r["tokens"], h // 8] @ q[h] * x.scale
+        assert r["lse"][h] == pytest.approx(logsumexp(s), abs=1e-12)
+
+
+def test_empty_request():
+    r = oracle.decode_request(np.zeros((16, 128)), np.ones((4, 64), np.int8),
+                              np.zeros((1, 64, 4, 64), np.int8), np.zeros((1, 64, 2, 128)),
+                              np.zeros((1, 64, 2, 128)), np.array([0]), 0, 2, 0.1)
+    assert r["kept"].size == 0 and r["tokens"].size == 0
+    assert np.all(r["out"] == 0) and np.all(np.isneginf(r["lse"]))
+
+
+def test_poisoned_rows_never_reach_the_result():
+    x = make_inputs(Workload("t", 3, ("list", 63, 129, 2500), 16, 2, 3), seed=21)
+    for r in oracle_decode(oracle, x):
+        assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
