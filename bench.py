@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the QSA decode path on one MI355X.
+
+One step = one call of the whole path (indexer scan + pooling + scores -> top-512
+selection -> paged gather + attention per slice -> LSE merge) for one decode token of
+every request of the batch, launched as qsa_decode on one stream. Inputs are resident
+in HBM before timing starts. Default workload: w4, the 256K-context batch (B=4, lengths
+uniform in [65536, 262144] drawn with seed 0, Hq/Hkv=32/4, head_dim 128, shuffled 64-token
+pages, P=4 slices).
+
+Prints one JSON line. `value` is decode calls/s; it also reports the algorithmic GB/s of
+the whole call, a roofline entry for the dominant kernel (the indexer scan, timed on its
+own with HIP events on the stream it runs on) and the CPU oracle's rate on the same
+workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload w4] [--sets R] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QSA decode attn calls/s and achieved HBM GB/s (% peak) at 256K ctx, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+IDX_TOKEN_BYTES = 256
+
+
+def algorithmic_bytes(lengths, hq, hkv, k=512):
+    """Bytes the method must move per call (intermediates excluded).
+
+    per request: 256*L (indexer keys) + 256 (q_idx) + 4*ceil(L/64) (page table)
+                 + |T|*Hkv*512 (kept K and V rows) + 256*Hq (q, bf16) + 512*Hq (out, fp32)
+    with |T| = number of kept token positions.
+    """
+    total = 0
+    for L in lengths:
+        nblk = (L + 3) // 4
+        K = min(k, nblk)
+        T = min(4 * K, L)                 # exact when the tail block is kept; <= 3 high otherwise
+        total += IDX_TOKEN_BYTES * L + 256 + 4 * ((L + 63) // 64) + T * hkv * 512 + 256 * hq + 512 * hq
+    return total
+
+
+def index_bytes(lengths):
+    """Algorithmic bytes of the indexer scan: keys + q_idx + page table + block scores written."""
+    return sum(IDX_TOKEN_BYTES * L + 256 + 4 * ((L + 63) // 64) + 4 * ((L + 3) // 4) for L in lengths)
+
+
+def kept_tokens_exact(sel, lengths):
+    """|T_b| from the kept block ids (tail block counted with its valid tokens only)."""
+    import numpy as np
+    total = 0
+    for b, L in enumerate(lengths):
+        s = sel[b][sel[b] >= 0]
+        toks = (s[:, None] * 4 + np.arange(4)[None]).reshape(-1)
+        total += int((toks < L).sum())
+    return total
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The CPU oracle, as it stands, on the same batch (host copies of set 0), one thread."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from sparse_attention_decode_qsa_amd.inputs import bf16_bits
+
+    a = dict(q=bf16_bits(x.q), q_idx=x.q_idx.cpu().numpy(), idx=x.idx_cache.cpu().numpy(),
+             k=bf16_bits(x.k_cache), v=bf16_bits(x.v_cache), pt=x.page_table.cpu().numpy())
+    calls, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        while t_total < budget_s:
+            t0 = time.perf_counter()
+            oracle.decode(a["q"], a["q_idx"], a["idx"], a["k"], a["v"], a["pt"], x.lengths,
+                          x.workload.slices, x.scale)
+            t_total += time.perf_counter() - t0
+            calls += 1
+    return {"value": calls / t_total, "unit": "calls/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full calls on the benchmarked batch (all {x.batch} requests, input set 0), "
+                      f"numpy float64/int64 on one host thread, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="w4")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_decode_qsa_amd import qsa
+    from sparse_attention_decode_qsa_amd.inputs import WORKLOADS, draw_lengths, make_inputs
+
+    w = WORKLOADS[args.workload]
+    lengths = draw_lengths(w, args.seed)
+    wl = w.with_(lengths=("list",) + tuple(lengths))   # every rotated set keeps seed-0 lengths
+    idx_bytes_per_set = IDX_TOKEN_BYTES * sum(lengths)
+    sets = args.sets or max(1, min(16, math.ceil((1 << 30) / max(idx_bytes_per_set, 1))))
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    plans, inputs = [], []
+    for r in range(sets):
+        x = make_inputs(wl, args.seed + 1000 * r, dev)
+        inputs.append(x)
+        plans.append(qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
+                                    x.context_lens, w.slices))
+    torch.cuda.synchronize()
+    print(f"# workload {args.workload}: B={len(lengths)} lengths={lengths[:8]}{'...' if len(lengths) > 8 else ''} "
+          f"sets={sets}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    # ---- whole path
+    for i in range(args.warmup):
+        plans[i % sets].run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        plans[i % sets].run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- the dominant kernel alone (indexer scan), same stream, same inputs
+    k_iters = max(args.steps, 100)
+    for i in range(10):
+        x = inputs[i % sets]
+        qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(k_iters):
+        x = inputs[i % sets]
+        qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_k1 = e0.elapsed_time(e1) / k_iters
+
+    sel = plans[0].sel.cpu().numpy()
+    T_exact = kept_tokens_exact(sel, lengths)
+    algo = algorithmic_bytes(lengths, w.hq, w.hkv)
+    # replace the |T| upper bound by the exact kept count of set 0
+    algo += (T_exact - sum(min(4 * min(512, (L + 3) // 4), L) for L in lengths)) * w.hkv * 512
+    gbs = algo / (ms_step * 1e-3) / 1e9
+    k1_bytes = index_bytes(lengths)
+    k1_gbs = k1_bytes / (ms_k1 * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: B={len(lengths)}, L={lengths}, Hq/Hkv={w.hq}/{w.hkv}, head_dim=128, "
+                        f"indexer 4x64 int8, page=64 shuffled, top-512 blocks of 4, P={w.slices}, seed {args.seed}",
+            "global_batch": len(lengths),
+            "seq_len": max(lengths),
+            "parallelism": f"1 GPU, P={w.slices} slices merged by LSE",
+            "rotated_input_sets": sets,
+        },
+        "achieved_GBps": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_call": algo,
+        "roofline": {
+            "kernel": "index_score_kernel (indexer scan + pooling + scores)",
+            "bound": "hbm",
+            "achieved": round(k1_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(ms_k1 * 1000, 3),
+            "bytes_per_launch": k1_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on the same workload", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inputs[0])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * qsa.h - C ABI of libqsa, the QSA (Qwen Sparse Attention) decode path on AMD gfx950.
+ *
+ * The method, as the article "Qwen 4 QSA gets decode context parallelism: inside vLLM's
+ * draft PR for Qwen3.8-Flash-Next" (orcarouter.ai blog) describes it:
+ *   - section "What the pull request actually changes", second paragraph: a light
+ *     indexer compresses the keys into micro-blocks of 4 tokens and scores them; the 512
+ *     best blocks (about 2,048 positions) are kept; the final softmax and the value
+ *     aggregation run on the uncompressed K and V.
+ *   - same section, first paragraph and bullets, and section "Questions worth answering
+ *     directly" (DCP versus TP): each decode-context-parallel rank reads only its slice of
+ *     the context and the partial attention results are combined afterwards. Here the P
+ *     slices of one request are read on one GPU and merged by log-sum-exp.
+ *
+ * One decode step of one QSA layer is the chain
+ *     qsa_index_score -> qsa_topk_select -> qsa_sparse_attn_decode -> qsa_lse_merge
+ * (or qsa_decode, which runs the four on one stream).
+ *
+ * Conventions for every entry point
+ *   Memory     every pointer is device memory of the current HIP device, unless noted.
+ *              The caller owns every buffer. The library allocates no device memory and
+ *              keeps no pointer, view or handle after a call returns.
+ *   Streams    `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *              work and return; they never synchronize. Buffers must stay alive until the
+ *              stream has passed the work. Inputs are read-only; outputs must not alias
+ *              inputs.
+ *   Layouts    row-major, densely packed, base pointers 16-byte aligned.
+ *              indexer keys  idx_cache  [num_pages, page_size, n_idx_heads, idx_dim] int8
+ *              keys, values  k_cache, v_cache [num_pages, page_size, Hkv, head_dim] bf16
+ *              page table    page_table [B, max_pages_per_seq] int32 (physical page ids)
+ *              lengths       context_lens [B] int32, 0 <= L_b <= max_pages_per_seq*page_size
+ *              Token t of request b lives in page page_table[b][t / page_size], row
+ *              t % page_size, in all three caches (one page table for the indexer keys
+ *              and K/V: the article's "one cache group" bullet).
+ *   Compiled   page_size 64, n_idx_heads 4, idx_dim 64, head_dim 128, Hq/Hkv <= 16,
+ *              k <= 512. Other values return QSA_ERR_UNSUPPORTED.
+ *   Errors     arguments visible on the host are checked before anything is enqueued;
+ *              a failing check returns its code and launches nothing. Launch failures
+ *              return QSA_ERR_HIP (see qsa_last_hip_error). Device-side preconditions
+ *              (page ids in range, lengths within the page table) are the caller's and
+ *              are not checked. No C++ exception crosses this interface.
+ *   Workspace  entry points that take a workspace need qsa_*_workspace_size() bytes,
+ *              16-byte aligned. A workspace must be filled with zero bytes once before its
+ *              first use (hipMemset or qsa_workspace_clear); every call leaves the parts
+ *              it used at zero again, so no per-call clearing is needed. Calls that share
+ *              a workspace must not overlap in time.
+ *   Threads    stateless and re-entrant apart from the thread-local qsa_last_hip_error.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  QSA_ERR_SHAPE = 2,        /* sizes are negative or inconsistent                  */
+  QSA_ERR_UNSUPPORTED = 3,  /* a size outside what the kernels are compiled for    */
+  QSA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required          */
+  QSA_ERR_HIP = 5           /* the HIP runtime reported an error                   */
+} qsa_status_t;
+
+/* Static description of a status code; never NULL. */
+const char* qsa_status_string(int status);
+
+/* hipError_t of the last HIP failure seen by this thread (0 if none). */
+int qsa_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int qsa_version(void);
+
+/*
+ * qsa_index_score - indexer scan, micro-block pooling and block scoring.
+ *
+ * Article, section "What the pull request actually changes", second paragraph: the
+ * indexer compresses keys into micro-blocks of 4 tokens and scores them. With the
+ * compiled shapes, for request b of length L_b and block j < ceil(L_b/4):
+ *     pooled[j][h][d] = sum of idx key[t][h][d] over tokens t = 4j .. min(4j+3, L_b-1)
+ *     block_scores[b][j] = sum_h sum_d q_idx[b][h][d] * pooled[j][h][d]      (exact)
+ * The score always fits int32 (|S| <= 4*256*128*128 = 2^24).
+ *
+ *   q_idx        [B, n_idx_heads, idx_dim] int8   indexer query of the decode token
+ *   idx_cache    paged indexer keys (see Layouts)
+ *   page_table   [B, max_pages_per_seq] int32
+ *   context_lens [B] int32
+ *   max_blocks   row stride of block_scores; must be >= max_pages_per_seq*page_size/4
+ *   block_scores out [B, max_blocks] int32; entries j >= ceil(L_b/4) are not written
+ * B == 0 is a no-op.
+ */
+qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache,
+                             const int32_t* page_table, const int32_t* context_lens,
+                             int B, int n_idx_heads, int idx_dim, int page_size,
+                             int max_pages_per_seq, int max_blocks,
+                             int32_t* block_scores, void* stream);
+
+/*
+ * qsa_topk_select - keep the best k micro-blocks of each request.
+ *
+ * Article, same paragraph: the best 512 blocks are kept. For request b with
+ * n_b = ceil(L_b/4) blocks, K_b = min(k, n_b) blocks are kept: the first K_b under the
+ * strict order (higher score first, then lower block index). Exactly one set satisfies
+ * this, so the result is deterministic.
+ *
+ *   block_scores [B, max_blocks] int32 (as written by qsa_index_score)
+ *   context_lens [B] int32
+ *   k            blocks to keep, 1 <= k <= 512
+ *   sel_blocks   out [B, k] int32: the kept block ids in ascending order, then -1
+ *   sel_count    out [B] int32: K_b
+ *   workspace    qsa_topk_workspace_size(B, max_blocks, k) bytes (see Workspace)
+ */
+size_t qsa_topk_workspace_size(int B, int max_blocks, int k);
+qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context_lens,
+                             int B, int max_blocks, int k,
+                             int32_t* sel_blocks, int32_t* sel_count,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qsa_sparse_attn_decode - attention of the decode query over the kept tokens, per slice.
+ *
+ * Article, same paragraph: the final softmax and the value aggregation use the
+ * uncompressed K and V at the kept positions; section "What the pull request actually
+ * changes", first paragraph and bullets: each rank reads only its own slice of the
+ * context. Request b's pages are cut into P contiguous runs of S_b = ceil(ceil(L_b/64)/P)
+ * pages; slice p covers tokens [64*p*S_b, min(64*(p+1)*S_b, L_b)). For each slice p and
+ * query head h (KV head g = h / (Hq/Hkv)), over the kept tokens t of slice p:
+ *     s_t = softmax_scale * dot(q[b][h], K[t][g])
+ *     partial_out[b][p][h] = sum_t exp(s_t - m) V[t][g] / sum_t exp(s_t - m),  m = max s_t
+ *     partial_lse[b][p][h] = m + ln(sum_t exp(s_t - m))
+ * A slice without kept tokens gives partial_out = 0 and partial_lse = -inf.
+ *
+ *   q            [B, Hq, head_dim] bf16
+ *   k_cache, v_cache, page_table, context_lens: see Layouts
+ *   sel_blocks   [B, k] int32 and sel_count [B] int32, as written by qsa_topk_select
+ *   P            slices per request, 1 <= P <= 64
+ *   partial_out  out [B, P, Hq, head_dim] float32 (each slice normalised on its own)
+ *   partial_lse  out [B, P, Hq] float32, natural log
+ *   workspace    qsa_attn_workspace_size(B, Hq, Hkv, k, P) bytes (see Workspace)
+ */
+size_t qsa_attn_workspace_size(int B, int Hq, int Hkv, int k, int P);
+qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, const int32_t* context_lens,
+                                    const int32_t* sel_blocks, const int32_t* sel_count,
+                                    int B, int Hq, int Hkv, int head_dim, int page_size,
+                                    int max_pages_per_seq, int k, int P, float softmax_scale,
+                                    float* partial_out, float* partial_lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qsa_lse_merge - combine the P slice partials of every (request, head).
+ *
+ * Article, section "What the pull request actually changes", bullets, and section
+ * "Questions worth answering directly" (DCP versus TP): the partial attention results of
+ * the slices are combined after the split read. With M = max over p of the finite
+ * partial_lse, w_p = exp(partial_lse - M):
+ *     out = sum_p w_p partial_out[p] / sum_p w_p,   out_lse = M + ln(sum_p w_p)
+ * Slices with lse = -inf carry no weight; if every slice is -inf, out = 0, out_lse = -inf.
+ *
+ *   partial_out  [B, P, Hq, head_dim] float32,  partial_lse [B, P, Hq] float32
+ *   out          out [B, Hq, head_dim] float32
+ *   out_lse      out [B, Hq] float32, or NULL
+ */
+qsa_status_t qsa_lse_merge(const float* partial_out, const float* partial_lse,
+                           int B, int P, int Hq, int head_dim,
+                           float* out, float* out_lse, void* stream);
+
+/*
+ * qsa_decode - the whole chain on one stream, one workspace for everything.
+ * Arguments as in the four calls above. block_scores, sel_blocks, sel_count,
+ * partial_out and partial_lse are still caller buffers, so the intermediates stay
+ * inspectable; out_lse may be NULL.
+ */
+size_t qsa_decode_workspace_size(int B, int Hq, int Hkv, int max_blocks, int k, int P);
+qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache,
+                        const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, const int32_t* context_lens,
+                        int B, int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim,
+                        int page_size, int max_pages_per_seq, int max_blocks, int k, int P,
+                        float softmax_scale,
+                        int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
+                        float* partial_out, float* partial_lse, float* out, float* out_lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fill a workspace with zero bytes on `stream` (for its first use). */
+qsa_status_t qsa_workspace_clear(void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QSA_H_ */

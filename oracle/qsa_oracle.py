@@ -167,14 +167,17 @@ def slice_ranges(length: int, P: int, page_size: int):
 
 
 def partial_attention(q, k_rows, v_rows, tokens, ranges, scale):
-    """Per-slice partials over the kept tokens that fall in each slice, R8 and R9."""
+    """Per-slice partials over the kept tokens that fall in each slice, R8 and R9.
+
+    k_rows[i], v_rows[i] are the K/V rows of token position tokens[i].
+    """
     Hq, D = q.shape
     P = len(ranges)
     o_part = np.zeros((P, Hq, D))
     lse_part = np.full((P, Hq), -np.inf)
     for p, (lo, hi) in enumerate(ranges):
-        t = tokens[(tokens >= lo) & (tokens < hi)]
-        o_part[p], lse_part[p] = attend(q, k_rows[t], v_rows[t], scale)
+        inside = (tokens >= lo) & (tokens < hi)
+        o_part[p], lse_part[p] = attend(q, k_rows[inside], v_rows[inside], scale)
     return o_part, lse_part
 
 
@@ -212,8 +215,8 @@ def decode_request(q, q_idx, idx_cache, k_cache, v_cache, page_table_row, length
     scores = index_scores(q_idx, idx_cache, page_table_row, length)
     kept = select_blocks(scores, k)
     tokens = kept_tokens(kept, length)
-    k_rows = bf16_to_f64(request_rows(k_cache, page_table_row, length))
-    v_rows = bf16_to_f64(request_rows(v_cache, page_table_row, length))
+    k_rows = bf16_to_f64(request_rows(k_cache, page_table_row, length)[tokens])
+    v_rows = bf16_to_f64(request_rows(v_cache, page_table_row, length)[tokens])
     qf = bf16_to_f64(q)
     ranges = slice_ranges(length, P, page_size)
     o_part, lse_part = partial_attention(qf, k_rows, v_rows, tokens, ranges, scale)

@@ -1,0 +1,234 @@
+// qsa_api.hip - the C ABI of libqsa: argument checks, workspace sizing, launches.
+// Every check that can be made on the host runs before anything is enqueued.
+#include "../../include/qsa.h"
+#include "qsa_device.h"
+
+namespace qsa {
+hipError_t launch_index_score(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int,
+                              int, int32_t*, int, hipStream_t);
+size_t topk_workspace_bytes(int B, int max_blocks);
+hipError_t launch_topk_select(const int32_t*, const int32_t*, int, int, int, int32_t*, int32_t*, void*,
+                              hipStream_t);
+size_t attn_workspace_bytes(int B, int Hkv, int k, int P);
+hipError_t launch_sparse_attn(const void*, const void*, const void*, const int32_t*, const int32_t*,
+                              const int32_t*, const int32_t*, int, int, int, int, int, int, float, float*,
+                              float*, void*, hipStream_t);
+hipError_t launch_lse_merge(const float*, const float*, int, int, int, float*, float*, hipStream_t);
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+qsa_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return QSA_OK;
+  g_last_hip_error = (int)e;
+  return QSA_ERR_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+int g_num_cu[kMaxDevices];
+
+// Compute units of the current device (queried once per device).
+qsa_status_t device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return QSA_ERR_UNSUPPORTED;
+  int n = __atomic_load_n(&g_num_cu[dev], __ATOMIC_RELAXED);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e);
+    __atomic_store_n(&g_num_cu[dev], n, __ATOMIC_RELAXED);
+  }
+  *out = n;
+  return QSA_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+qsa_status_t check_index(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
+                         const int32_t* lens, int B, int n_idx_heads, int idx_dim, int page_size,
+                         int max_pages, int max_blocks, const int32_t* scores) {
+  if (B < 0 || max_pages < 1 || max_blocks < 1) return QSA_ERR_SHAPE;
+  if (n_idx_heads != kIdxHeads || idx_dim != kIdxDim || page_size != kPageSize) return QSA_ERR_UNSUPPORTED;
+  if ((long long)max_blocks < (long long)max_pages * kBlocksPerPage) return QSA_ERR_SHAPE;
+  if (B > kMaxBatch) return QSA_ERR_UNSUPPORTED;
+  if (B == 0) return QSA_OK;
+  if (!q_idx || !idx_cache || !page_table || !lens || !scores) return QSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(idx_cache)) return QSA_ERR_SHAPE;
+  return QSA_OK;
+}
+
+qsa_status_t check_topk(const int32_t* scores, const int32_t* lens, int B, int max_blocks, int k,
+                        const int32_t* sel, const int32_t* cnt) {
+  if (B < 0 || max_blocks < 1 || k < 1) return QSA_ERR_SHAPE;
+  if (k > kMaxK) return QSA_ERR_UNSUPPORTED;
+  if (B > 65535) return QSA_ERR_UNSUPPORTED;
+  if (B == 0) return QSA_OK;
+  if (!scores || !lens || !sel || !cnt) return QSA_ERR_NULL;
+  return QSA_OK;
+}
+
+qsa_status_t check_attn(const void* q, const void* kc, const void* vc, const int32_t* page_table,
+                        const int32_t* lens, const int32_t* sel, const int32_t* cnt, int B, int Hq,
+                        int Hkv, int head_dim, int page_size, int max_pages, int k, int P,
+                        const float* po, const float* pl) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || max_pages < 1 || k < 1 || P < 1) return QSA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return QSA_ERR_SHAPE;
+  if (head_dim != kHeadDim || page_size != kPageSize) return QSA_ERR_UNSUPPORTED;
+  if (Hq / Hkv > kMaxGroup || k > kMaxK || P > kMaxSlices) return QSA_ERR_UNSUPPORTED;
+  if (B > 65535 || Hkv > 65535) return QSA_ERR_UNSUPPORTED;
+  if (B == 0) return QSA_OK;
+  if (!q || !kc || !vc || !page_table || !lens || !sel || !cnt || !po || !pl) return QSA_ERR_NULL;
+  if (misaligned(q) || misaligned(kc) || misaligned(vc)) return QSA_ERR_SHAPE;
+  return QSA_OK;
+}
+
+qsa_status_t check_merge(const float* po, const float* pl, int B, int P, int Hq, int head_dim,
+                         const float* out) {
+  if (B < 0 || P < 1 || Hq < 1) return QSA_ERR_SHAPE;
+  if (head_dim != kHeadDim) return QSA_ERR_UNSUPPORTED;
+  if (B > 65535 || Hq > 65535) return QSA_ERR_UNSUPPORTED;
+  if (B == 0) return QSA_OK;
+  if (!po || !pl || !out) return QSA_ERR_NULL;
+  return QSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__global__ void zero_fill_kernel(uint32_t* p, size_t nwords) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+}  // namespace
+}  // namespace qsa
+
+using namespace qsa;
+
+extern "C" {
+
+const char* qsa_status_string(int s) {
+  switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL: return "a required pointer is NULL";
+    case QSA_ERR_SHAPE: return "sizes are negative or inconsistent";
+    case QSA_ERR_UNSUPPORTED: return "size outside the compiled kernel shapes";
+    case QSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int qsa_last_hip_error(void) { return g_last_hip_error; }
+
+int qsa_version(void) { return 100; }
+
+qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
+                             const int32_t* context_lens, int B, int n_idx_heads, int idx_dim,
+                             int page_size, int max_pages_per_seq, int max_blocks,
+                             int32_t* block_scores, void* stream) {
+  qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim,
+                                page_size, max_pages_per_seq, max_blocks, block_scores);
+  if (st != QSA_OK || B == 0) return st;
+  int ncu = 0;
+  if ((st = device_cus(&ncu)) != QSA_OK) return st;
+  return hip_status(launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
+                                       max_blocks, block_scores, ncu, (hipStream_t)stream));
+}
+
+size_t qsa_topk_workspace_size(int B, int max_blocks, int k) {
+  (void)k;
+  if (B <= 0 || max_blocks <= 0) return 0;
+  return topk_workspace_bytes(B, max_blocks);
+}
+
+qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context_lens, int B,
+                             int max_blocks, int k, int32_t* sel_blocks, int32_t* sel_count,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  qsa_status_t st = check_topk(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count);
+  if (st != QSA_OK || B == 0) return st;
+  if (!workspace || workspace_bytes < topk_workspace_bytes(B, max_blocks)) return QSA_ERR_WORKSPACE;
+  return hip_status(launch_topk_select(block_scores, context_lens, B, max_blocks, k, sel_blocks,
+                                       sel_count, workspace, (hipStream_t)stream));
+}
+
+size_t qsa_attn_workspace_size(int B, int Hq, int Hkv, int k, int P) {
+  (void)Hq;
+  if (B <= 0 || Hkv <= 0 || k <= 0 || P <= 0) return 0;
+  return attn_workspace_bytes(B, Hkv, k, P);
+}
+
+qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, const int32_t* context_lens,
+                                    const int32_t* sel_blocks, const int32_t* sel_count, int B, int Hq,
+                                    int Hkv, int head_dim, int page_size, int max_pages_per_seq, int k,
+                                    int P, float softmax_scale, float* partial_out, float* partial_lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  qsa_status_t st = check_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B,
+                               Hq, Hkv, head_dim, page_size, max_pages_per_seq, k, P, partial_out,
+                               partial_lse);
+  if (st != QSA_OK || B == 0) return st;
+  if (!workspace || workspace_bytes < attn_workspace_bytes(B, Hkv, k, P)) return QSA_ERR_WORKSPACE;
+  return hip_status(launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks,
+                                       sel_count, B, Hq, Hkv, max_pages_per_seq, k, P, softmax_scale,
+                                       partial_out, partial_lse, workspace, (hipStream_t)stream));
+}
+
+qsa_status_t qsa_lse_merge(const float* partial_out, const float* partial_lse, int B, int P, int Hq,
+                           int head_dim, float* out, float* out_lse, void* stream) {
+  qsa_status_t st = check_merge(partial_out, partial_lse, B, P, Hq, head_dim, out);
+  if (st != QSA_OK || B == 0) return st;
+  return hip_status(launch_lse_merge(partial_out, partial_lse, B, P, Hq, out, out_lse, (hipStream_t)stream));
+}
+
+size_t qsa_decode_workspace_size(int B, int Hq, int Hkv, int max_blocks, int k, int P) {
+  if (B <= 0) return 0;
+  return align256(qsa_topk_workspace_size(B, max_blocks, k)) + qsa_attn_workspace_size(B, Hq, Hkv, k, P);
+}
+
+qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const void* k_cache,
+                        const void* v_cache, const int32_t* page_table, const int32_t* context_lens, int B,
+                        int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim, int page_size,
+                        int max_pages_per_seq, int max_blocks, int k, int P, float softmax_scale,
+                        int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count, float* partial_out,
+                        float* partial_lse, float* out, float* out_lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim,
+                                page_size, max_pages_per_seq, max_blocks, block_scores);
+  if (st == QSA_OK) st = check_topk(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count);
+  if (st == QSA_OK)
+    st = check_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
+                    head_dim, page_size, max_pages_per_seq, k, P, partial_out, partial_lse);
+  if (st == QSA_OK) st = check_merge(partial_out, partial_lse, B, P, Hq, head_dim, out);
+  if (st != QSA_OK || B == 0) return st;
+  const size_t tb = align256(topk_workspace_bytes(B, max_blocks));
+  if (!workspace || workspace_bytes < tb + attn_workspace_bytes(B, Hkv, k, P)) return QSA_ERR_WORKSPACE;
+  int ncu = 0;
+  if ((st = device_cus(&ncu)) != QSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
+                                    max_blocks, block_scores, ncu, s);
+  if (e == hipSuccess)
+    e = launch_topk_select(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count, workspace, s);
+  if (e == hipSuccess)
+    e = launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
+                           max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse,
+                           static_cast<char*>(workspace) + tb, s);
+  if (e == hipSuccess) e = launch_lse_merge(partial_out, partial_lse, B, P, Hq, out, out_lse, s);
+  return hip_status(e);
+}
+
+qsa_status_t qsa_workspace_clear(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return QSA_OK;
+  if (!workspace) return QSA_ERR_NULL;
+  if ((workspace_bytes & 3u) != 0 || misaligned(workspace)) return QSA_ERR_SHAPE;
+  const size_t nwords = workspace_bytes / 4;
+  size_t grid = (nwords + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<uint32_t*>(workspace), nwords);
+  return hip_status(hipGetLastError());
+}
+
+}  // extern "C"

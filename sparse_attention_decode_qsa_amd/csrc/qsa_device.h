@@ -1,0 +1,72 @@
+// qsa_device.h - shapes, vector types and wave/block helpers shared by the QSA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Compiled shapes.
+constexpr int kPageSize = 64;                 // tokens per page
+constexpr int kTokensPerBlock = 4;            // micro-block size (compression ratio 4)
+constexpr int kBlocksPerPage = kPageSize / kTokensPerBlock;
+constexpr int kIdxHeads = 4;
+constexpr int kIdxDim = 64;
+constexpr int kIdxTokenBytes = kIdxHeads * kIdxDim;          // 256
+constexpr int kIdxPageBytes = kPageSize * kIdxTokenBytes;    // 16 KiB
+constexpr int kHeadDim = 128;
+constexpr int kMaxK = 512;                    // kept blocks
+constexpr int kMaxGroup = 16;                 // query heads per KV head (MFMA rows)
+constexpr int kMaxSlices = 64;
+constexpr int kMaxBatch = 16384;              // prefix table of the indexer scan lives in LDS
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Sum over the 16 lanes of each DPP row; every lane of the row gets the row total.
+__device__ __forceinline__ int row16_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);  // row_ror:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false);  // row_ror:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false);  // row_ror:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false);  // row_ror:1
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan over the threads of a block of NT threads (NT a multiple of 64, <= 1024).
+// `tmp` holds at least NT/64 + 1 ints of LDS. Returns the exclusive prefix and writes
+// the block total to *total. Must be reached by every thread of the block.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int inc = wave_inclusive_scan(x);
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) { int v = tmp[w]; tmp[w] = run; run += v; }
+    tmp[NW] = run;
+  }
+  __syncthreads();
+  int r = tmp[wave] + inc - x;
+  *total = tmp[NW];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace qsa

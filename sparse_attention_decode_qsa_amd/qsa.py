@@ -1,0 +1,240 @@
+"""Python binding of libqsa: the C ABI entry points with the same names, on torch tensors.
+
+Argument marshalling only. Every step of the decode path runs in the HIP kernels of
+libqsa.so; there is no fallback. Loading fails with an error if the library has not
+been built (python -m sparse_attention_decode_qsa_amd.build).
+
+Tensors must be contiguous and on the current GPU; calls enqueue on torch's current
+stream and return without synchronizing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
+
+PAGE_SIZE = 64
+IDX_HEADS = 4
+IDX_DIM = 64
+HEAD_DIM = 128
+MAX_K = 512
+
+STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPPORTED",
+          4: "QSA_ERR_WORKSPACE", 5: "QSA_ERR_HIP"}
+
+# (name, restype, argtypes) of every symbol declared in include/qsa.h
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "qsa_status_string": (ctypes.c_char_p, [_I]),
+    "qsa_last_hip_error": (_I, []),
+    "qsa_version": (_I, []),
+    "qsa_index_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "qsa_topk_workspace_size": (_Z, [_I, _I, _I]),
+    "qsa_topk_select": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "qsa_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "qsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                    _P, _P, _P, _Z, _P]),
+    "qsa_lse_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "qsa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "qsa_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                        _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "qsa_workspace_clear": (_I, [_P, _Z, _P]),
+}
+
+
+class QsaError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqsa.so (raises if it is missing: there is no other implementation)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m sparse_attention_decode_qsa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        msg = L.qsa_status_string(status).decode()
+        extra = f" (hipError {L.qsa_last_hip_error()})" if status == 5 else ""
+        raise QsaError(f"{STATUS.get(status, status)}: {msg}{extra}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name}: expected {dim} dims, got {tuple(t.shape)}")
+
+
+class Workspace:
+    """A zero-filled device workspace (libqsa leaves it zeroed after every call)."""
+
+    def __init__(self, nbytes: int, device=None):
+        self.nbytes = int(nbytes)
+        self.tensor = torch.zeros(max(self.nbytes, 16), dtype=torch.uint8, device=device or "cuda")
+
+    def ptr(self):
+        return ctypes.c_void_p(self.tensor.data_ptr())
+
+
+def topk_workspace_size(B, max_blocks, k=MAX_K) -> int:
+    return int(lib().qsa_topk_workspace_size(B, max_blocks, k))
+
+
+def attn_workspace_size(B, Hq, Hkv, k=MAX_K, P=1) -> int:
+    return int(lib().qsa_attn_workspace_size(B, Hq, Hkv, k, P))
+
+
+def decode_workspace_size(B, Hq, Hkv, max_blocks, k=MAX_K, P=1) -> int:
+    return int(lib().qsa_decode_workspace_size(B, Hq, Hkv, max_blocks, k, P))
+
+
+def index_score(q_idx, idx_cache, page_table, context_lens, max_blocks=None, out=None):
+    """Block scores [B, max_blocks] int32 (entries past ceil(L_b/4) are left as they are)."""
+    _need(q_idx, torch.int8, "q_idx", 3)
+    _need(idx_cache, torch.int8, "idx_cache", 4)
+    _need(page_table, torch.int32, "page_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, max_pages = page_table.shape
+    max_blocks = max_pages * PAGE_SIZE // 4 if max_blocks is None else max_blocks
+    if out is None:
+        out = torch.empty((B, max_blocks), dtype=torch.int32, device=q_idx.device)
+    _need(out, torch.int32, "out", 2)
+    _check(lib().qsa_index_score(_ptr(q_idx), _ptr(idx_cache), _ptr(page_table), _ptr(context_lens),
+                                 B, q_idx.shape[1], q_idx.shape[2], idx_cache.shape[1], max_pages,
+                                 out.shape[1], _ptr(out), _stream()))
+    return out
+
+
+def topk_select(block_scores, context_lens, k=MAX_K, workspace=None, sel=None, count=None):
+    """(sel_blocks [B, k] int32 ascending, -1 padded; sel_count [B] int32)."""
+    _need(block_scores, torch.int32, "block_scores", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, max_blocks = block_scores.shape
+    dev = block_scores.device
+    sel = torch.empty((B, k), dtype=torch.int32, device=dev) if sel is None else sel
+    count = torch.empty((B,), dtype=torch.int32, device=dev) if count is None else count
+    ws = workspace or Workspace(topk_workspace_size(B, max_blocks, k), dev)
+    _check(lib().qsa_topk_select(_ptr(block_scores), _ptr(context_lens), B, max_blocks, k, _ptr(sel),
+                                 _ptr(count), ws.ptr(), ws.nbytes, _stream()))
+    return sel, count
+
+
+def sparse_attn_decode(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, P=1,
+                       softmax_scale=None, workspace=None, out=None, lse=None):
+    """Per-slice partials: (partial_out [B, P, Hq, 128] f32, partial_lse [B, P, Hq] f32)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(page_table, torch.int32, "page_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    _need(sel_blocks, torch.int32, "sel_blocks", 2)
+    _need(sel_count, torch.int32, "sel_count", 1)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    k = sel_blocks.shape[1]
+    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    dev = q.device
+    out = torch.empty((B, P, Hq, D), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, P, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    ws = workspace or Workspace(attn_workspace_size(B, Hq, Hkv, k, P), dev)
+    _check(lib().qsa_sparse_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(context_lens), _ptr(sel_blocks),
+        _ptr(sel_count), B, Hq, Hkv, D, k_cache.shape[1], page_table.shape[1], k, P, scale, _ptr(out),
+        _ptr(lse), ws.ptr(), ws.nbytes, _stream()))
+    return out, lse
+
+
+def lse_merge(partial_out, partial_lse, out=None, out_lse=None, want_lse=True):
+    """(out [B, Hq, 128] f32, out_lse [B, Hq] f32 or None)."""
+    _need(partial_out, torch.float32, "partial_out", 4)
+    _need(partial_lse, torch.float32, "partial_lse", 3)
+    B, P, Hq, D = partial_out.shape
+    dev = partial_out.device
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev) if out is None else out
+    if want_lse and out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check(lib().qsa_lse_merge(_ptr(partial_out), _ptr(partial_lse), B, P, Hq, D, _ptr(out),
+                               _ptr(out_lse), _stream()))
+    return out, out_lse
+
+
+class DecodePlan:
+    """Preallocated buffers and one qsa_decode call per run(): the whole chain on one stream.
+
+    Holds every intermediate (scores, sel, sel_count, partials) and the outputs.
+    """
+
+    def __init__(self, q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P, k=MAX_K,
+                 softmax_scale=None, max_blocks=None):
+        for t, dt, n in ((q, torch.bfloat16, "q"), (q_idx, torch.int8, "q_idx"),
+                         (idx_cache, torch.int8, "idx_cache"), (k_cache, torch.bfloat16, "k_cache"),
+                         (v_cache, torch.bfloat16, "v_cache"), (page_table, torch.int32, "page_table"),
+                         (context_lens, torch.int32, "context_lens")):
+            _need(t, dt, n)
+        self.inputs = (q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens)
+        B, Hq, D = q.shape
+        Hkv = k_cache.shape[2]
+        max_pages = page_table.shape[1]
+        self.max_blocks = max_pages * PAGE_SIZE // 4 if max_blocks is None else max_blocks
+        dev = q.device
+        self.scores = torch.empty((B, self.max_blocks), dtype=torch.int32, device=dev)
+        self.sel = torch.empty((B, k), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.partial_out = torch.empty((B, P, Hq, D), dtype=torch.float32, device=dev)
+        self.partial_lse = torch.empty((B, P, Hq), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        self.out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.workspace = Workspace(decode_workspace_size(B, Hq, Hkv, self.max_blocks, k, P), dev)
+        scale = D ** -0.5 if softmax_scale is None else softmax_scale
+        self._fn = lib().qsa_decode
+        self._args = [
+            _ptr(q), _ptr(q_idx), _ptr(idx_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+            _ptr(context_lens), B, Hq, Hkv, D, q_idx.shape[1], q_idx.shape[2], k_cache.shape[1],
+            max_pages, self.max_blocks, k, P, ctypes.c_float(scale), _ptr(self.scores), _ptr(self.sel),
+            _ptr(self.sel_count), _ptr(self.partial_out), _ptr(self.partial_lse), _ptr(self.out),
+            _ptr(self.out_lse), self.workspace.ptr(), self.workspace.nbytes]
+
+    def run(self, stream=None):
+        s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
+        _check(self._fn(*self._args, s))
+        return self.out, self.out_lse
+
+
+def decode(q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P=1, k=MAX_K,
+           softmax_scale=None):
+    """The whole path; returns the DecodePlan holding the outputs and intermediates."""
+    plan = DecodePlan(q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P, k, softmax_scale)
+    plan.run()
+    return plan

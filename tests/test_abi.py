@@ -1,0 +1,126 @@
+"""The C ABI on the CPU: the library loads, exports what include/qsa.h declares, and its
+host-side argument checks return their documented codes before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_decode_qsa_amd import qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails a host check
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(qsa.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = qsa.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    L = qsa.lib()
+    for s in range(6):
+        assert L.qsa_status_string(s)
+    assert L.qsa_status_string(99) == b"unknown status"
+    assert L.qsa_version() >= 100
+    assert L.qsa_last_hip_error() == 0
+
+
+def _index(L, **kw):
+    a = dict(q_idx=FAKE, idx=FAKE, pt=FAKE, lens=FAKE, B=2, nh=4, dim=64, ps=64, mp=16, mb=256, out=FAKE)
+    a.update(kw)
+    return L.qsa_index_score(a["q_idx"], a["idx"], a["pt"], a["lens"], a["B"], a["nh"], a["dim"], a["ps"],
+                             a["mp"], a["mb"], a["out"], None)
+
+
+def test_index_score_checks():
+    L = qsa.lib()
+    assert _index(L, B=0) == OK
+    assert _index(L, q_idx=None) == NULL
+    assert _index(L, out=None) == NULL
+    assert _index(L, B=-1) == SHAPE
+    assert _index(L, mb=255) == SHAPE            # rows must hold every block of a full table
+    assert _index(L, nh=8) == UNSUP
+    assert _index(L, dim=128) == UNSUP
+    assert _index(L, ps=32) == UNSUP
+    assert _index(L, idx=ctypes.c_void_p(0x1001)) == SHAPE   # 16-byte alignment
+    assert _index(L, B=16385) == UNSUP
+
+
+def test_topk_checks():
+    L = qsa.lib()
+    f = L.qsa_topk_select
+    assert f(FAKE, FAKE, 0, 100, 512, FAKE, FAKE, None, 0, None) == OK
+    assert f(None, FAKE, 2, 100, 512, FAKE, FAKE, FAKE, 1 << 30, None) == NULL
+    assert f(FAKE, FAKE, 2, 100, 0, FAKE, FAKE, FAKE, 1 << 30, None) == SHAPE
+    assert f(FAKE, FAKE, 2, 100, 513, FAKE, FAKE, FAKE, 1 << 30, None) == UNSUP
+    need = L.qsa_topk_workspace_size(2, 100, 512)
+    assert need > 0
+    assert f(FAKE, FAKE, 2, 100, 512, FAKE, FAKE, None, need, None) == WS
+    assert f(FAKE, FAKE, 2, 100, 512, FAKE, FAKE, FAKE, need - 1, None) == WS
+
+
+def _attn(L, **kw):
+    a = dict(B=2, Hq=32, Hkv=4, D=128, ps=64, mp=16, k=512, P=4, ws=FAKE, nbytes=1 << 30, q=FAKE, po=FAKE)
+    a.update(kw)
+    return L.qsa_sparse_attn_decode(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"],
+                                    a["D"], a["ps"], a["mp"], a["k"], a["P"], 0.1, a["po"], FAKE, a["ws"],
+                                    a["nbytes"], None)
+
+
+def test_attention_checks():
+    L = qsa.lib()
+    assert _attn(L, B=0) == OK
+    assert _attn(L, q=None) == NULL
+    assert _attn(L, po=None) == NULL
+    assert _attn(L, Hq=30) == SHAPE               # Hq % Hkv
+    assert _attn(L, P=0) == SHAPE
+    assert _attn(L, P=65) == UNSUP
+    assert _attn(L, Hq=68, Hkv=4) == UNSUP         # group of 17 > 16 MFMA rows
+    assert _attn(L, D=64) == UNSUP
+    assert _attn(L, k=600) == UNSUP
+    assert _attn(L, ws=None) == WS
+    need = L.qsa_attn_workspace_size(2, 32, 4, 512, 4)
+    assert _attn(L, nbytes=need - 1) == WS
+
+
+def test_merge_and_decode_checks():
+    L = qsa.lib()
+    m = L.qsa_lse_merge
+    assert m(FAKE, FAKE, 0, 4, 32, 128, FAKE, None, None) == OK
+    assert m(FAKE, None, 2, 4, 32, 128, FAKE, None, None) == NULL
+    assert m(FAKE, FAKE, 2, 0, 32, 128, FAKE, None, None) == SHAPE
+    assert m(FAKE, FAKE, 2, 4, 32, 64, FAKE, None, None) == UNSUP
+    d = L.qsa_decode
+    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 0, None]
+    assert d(*args) == WS
+    bad = list(args)
+    bad[1] = None
+    assert d(*bad) == NULL
+    bad = list(args)
+    bad[8] = 33
+    assert d(*bad) == SHAPE
+    assert L.qsa_workspace_clear(None, 0, None) == OK
+    assert L.qsa_workspace_clear(None, 64, None) == NULL
+    assert L.qsa_workspace_clear(FAKE, 63, None) == SHAPE
+
+
+def test_workspace_sizes_grow_with_the_batch():
+    L = qsa.lib()
+    assert L.qsa_decode_workspace_size(0, 32, 4, 65536, 512, 4) == 0
+    a = L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4)
+    b = L.qsa_decode_workspace_size(8, 32, 4, 65536, 512, 4)
+    assert 0 < a < b
+    assert a >= L.qsa_topk_workspace_size(4, 65536, 512) + L.qsa_attn_workspace_size(4, 32, 4, 512, 4)

@@ -1,0 +1,222 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Block scores, kept block ids and counts must match bit for bit. Attention partials and
+merged outputs must satisfy |gpu - oracle| <= 2e-3 + 1e-2*|oracle| element-wise (the
+oracle is float64). Small batches are checked whole; the full-size workloads are checked
+on sampled requests plus properties that hold for every request.
+"""
+import math
+import random
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_qsa_amd import qsa
+from sparse_attention_decode_qsa_amd.inputs import (PAGE_SIZE, WORKLOADS, Workload, make_inputs,
+                                                    request_subset)
+from tests.helpers import oracle_decode, tolerance_report
+
+pytestmark = pytest.mark.gpu
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_chain(x, P=None, k=512):
+    """The four entry points one after the other; returns host copies of every result."""
+    P = x.workload.slices if P is None else P
+    scores = qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens)
+    sel, cnt = qsa.topk_select(scores, x.context_lens, k)
+    po, pl = qsa.sparse_attn_decode(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, sel, cnt, P,
+                                    x.scale)
+    out, lse = qsa.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    return dict(scores=scores.cpu().numpy(), sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(),
+                po=po.cpu().numpy(), pl=pl.cpu().numpy(), out=out.cpu().numpy(), lse=lse.cpu().numpy())
+
+
+def check_request(g, b, r, L, k=512, what=""):
+    """Compare request b of GPU results g with oracle result r."""
+    nblk = (L + 3) // 4
+    assert np.array_equal(g["scores"][b, :nblk], r["scores"]), f"{what} scores differ (b={b})"
+    K = len(r["kept"])
+    assert g["cnt"][b] == K, f"{what} sel_count {g['cnt'][b]} != {K}"
+    assert np.array_equal(g["sel"][b, :K], r["kept"]), f"{what} kept blocks differ (b={b})"
+    assert np.all(g["sel"][b, K:] == -1)
+    for name, got, ref in (("partial_out", g["po"][b], r["o_part"]), ("out", g["out"][b], r["out"])):
+        ok, ma, mr = tolerance_report(got, ref, ATOL, RTOL)
+        assert ok, f"{what} {name} outside tolerance (b={b}, max abs {ma:.3g}, max rel {mr:.3g})"
+    for name, got, ref in (("partial_lse", g["pl"][b], r["lse_part"]), ("lse", g["lse"][b], r["lse"])):
+        fin = np.isfinite(ref)
+        assert np.array_equal(np.isfinite(got), fin), f"{what} {name}: -inf pattern differs (b={b})"
+        ok, ma, mr = tolerance_report(got[fin], ref[fin], ATOL, RTOL)
+        assert ok, f"{what} {name} outside tolerance (b={b}, max abs {ma:.3g})"
+    return tolerance_report(g["out"][b], r["out"], ATOL, RTOL)
+
+
+def check_whole(x, P=None, k=512, what=""):
+    say(f"[{what}] B={x.batch} lens={x.lengths[:8]} Hq/Hkv={x.workload.hq}/{x.workload.hkv} "
+        f"P={P or x.workload.slices} k={k}")
+    g = run_chain(x, P, k)
+    refs = oracle_decode(oracle, x, P=P, k=k)
+    for b, r in enumerate(refs):
+        check_request(g, b, r, x.lengths[b], k, what)
+    return g, refs
+
+
+def check_properties(x, g, k=512):
+    """Hold for every request at any size: counts, order, range, padding."""
+    for b, L in enumerate(x.lengths):
+        nblk = (L + 3) // 4
+        K = min(k, nblk)
+        assert g["cnt"][b] == K
+        s = g["sel"][b]
+        assert np.all(np.diff(s[:K]) > 0) and (K == 0 or (s[0] >= 0 and s[K - 1] < nblk))
+        assert np.all(s[K:] == -1)
+        assert np.all(np.isfinite(g["out"][b])) and np.all(np.isfinite(g["lse"][b]) | (L == 0))
+
+
+def spot_check_scores(x, g, n=64, seed=0):
+    """Scores of random blocks of every request, each computed by the oracle on its own."""
+    rng = random.Random(seed)
+    pt = x.page_table.cpu().numpy()
+    qi = x.q_idx.cpu().numpy()
+    for b, L in enumerate(x.lengths):
+        nblk = (L + 3) // 4
+        for j in [0, nblk - 1] + [rng.randrange(nblk) for _ in range(n)]:
+            toks = range(4 * j, min(4 * j + 4, L))
+            rows = np.stack([x.idx_cache[int(pt[b, t // PAGE_SIZE]), t % PAGE_SIZE].cpu().numpy() for t in toks])
+            ref = oracle.block_scores(qi[b], oracle.pooled_keys(rows))[0]
+            assert g["scores"][b, j] == ref, f"score of block {j} of request {b}"
+
+
+# ---------------------------------------------------------------- small, whole batches
+
+def W(name, lens, hq=32, hkv=4, P=3, **kw):
+    return Workload(name, len(lens), ("list",) + tuple(lens), hq, hkv, P, **kw)
+
+
+def test_w1_whole():
+    check_whole(make_inputs(WORKLOADS["w1"], 0, "cuda"), what="w1")
+
+
+def test_ragged_tiles_and_tails():
+    check_whole(make_inputs(W("ragged", (1, 4097, 9000, 130)), 1, "cuda"), what="ragged")
+
+
+def test_dense_boundary():
+    check_whole(make_inputs(W("dense", (2047, 2048, 2049, 2052), 16, 2, 2), 2, "cuda"), what="dense")
+
+
+def test_all_ties_zero_query():
+    x = make_inputs(W("zero_q", (5000, 3000), P=4, alphabet="zero_q"), 3, "cuda")
+    g, _ = check_whole(x, what="zero_q")
+    assert np.array_equal(g["sel"][0], np.arange(512))
+
+
+def test_small_alphabet_ties():
+    check_whole(make_inputs(W("u2", (20000, 700, 65536, 2100), P=4, alphabet="u2"), 4, "cuda"), what="u2")
+
+
+def test_planted_blocks():
+    x = make_inputs(W("planted", (8192, 8192, 12000), 16, 2, 2, planted=512), 5, "cuda")
+    g, _ = check_whole(x, what="planted")
+    for b in range(3):
+        assert g["sel"][b].tolist() == x.planted[b]
+
+
+def test_empty_and_tiny_requests():
+    check_whole(make_inputs(W("tiny", (0, 1, 3, 64, 65, 0, 200), P=4), 6, "cuda"), what="tiny")
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 300])
+def test_other_k(k):
+    check_whole(make_inputs(W("k", (3000, 10, 5555)), 7, "cuda"), k=k, what=f"k{k}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 1), (8, 8), (12, 4), (64, 4)])
+def test_group_shapes(hq, hkv):
+    check_whole(make_inputs(W("grp", (3000, 777), hq, hkv, P=2), 8, "cuda"), what=f"grp{hq}/{hkv}")
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 8, 64])
+def test_slice_counts(P):
+    check_whole(make_inputs(W("P", (50000, 9000, 129)), 9, "cuda"), P=P, what=f"P{P}")
+
+
+def test_repeat_is_bitwise_and_workspace_is_reusable():
+    x = make_inputs(W("rep", (70000, 3000, 20000), P=4), 10, "cuda")
+    plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4)
+    plan.run()
+    a = [t.clone() for t in (plan.scores, plan.sel, plan.out, plan.out_lse)]
+    for _ in range(3):
+        plan.run()
+    torch.cuda.synchronize()
+    for u, v in zip(a, (plan.scores, plan.sel, plan.out, plan.out_lse)):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+    refs = oracle_decode(oracle, x, P=4)
+    g = dict(scores=plan.scores.cpu().numpy(), sel=plan.sel.cpu().numpy(), cnt=plan.sel_count.cpu().numpy(),
+             po=plan.partial_out.cpu().numpy(), pl=plan.partial_lse.cpu().numpy(), out=plan.out.cpu().numpy(),
+             lse=plan.out_lse.cpu().numpy())
+    for b, r in enumerate(refs):
+        check_request(g, b, r, x.lengths[b], what="plan")
+
+
+# ------------------------------------------------------ full-size workloads, sampled
+
+def _full(name, sample):
+    x = make_inputs(WORKLOADS[name], 0, "cuda")
+    plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens,
+                          x.workload.slices)
+    plan.run()
+    torch.cuda.synchronize()
+    g = dict(scores=plan.scores.cpu().numpy(), sel=plan.sel.cpu().numpy(), cnt=plan.sel_count.cpu().numpy(),
+             po=plan.partial_out.cpu().numpy(), pl=plan.partial_lse.cpu().numpy(), out=plan.out.cpu().numpy(),
+             lse=plan.out_lse.cpu().numpy())
+    check_properties(x, g)
+    spot_check_scores(x, g)
+    rows = sample(x)
+    say(f"[{name}] lens={len(x.lengths)} requests, checking {rows}")
+    sub = request_subset(x, rows)
+    refs = oracle_decode(oracle, sub)
+    worst = 0.0
+    for i, b in enumerate(rows):
+        gi = {key: v[b:b + 1] for key, v in g.items()}
+        ok, ma, mr = check_request(gi, 0, refs[i], x.lengths[b], what=name)
+        worst = max(worst, ma)
+    say(f"[{name}] max abs err of out over sampled requests: {worst:.3g}")
+    return x, g
+
+
+def test_full_w2_planted_selection_everywhere():
+    x, g = _full("w2", lambda x: [0, 17, 31])
+    for b in range(x.batch):
+        assert g["sel"][b].tolist() == x.planted[b]
+
+
+def test_full_w3():
+    _full("w3", lambda x: [0, 5])
+
+
+def test_full_w4_all_requests():
+    _full("w4", lambda x: list(range(x.batch)))
+
+
+def test_full_w4_fixed_max_context():
+    _full("w4_fixed", lambda x: [3])
+
+
+def test_full_w5_dense_and_sampled():
+    def pick(x):
+        L = x.lengths
+        dense = [b for b, v in enumerate(L) if v <= 2048]
+        assert dense, "the lognormal batch must hold a request of at most 2048 tokens"
+        extremes = [int(np.argmin(L)), int(np.argmax(L))]
+        return sorted(set(dense + extremes + [3, 64]))
+    _full("w5", pick)
