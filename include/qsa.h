@@ -40,10 +40,11 @@
  *              (page ids in range, lengths within the page table) are the caller's and
  *              are not checked. No C++ exception crosses this interface.
  *   Workspace  entry points that take a workspace need qsa_*_workspace_size() bytes,
- *              16-byte aligned. A workspace must be filled with zero bytes once before its
- *              first use (hipMemset or qsa_workspace_clear); every call leaves the parts
- *              it used at zero again, so no per-call clearing is needed. Calls that share
- *              a workspace must not overlap in time.
+ *              16-byte aligned; when that size is 0 (as it is for every call of this
+ *              version: no kernel keeps scratch between workgroups) the pointer may be
+ *              NULL. A non-empty workspace must be filled with zero bytes once before its
+ *              first use (qsa_workspace_clear). Calls that share a workspace must not
+ *              overlap in time.
  *   Threads    stateless and re-entrant apart from the thread-local qsa_last_hip_error.
  */
 #ifndef QSA_H_

@@ -9,8 +9,9 @@
 // against q_idx into the block's accumulator (sum_t dot(q, key_t) = dot(q, sum_t key_t)
 // holds exactly in integer arithmetic), so the pooled key never has to be widened.
 //
-// Mapping. The work is the flat list of pages of all requests (a prefix table over the
-// page counts lives in LDS). One wave64 scores one 16 KiB page = 16 blocks per step:
+// Mapping. Grid (page groups, B): wave w of workgroup x scores page x*WAVES + w of
+// request blockIdx.y (workgroups past the request's pages exit at once), one 16 KiB
+// page = 16 blocks per wave:
 //   lane = 16*r4 + c  (r4 = DPP row 0..3, c = 0..15)
 //   load i (i = 0..15) of the lane reads the 16 bytes at offset 16*c of token
 //   16*r4 + i of the page, so every load instruction reads four contiguous 256-byte
@@ -27,86 +28,53 @@ namespace qsa {
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ idx_cache,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int B,
-    int max_pages, int max_blocks, int32_t* __restrict__ scores) {
-  extern __shared__ int s_prefix[];  // [B + 1] exclusive prefix of page counts, + scan tmp
-  int* s_tmp = s_prefix + B + 1;
-
-  // Prefix table of page counts (contiguous ranges of requests per thread).
-  {
-    constexpr int NT = WAVES * 64;
-    const int per = (B + NT - 1) / NT;
-    const int lo = threadIdx.x * per, hi = min(B, lo + per);
-    int local = 0;
-    for (int i = lo; i < hi; ++i) local += (lens[i] + kPageSize - 1) / kPageSize;
-    int total;
-    int run = block_exclusive_scan<NT>(local, s_tmp, &total);
-    for (int i = lo; i < hi; ++i) {
-      s_prefix[i] = run;
-      run += (lens[i] + kPageSize - 1) / kPageSize;
-    }
-    if (threadIdx.x == 0) s_prefix[B] = total;
-    __syncthreads();
-  }
-  const int total_pages = s_prefix[B];
-
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages,
+    int max_blocks, int32_t* __restrict__ scores) {
+  const int b = blockIdx.y;
+  const int L = lens[b];
+  const int npages = (L + kPageSize - 1) / kPageSize;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
+  const int p = blockIdx.x * WAVES + wave;
+  if (p >= npages) return;
   const int r4 = lane >> 4, c = lane & 15;
-  const int nworkers = gridDim.x * WAVES;
 
-  int qb = -1;
-  i32x4 qv = {0, 0, 0, 0};
-  for (int g = blockIdx.x * WAVES + wave; g < total_pages; g += nworkers) {
-    // request owning flat page g: the largest b with s_prefix[b] <= g
-    int lo = 0, hi = B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_prefix[mid] <= g) lo = mid; else hi = mid;
-    }
-    const int b = lo;
-    const int p = g - s_prefix[b];
-    const int L = lens[b];
-    const int page = page_table[(size_t)b * max_pages + p];
-    if (b != qb) {
-      qv = *reinterpret_cast<const i32x4*>(q_idx + (size_t)b * kIdxTokenBytes + 16 * c);
-      qb = b;
-    }
-    const int8_t* base = idx_cache + (size_t)page * kIdxPageBytes + r4 * (16 * kIdxTokenBytes) + 16 * c;
+  const int page = page_table[(size_t)b * max_pages + p];
+  const i32x4 qv = *reinterpret_cast<const i32x4*>(q_idx + (size_t)b * kIdxTokenBytes + 16 * c);
+  const int8_t* base = idx_cache + (size_t)page * kIdxPageBytes + r4 * (16 * kIdxTokenBytes) + 16 * c;
 
-    i32x4 x[16];
+  i32x4 x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    x[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + i * kIdxTokenBytes));
+
+  const int valid = L - p * kPageSize;  // tokens of this page below L (>= 1)
+  if (valid < kPageSize) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      x[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + i * kIdxTokenBytes));
+      if (16 * r4 + i >= valid) x[i] = i32x4{0, 0, 0, 0};
+  }
 
-    const int valid = L - p * kPageSize;  // tokens of this page below L (>= 1)
-    if (valid < kPageSize) {
+  int acc[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (16 * r4 + i >= valid) x[i] = i32x4{0, 0, 0, 0};
+  for (int r = 0; r < 4; ++r) {
+    int a = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const i32x4 v = x[4 * r + t];
+      a = __builtin_amdgcn_sdot4(v.x, qv.x, a, false);
+      a = __builtin_amdgcn_sdot4(v.y, qv.y, a, false);
+      a = __builtin_amdgcn_sdot4(v.z, qv.z, a, false);
+      a = __builtin_amdgcn_sdot4(v.w, qv.w, a, false);
     }
+    acc[r] = row16_sum(a);
+  }
 
-    int acc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int a = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const i32x4 v = x[4 * r + t];
-        a = __builtin_amdgcn_sdot4(v.x, qv.x, a, false);
-        a = __builtin_amdgcn_sdot4(v.y, qv.y, a, false);
-        a = __builtin_amdgcn_sdot4(v.z, qv.z, a, false);
-        a = __builtin_amdgcn_sdot4(v.w, qv.w, a, false);
-      }
-      acc[r] = row16_sum(a);
-    }
-
-    const int nblk = (L + kTokensPerBlock - 1) / kTokensPerBlock;
-    const int blk = p * kBlocksPerPage + 4 * r4 + c;
-    if (c < 4 && blk < nblk) {
-      const int v = c == 0 ? acc[0] : c == 1 ? acc[1] : c == 2 ? acc[2] : acc[3];
-      scores[(size_t)b * max_blocks + blk] = v;
-    }
+  const int nblk = (L + kTokensPerBlock - 1) / kTokensPerBlock;
+  const int blk = p * kBlocksPerPage + 4 * r4 + c;
+  if (c < 4 && blk < nblk) {
+    const int v = c == 0 ? acc[0] : c == 1 ? acc[1] : c == 2 ? acc[2] : acc[3];
+    scores[(size_t)b * max_blocks + blk] = v;
   }
 }
 
@@ -116,15 +84,10 @@ hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                               const int32_t* page_table, const int32_t* lens, int B,
                               int max_pages, int max_blocks, int32_t* scores, int num_cu,
                               hipStream_t stream) {
-  const long long units = (long long)B * max_pages;            // upper bound on pages
-  long long grid = (units + kScoreWaves - 1) / kScoreWaves;
-  const long long cap = (long long)num_cu * 8;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  const size_t lds = (size_t)(B + 1 + kScoreWaves + 1) * sizeof(int);
-  hipLaunchKernelGGL(index_score_kernel<kScoreWaves>, dim3((unsigned)grid), dim3(kScoreWaves * 64),
-                     lds, stream, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks,
-                     scores);
+  (void)num_cu;
+  const unsigned gx = (unsigned)((max_pages + kScoreWaves - 1) / kScoreWaves);
+  hipLaunchKernelGGL(index_score_kernel<kScoreWaves>, dim3(gx, B), dim3(kScoreWaves * 64), 0, stream,
+                     q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@ namespace qsa {
 hipError_t launch_index_score(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int,
                               int, int32_t*, int, hipStream_t);
 size_t topk_workspace_bytes(int B, int max_blocks);
+constexpr int kMaxSelBlocks = 262144;
 hipError_t launch_topk_select(const int32_t*, const int32_t*, int, int, int, int32_t*, int32_t*, void*,
                               hipStream_t);
 size_t attn_workspace_bytes(int B, int Hkv, int k, int P);
@@ -52,7 +53,7 @@ qsa_status_t check_index(const int8_t* q_idx, const int8_t* idx_cache, const int
   if (B < 0 || max_pages < 1 || max_blocks < 1) return QSA_ERR_SHAPE;
   if (n_idx_heads != kIdxHeads || idx_dim != kIdxDim || page_size != kPageSize) return QSA_ERR_UNSUPPORTED;
   if ((long long)max_blocks < (long long)max_pages * kBlocksPerPage) return QSA_ERR_SHAPE;
-  if (B > kMaxBatch) return QSA_ERR_UNSUPPORTED;
+  if (B > 65535) return QSA_ERR_UNSUPPORTED;
   if (B == 0) return QSA_OK;
   if (!q_idx || !idx_cache || !page_table || !lens || !scores) return QSA_ERR_NULL;
   if (misaligned(q_idx) || misaligned(idx_cache)) return QSA_ERR_SHAPE;
@@ -62,7 +63,7 @@ qsa_status_t check_index(const int8_t* q_idx, const int8_t* idx_cache, const int
 qsa_status_t check_topk(const int32_t* scores, const int32_t* lens, int B, int max_blocks, int k,
                         const int32_t* sel, const int32_t* cnt) {
   if (B < 0 || max_blocks < 1 || k < 1) return QSA_ERR_SHAPE;
-  if (k > kMaxK) return QSA_ERR_UNSUPPORTED;
+  if (k > kMaxK || max_blocks > kMaxSelBlocks) return QSA_ERR_UNSUPPORTED;
   if (B > 65535) return QSA_ERR_UNSUPPORTED;
   if (B == 0) return QSA_OK;
   if (!scores || !lens || !sel || !cnt) return QSA_ERR_NULL;
@@ -95,6 +96,11 @@ qsa_status_t check_merge(const float* po, const float* pl, int B, int P, int Hq,
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// A workspace of `need` bytes: may be NULL when nothing is needed.
+bool workspace_ok(const void* ws, size_t have, size_t need) {
+  return need == 0 || (ws != nullptr && have >= need);
+}
 
 __global__ void zero_fill_kernel(uint32_t* p, size_t nwords) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += (size_t)gridDim.x * blockDim.x)
@@ -148,7 +154,7 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
                              void* workspace, size_t workspace_bytes, void* stream) {
   qsa_status_t st = check_topk(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count);
   if (st != QSA_OK || B == 0) return st;
-  if (!workspace || workspace_bytes < topk_workspace_bytes(B, max_blocks)) return QSA_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, topk_workspace_bytes(B, max_blocks))) return QSA_ERR_WORKSPACE;
   return hip_status(launch_topk_select(block_scores, context_lens, B, max_blocks, k, sel_blocks,
                                        sel_count, workspace, (hipStream_t)stream));
 }
@@ -169,7 +175,7 @@ qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const vo
                                Hq, Hkv, head_dim, page_size, max_pages_per_seq, k, P, partial_out,
                                partial_lse);
   if (st != QSA_OK || B == 0) return st;
-  if (!workspace || workspace_bytes < attn_workspace_bytes(B, Hkv, k, P)) return QSA_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, attn_workspace_bytes(B, Hkv, k, P))) return QSA_ERR_WORKSPACE;
   return hip_status(launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks,
                                        sel_count, B, Hq, Hkv, max_pages_per_seq, k, P, softmax_scale,
                                        partial_out, partial_lse, workspace, (hipStream_t)stream));
@@ -203,7 +209,8 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
   if (st == QSA_OK) st = check_merge(partial_out, partial_lse, B, P, Hq, head_dim, out);
   if (st != QSA_OK || B == 0) return st;
   const size_t tb = align256(topk_workspace_bytes(B, max_blocks));
-  if (!workspace || workspace_bytes < tb + attn_workspace_bytes(B, Hkv, k, P)) return QSA_ERR_WORKSPACE;
+  char* ws_attn = workspace ? static_cast<char*>(workspace) + tb : nullptr;
+  if (!workspace_ok(workspace, workspace_bytes, tb + attn_workspace_bytes(B, Hkv, k, P))) return QSA_ERR_WORKSPACE;
   int ncu = 0;
   if ((st = device_cus(&ncu)) != QSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -214,7 +221,7 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
   if (e == hipSuccess)
     e = launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
                            max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse,
-                           static_cast<char*>(workspace) + tb, s);
+                           ws_attn, s);
   if (e == hipSuccess) e = launch_lse_merge(partial_out, partial_lse, B, P, Hq, out, out_lse, s);
   return hip_status(e);
 }

@@ -19,7 +19,6 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxK = 512;                    // kept blocks
 constexpr int kMaxGroup = 16;                 // query heads per KV head (MFMA rows)
 constexpr int kMaxSlices = 64;
-constexpr int kMaxBatch = 16384;              // prefix table of the indexer scan lives in LDS
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

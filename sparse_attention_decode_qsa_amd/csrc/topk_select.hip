@@ -6,303 +6,233 @@
 // block index), so exactly one set of K_b = min(k, n_b) blocks is correct; it is
 // reported in ascending block order.
 //
-// Method: radix selection on the order-preserving key u = uint32(score) ^ 0x80000000.
-//   pass A  (topk_hist_kernel)  every workgroup histograms one chunk of 4096 scores
-//           into 2048 bins of width 2^14 over u in [2^31 - 2^24, 2^31 + 2^24) (the range
-//           of indexer scores; the two end bins also take anything beyond) and adds its
-//           bins into the request's global histogram.
-//   pass B  (topk_select_kernel) every workgroup finds, from the histogram, the bin
-//           that holds the K_b-th key from the top ("bucket"), then writes two bitmaps
-//           of its chunk: keys above the bucket (kept for sure) and keys inside it.
-//           The last workgroup of the request to finish (an atomic ticket; nobody
-//           waits) resolves the bucket exactly:
-//             - it needs all its members, or it holds at most 256 of them: rank them
-//               by (key desc, index asc) in LDS and keep the best;
-//             - it spans one key value: the ties are taken in index order;
-//             - otherwise histogram the members again over the bucket's own range,
-//               narrowing it 2^11-fold, and repeat.
-//           It then turns the "kept" bitmap into ascending block ids and clears the
-//           histogram and ticket for the next call.
-// Requests with at most k blocks keep all of them and touch no workspace.
+// One 1024-thread workgroup per request; nothing is shared between workgroups, so there
+// is no atomic ticket, no device-scope fence and no workspace.
+//   load    thread t holds the order-preserving keys u = uint32(score) ^ 0x80000000 of
+//           blocks j = t + 1024*i (coalesced 4-byte loads; up to 64 per thread in
+//           registers, more are re-read from memory on every pass).
+//   range   [lo, hi] = [min u, max u] by block reduction.
+//   narrow  repeat: histogram the keys inside [lo, hi] into 2048 LDS bins of width
+//           2^shift (shift = bitlen(hi - lo) - 11, at least 0); the bin holding the
+//           need-th largest key becomes the new [lo, hi]; need drops by the keys above
+//           it. Stop when the bin's keys are all needed (then every key >= lo is kept) or
+//           the bin is a single value T (then every key > T is kept plus the first `need`
+//           keys equal to T in block order). Each pass shrinks the range 2^11-fold, so a
+//           32-bit key needs at most 3 passes; adaptive bin widths keep LDS atomic
+//           contention low for wide and for tie-heavy score distributions alike.
+//   output  one ballot per (wave, slot) gives 64 consecutive blocks, so the kept/tie
+//           masks land in LDS as 64-bit words without atomics; a block-wide prefix of
+//           popcounts turns them into ascending ids.
+// Requests with at most k blocks keep all of them.
 #include "qsa_device.h"
 
 namespace qsa {
 
-constexpr int kTopkThreads = 256;
-constexpr int kChunk = 4096;               // scores per workgroup
-constexpr int kBins = 2048;
-constexpr int kCap = 256;                  // bucket size resolved by ranking
-constexpr uint32_t kLo0 = 0x80000000u - (1u << 24);
-constexpr int kShift0 = 14;
-
-struct TopkWs {
-  uint32_t* hist;       // [B][kBins]
-  uint32_t* ticket;     // [B]
-  uint64_t* gt_bits;    // [B][nwords]
-  uint64_t* in_bits;    // [B][nwords]
-  int nwords;
-};
-
-__host__ __device__ inline size_t topk_nwords(int max_blocks) { return ((size_t)max_blocks + 63) / 64; }
-
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-__host__ __device__ inline size_t topk_ws_bytes(int B, int max_blocks) {
-  const size_t nw = topk_nwords(max_blocks);
-  return align256((size_t)B * kBins * 4) + align256((size_t)B * 4) + 2 * align256((size_t)B * nw * 8);
-}
-
-__host__ __device__ inline TopkWs topk_ws(void* base, int B, int max_blocks) {
-  char* p = static_cast<char*>(base);
-  const size_t nw = topk_nwords(max_blocks);
-  TopkWs w;
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)B * kBins * 4);
-  w.ticket = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)B * 4);
-  w.gt_bits = reinterpret_cast<uint64_t*>(p);
-  p += align256((size_t)B * nw * 8);
-  w.in_bits = reinterpret_cast<uint64_t*>(p);
-  w.nwords = (int)nw;
-  return w;
-}
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kRegSlots = 64;                    // keys held in registers per thread
+constexpr int kSelBins = 2048;
+constexpr int kMaxSelBlocks = 262144;            // contexts up to 1,048,576 tokens
 
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
 
-__device__ __forceinline__ int bin0(uint32_t u) {
-  if (u < kLo0) return 0;
-  const uint32_t d = (u - kLo0) >> kShift0;
-  return d > (uint32_t)(kBins - 1) ? kBins - 1 : (int)d;
-}
+struct SelShared {
+  uint32_t hist[kSelBins + 64];   // + one dummy bin per lane for keys that are not counted
+  int scan[kSelWaves + 1];
+  uint32_t red[2][kSelWaves];
+  int out[4];
+};
 
-// Key interval [lo, hi] of pass-A bin i.
-__device__ __forceinline__ void bin0_range(int i, uint32_t* lo, uint32_t* hi) {
-  *lo = i == 0 ? 0u : kLo0 + ((uint32_t)i << kShift0);
-  *hi = i == kBins - 1 ? 0xFFFFFFFFu : kLo0 + ((uint32_t)(i + 1) << kShift0) - 1u;
-}
-
-__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Within the histogram h[0..kBins) find the bin holding the need-th largest key:
-// sets *beta, *above (count of keys in bins above beta). Every thread must call it.
-__device__ void find_bucket(const uint32_t* h, uint32_t need, int* s_scan, int* beta,
-                            uint32_t* above, int* s_out) {
-  constexpr int per = kBins / kTopkThreads;  // 8 bins per thread
-  const int t = threadIdx.x;
-  int local = 0;
+// Block-wide min and max of x (every thread must call).
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, uint32_t* gmn,
+                                             uint32_t* gmx) {
 #pragma unroll
-  for (int i = 0; i < per; ++i) local += (int)h[t * per + i];
-  int total;
-  const int excl = block_exclusive_scan<kTopkThreads>(local, s_scan, &total);
-  uint32_t run = (uint32_t)(total - excl - local);  // keys in bins above this thread's range
-#pragma unroll
-  for (int i = per - 1; i >= 0; --i) {
-    const uint32_t c = h[t * per + i];
-    if (run < need && run + c >= need) { s_out[0] = t * per + i; s_out[1] = (int)run; }
-    run += c;
+  for (int d = 32; d >= 1; d >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
   }
+  const int wave = threadIdx.x >> 6;
+  if (lane_id() == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
   __syncthreads();
-  *beta = s_out[0];
-  *above = (uint32_t)s_out[1];
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) { a = min(a, sh.red[0][w]); b = max(b, sh.red[1][w]); }
+  *gmn = a;
+  *gmx = b;
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
-    const int32_t* __restrict__ scores, const int32_t* __restrict__ lens, int max_blocks, int k,
-    uint32_t* __restrict__ hist) {
-  const int b = blockIdx.y;
-  const int n = (lens[b] + kTokensPerBlock - 1) / kTokensPerBlock;
-  const int start = blockIdx.x * kChunk;
-  if (n <= k || start >= n) return;
-  __shared__ uint32_t h[kBins];
-  for (int i = threadIdx.x; i < kBins; i += kTopkThreads) h[i] = 0;
-  __syncthreads();
-  const int32_t* s = scores + (size_t)b * max_blocks + start;
-  const int cnt = min(kChunk, n - start);
-#pragma unroll 4
-  for (int i = threadIdx.x; i < cnt; i += kTopkThreads) atomicAdd(&h[bin0(score_key(s[i]))], 1u);
-  __syncthreads();
-  uint32_t* gh = hist + (size_t)b * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kTopkThreads)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
-    const int32_t* __restrict__ scores, const int32_t* __restrict__ lens, int B, int max_blocks,
-    int k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, void* workspace) {
-  const int b = blockIdx.y;
-  const int n = (lens[b] + kTokensPerBlock - 1) / kTokensPerBlock;
-  const int start = blockIdx.x * kChunk;
-  int32_t* out = sel + (size_t)b * k;
+// Bin holding the need-th largest key of the histogram: *beta and the number of keys in
+// the bins above it. Every thread must call.
+__device__ __forceinline__ void find_bucket(SelShared& sh, uint32_t need, int* beta, uint32_t* above) {
+  constexpr int per = kSelBins / kSelThreads;  // 2 bins per thread
   const int t = threadIdx.x;
+  const uint32_t c0 = sh.hist[t * per], c1 = sh.hist[t * per + 1];
+  int total;
+  const int excl = block_exclusive_scan<kSelThreads>((int)(c0 + c1), sh.scan, &total);
+  uint32_t run = (uint32_t)(total - excl) - (c0 + c1);   // keys in bins above this thread's pair
+  if (run < need && run + c1 >= need) { sh.out[0] = t * per + 1; sh.out[1] = (int)run; }
+  run += c1;
+  if (run < need && run + c0 >= need) { sh.out[0] = t * per; sh.out[1] = (int)run; }
+  __syncthreads();
+  *beta = sh.out[0];
+  *above = (uint32_t)sh.out[1];
+  __syncthreads();
+}
+
+template <bool kReg>
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t* __restrict__ scores,
+                                                                  const int32_t* __restrict__ lens,
+                                                                  int max_blocks, int k,
+                                                                  int32_t* __restrict__ sel,
+                                                                  int32_t* __restrict__ sel_count) {
+  extern __shared__ uint64_t s_bits[];  // [2][nw_max]: kept mask, tie mask
+  __shared__ SelShared sh;
+  const int b = blockIdx.x;
+  const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
+  const int n = (lens[b] + kTokensPerBlock - 1) / kTokensPerBlock;
+  int32_t* out = sel + (size_t)b * k;
 
   if (n <= k) {  // every block is kept
-    if (start < n)
-      for (int i = t; i < kChunk && start + i < n; i += kTopkThreads) out[start + i] = start + i;
-    if (blockIdx.x == 0) {
-      for (int i = n + t; i < k; i += kTopkThreads) out[i] = -1;
-      if (t == 0) sel_count[b] = n;
-    }
+    for (int i = t; i < k; i += kSelThreads) out[i] = i < n ? i : -1;
+    if (t == 0) sel_count[b] = n;
     return;
   }
-  if (start >= n) return;
-
-  TopkWs ws = topk_ws(workspace, B, max_blocks);
-  const int32_t* s = scores + (size_t)b * max_blocks;
-  uint32_t* gh = ws.hist + (size_t)b * kBins;
-  uint64_t* gt = ws.gt_bits + (size_t)b * ws.nwords;
-  uint64_t* in = ws.in_bits + (size_t)b * ws.nwords;
   const int K = k;
-
-  __shared__ uint32_t h[kBins];
-  __shared__ int s_scan[kTopkThreads / 64 + 1];
-  __shared__ int s_out[4];
-  __shared__ uint32_t s_ckey[kCap];
-  __shared__ int s_cidx[kCap];
-  __shared__ int s_flag;
-
-  for (int i = t; i < kBins; i += kTopkThreads) h[i] = gh[i];
-  __syncthreads();
-  int beta;
-  uint32_t above;
-  find_bucket(h, (uint32_t)K, s_scan, &beta, &above, s_out);
-  uint32_t lo, hi;
-  bin0_range(beta, &lo, &hi);
-
-  // Bitmaps of this chunk: one ballot per 64 consecutive blocks.
-  {
-    const int lane = lane_id(), wave = t >> 6;
-    for (int grp = wave; grp < kChunk / 64; grp += kTopkThreads / 64) {
-      const int j = start + grp * 64 + lane;
-      bool g = false, m = false;
-      if (j < n) {
-        const uint32_t u = score_key(s[j]);
-        g = u > hi;
-        m = u >= lo && u <= hi;
-      }
-      const uint64_t mg = __ballot(g), mm = __ballot(m);
-      const int w = (start >> 6) + grp;
-      if (lane == 0 && start + grp * 64 < n) { gt[w] = mg; in[w] = mm; }
-    }
-  }
-
-  // Ticket: the last workgroup of this request continues.
-  const int nwg = (n + kChunk - 1) / kChunk;
-  __threadfence();
-  __syncthreads();
-  if (t == 0) s_flag = atomicAdd(&ws.ticket[b], 1u) == (uint32_t)(nwg - 1);
-  __syncthreads();
-  if (!s_flag) return;
-  __threadfence();
-
+  const int32_t* s = scores + (size_t)b * max_blocks;
+  const int nslots = (n + kSelThreads - 1) / kSelThreads;   // slots i with t + 1024*i < n
   const int nw = (n + 63) / 64;
-  const int wper = (nw + kTopkThreads - 1) / kTopkThreads;  // contiguous words per thread
-  const int w0 = min(nw, t * wper), w1 = min(nw, w0 + wper);
-  uint32_t need = (uint32_t)K - above;  // still to take from the bucket
-  uint32_t count = h[beta];
+  uint64_t* keep_bits = s_bits;
+  uint64_t* tie_bits = s_bits + ((max_blocks + 63) / 64);
 
-  for (;;) {
-    if (count == need) {  // the whole bucket is kept
-      for (int w = w0; w < w1; ++w) gt[w] = ld_agent(&gt[w]) | ld_agent(&in[w]);
-      break;
-    }
-    if (count <= (uint32_t)kCap) {  // rank the members
-      if (t == 0) s_out[2] = 0;
-      __syncthreads();
-      for (int w = w0; w < w1; ++w) {
-        uint64_t m = ld_agent(&in[w]);
-        while (m) {
-          const int j = w * 64 + __builtin_ctzll(m);
-          m &= m - 1;
-          const int slot = atomicAdd(&s_out[2], 1);
-          if (slot < kCap) { s_ckey[slot] = score_key(s[j]); s_cidx[slot] = j; }
-        }
-      }
-      __syncthreads();
-      const int c = min(s_out[2], kCap);
-      if (t < c) {
-        const uint32_t u = s_ckey[t];
-        const int j = s_cidx[t];
-        uint32_t rank = 0;
-        for (int i = 0; i < c; ++i) {
-          const uint32_t v = s_ckey[i];
-          rank += (v > u) || (v == u && s_cidx[i] < j);
-        }
-        if (rank < need) atomicOr((unsigned long long*)&gt[j >> 6], 1ull << (j & 63));
-      }
-      break;
-    }
-    if (lo == hi) {  // one key value: ties in index order
-      int mine = 0;
-      for (int w = w0; w < w1; ++w) mine += __builtin_popcountll(ld_agent(&in[w]));
-      int tot;
-      int before = block_exclusive_scan<kTopkThreads>(mine, s_scan, &tot);
-      for (int w = w0; w < w1; ++w) {
-        uint64_t m = ld_agent(&in[w]), take = 0;
-        while (m && before < (int)need) {
-          const uint64_t bit = m & (~m + 1);
-          take |= bit;
-          m &= m - 1;
-          ++before;
-        }
-        if (take) gt[w] = ld_agent(&gt[w]) | take;
-      }
-      break;
-    }
-    // Narrow the bucket: histogram its members over [lo, hi].
-    const int shift = max(0, 32 - __builtin_clz(hi - lo) - 11);
-    for (int i = t; i < kBins; i += kTopkThreads) h[i] = 0;
-    __syncthreads();
-    for (int w = w0; w < w1; ++w) {
-      uint64_t m = ld_agent(&in[w]);
-      while (m) {
-        const int j = w * 64 + __builtin_ctzll(m);
-        m &= m - 1;
-        atomicAdd(&h[(score_key(s[j]) - lo) >> shift], 1u);
+  // Every slot loop below is branch-free: a key that should not be counted goes to the
+  // lane's own dummy bin, so no per-slot exec masks are kept and lanes never collide on
+  // a dummy address.
+  // Slots past the end (block t + 1024*i >= n) hold key 0. Such a key lies inside the
+  // current range only when lo == 0, and then it lands in bin 0: the passes subtract the
+  // known number of them there, and the kept mask is trimmed to n bits at the end. The
+  // slot loops therefore carry no per-slot validity masks and no branches; a key that
+  // is outside the range goes to the lane's own dummy bin (no address collisions).
+  const uint32_t dummy = kSelBins + lane;
+  const int nloop = kReg ? kRegSlots : nslots;
+  const uint32_t n_pad = (uint32_t)(nloop * kSelThreads - n);
+  uint32_t reg[kReg ? kRegSlots : 1];
+  auto for_slots = [&](auto&& f) {
+    if constexpr (kReg) {
+#pragma unroll
+      for (int i = 0; i < kRegSlots; ++i) f(i, reg[i]);
+    } else {
+      for (int i = 0; i < nslots; ++i) {
+        const int j = t + kSelThreads * i;
+        f(i, j < n ? score_key(s[j]) : 0u);
       }
     }
-    __syncthreads();
-    int beta2;
-    uint32_t above2;
-    find_bucket(h, need, s_scan, &beta2, &above2, s_out);
-    const uint32_t nlo = lo + ((uint32_t)beta2 << shift);
-    const uint32_t span = (shift >= 32) ? 0xFFFFFFFFu : ((1u << shift) - 1u);
-    const uint32_t nhi = (hi - nlo < span) ? hi : nlo + span;
-    for (int w = w0; w < w1; ++w) {
-      uint64_t m = ld_agent(&in[w]), up = 0, keep = 0;
-      uint64_t mm = m;
-      while (mm) {
-        const int bit = __builtin_ctzll(mm);
-        mm &= mm - 1;
-        const uint32_t u = score_key(s[w * 64 + bit]);
-        if (u > nhi) up |= 1ull << bit;
-        else if (u >= nlo) keep |= 1ull << bit;
-      }
-      if (up) gt[w] = ld_agent(&gt[w]) | up;
-      in[w] = keep;
+  };
+
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  if constexpr (kReg) {
+#pragma unroll
+    for (int i = 0; i < kRegSlots; ++i) {
+      const int j = t + kSelThreads * i;
+      const uint32_t u = score_key(s[min(j, n - 1)]);
+      reg[i] = j < n ? u : 0u;
+      mn = min(mn, u);             // the clamped load repeats block n-1: harmless for min/max
+      mx = max(mx, u);
     }
-    need -= above2;
-    count = h[beta2];
-    lo = nlo;
-    hi = nhi;
-    __threadfence_block();
-    __syncthreads();
+  } else {
+    for (int i = 0; i < nslots; ++i) {
+      const uint32_t u = score_key(s[min(t + kSelThreads * i, n - 1)]);
+      mn = min(mn, u);
+      mx = max(mx, u);
+    }
   }
-  __threadfence_block();
+  uint32_t lo, hi;
+  block_minmax(mn, mx, sh, &lo, &hi);
+
+  uint32_t need = (uint32_t)K;
+  bool all_of_bucket = false;
+  while (lo != hi) {
+    const int shift = max(0, 32 - __builtin_clz(hi - lo) - 11);
+    for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    const uint32_t clo = lo, span_all = hi - lo;
+    for_slots([&](int, uint32_t u) {
+      const uint32_t d = u - clo;
+      atomicAdd(&sh.hist[d <= span_all ? d >> shift : dummy], 1u);
+    });
+    __syncthreads();
+    if (t == 0 && clo == 0) sh.hist[0] -= n_pad;
+    __syncthreads();
+    int beta;
+    uint32_t above;
+    find_bucket(sh, need, &beta, &above);
+    const uint32_t count = sh.hist[beta];
+    const uint32_t nlo = lo + ((uint32_t)beta << shift);
+    const uint32_t span = (1u << shift) - 1u;
+    hi = (hi - nlo < span) ? hi : nlo + span;
+    lo = nlo;
+    need -= above;
+    __syncthreads();
+    if (count == need) { all_of_bucket = true; break; }
+  }
+
+  // Kept and tie masks, one ballot per (wave, slot) covering blocks 1024*i + 64*wave ..
+  // +63 (word 16*i + wave). Lane i%64 of the wave keeps the words of slot i (a select,
+  // not a branch) and stores them once. Bits past block n-1 are cleared afterwards.
+  {
+    const uint32_t flo = lo, fhi = hi;
+    const bool fall = all_of_bucket;
+    uint64_t my_keep = 0, my_tie = 0;
+    int my_slot = lane;
+    auto store = [&](int slot) {
+      const int w = kSelWaves * slot + wave;
+      if (slot < nslots && w < nw) { keep_bits[w] = my_keep; tie_bits[w] = my_tie; }
+    };
+    for_slots([&](int i, uint32_t u) {
+      const bool kept = fall ? (u >= flo) : (u > fhi);
+      const bool tie = !fall & (u == flo);
+      const uint64_t mk = __ballot(kept), mt = __ballot(tie);
+      if constexpr (!kReg) {
+        if ((i & 63) == 0 && i > 0) { store(my_slot); my_slot += 64; }
+      }
+      my_keep = (lane == (i & 63)) ? mk : my_keep;
+      my_tie = (lane == (i & 63)) ? mt : my_tie;
+    });
+    store(my_slot);
+  }
+  __syncthreads();
+  if (t == 0 && (n & 63)) {
+    const uint64_t live = (1ull << (n & 63)) - 1ull;
+    keep_bits[nw - 1] &= live;
+    tie_bits[nw - 1] &= live;
+  }
   __syncthreads();
 
-  // Kept bitmap -> ascending block ids.
+  // Contiguous word ranges per thread keep block order through the prefix sums.
+  const int wper = (nw + kSelThreads - 1) / kSelThreads;
+  const int w0 = min(nw, t * wper), w1 = min(nw, w0 + wper);
+  if (!all_of_bucket) {  // take the first `need` ties in block order
+    int mine = 0;
+    for (int w = w0; w < w1; ++w) mine += __builtin_popcountll(tie_bits[w]);
+    int tot;
+    int before = block_exclusive_scan<kSelThreads>(mine, sh.scan, &tot);
+    for (int w = w0; w < w1; ++w) {
+      uint64_t m = tie_bits[w], take = 0;
+      while (m && before < (int)need) {
+        take |= m & (~m + 1);
+        m &= m - 1;
+        ++before;
+      }
+      keep_bits[w] |= take;
+    }
+    __syncthreads();
+  }
   int mine = 0;
-  for (int w = w0; w < w1; ++w) mine += __builtin_popcountll(ld_agent(&gt[w]));
+  for (int w = w0; w < w1; ++w) mine += __builtin_popcountll(keep_bits[w]);
   int tot;
-  int pos = block_exclusive_scan<kTopkThreads>(mine, s_scan, &tot);
+  int pos = block_exclusive_scan<kSelThreads>(mine, sh.scan, &tot);
   for (int w = w0; w < w1; ++w) {
-    uint64_t m = ld_agent(&gt[w]);
+    uint64_t m = keep_bits[w];
     while (m) {
       const int j = w * 64 + __builtin_ctzll(m);
       m &= m - 1;
@@ -310,27 +240,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
       ++pos;
     }
   }
-  for (int i = tot + t; i < k; i += kTopkThreads) out[i] = -1;
-  if (t == 0) {
-    sel_count[b] = min(tot, k);
-    ws.ticket[b] = 0;
-  }
-  for (int i = t; i < kBins; i += kTopkThreads) gh[i] = 0;
+  for (int i = tot + t; i < k; i += kSelThreads) out[i] = -1;
+  if (t == 0) sel_count[b] = min(tot, k);
 }
 
-size_t topk_workspace_bytes(int B, int max_blocks) { return topk_ws_bytes(B, max_blocks); }
+size_t topk_workspace_bytes(int B, int max_blocks) {
+  (void)B;
+  (void)max_blocks;
+  return 0;
+}
 
-hipError_t launch_topk_select(const int32_t* scores, const int32_t* lens, int B, int max_blocks,
-                              int k, int32_t* sel, int32_t* sel_count, void* workspace,
-                              hipStream_t stream) {
-  const unsigned chunks = (unsigned)((max_blocks + kChunk - 1) / kChunk);
-  TopkWs ws = topk_ws(workspace, B, max_blocks);
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(chunks, B), dim3(kTopkThreads), 0, stream, scores,
-                     lens, max_blocks, k, ws.hist);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(chunks, B), dim3(kTopkThreads), 0, stream, scores,
-                     lens, B, max_blocks, k, sel, sel_count, workspace);
+hipError_t launch_topk_select(const int32_t* scores, const int32_t* lens, int B, int max_blocks, int k,
+                              int32_t* sel, int32_t* sel_count, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  const size_t lds = 2 * (size_t)((max_blocks + 63) / 64) * sizeof(uint64_t);
+  if (max_blocks <= kRegSlots * kSelThreads)
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
+                       max_blocks, k, sel, sel_count);
+  else
+    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
+                       max_blocks, k, sel, sel_count);
   return hipGetLastError();
 }
 

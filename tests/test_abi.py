@@ -56,20 +56,20 @@ def test_index_score_checks():
     assert _index(L, dim=128) == UNSUP
     assert _index(L, ps=32) == UNSUP
     assert _index(L, idx=ctypes.c_void_p(0x1001)) == SHAPE   # 16-byte alignment
-    assert _index(L, B=16385) == UNSUP
+    assert _index(L, B=65536) == UNSUP
 
 
 def test_topk_checks():
     L = qsa.lib()
     f = L.qsa_topk_select
     assert f(FAKE, FAKE, 0, 100, 512, FAKE, FAKE, None, 0, None) == OK
-    assert f(None, FAKE, 2, 100, 512, FAKE, FAKE, FAKE, 1 << 30, None) == NULL
-    assert f(FAKE, FAKE, 2, 100, 0, FAKE, FAKE, FAKE, 1 << 30, None) == SHAPE
-    assert f(FAKE, FAKE, 2, 100, 513, FAKE, FAKE, FAKE, 1 << 30, None) == UNSUP
-    need = L.qsa_topk_workspace_size(2, 100, 512)
-    assert need > 0
-    assert f(FAKE, FAKE, 2, 100, 512, FAKE, FAKE, None, need, None) == WS
-    assert f(FAKE, FAKE, 2, 100, 512, FAKE, FAKE, FAKE, need - 1, None) == WS
+    assert f(None, FAKE, 2, 100, 512, FAKE, FAKE, None, 0, None) == NULL
+    assert f(FAKE, FAKE, 2, 100, 512, None, FAKE, None, 0, None) == NULL
+    assert f(FAKE, FAKE, 2, 100, 0, FAKE, FAKE, None, 0, None) == SHAPE
+    assert f(FAKE, FAKE, -1, 100, 512, FAKE, FAKE, None, 0, None) == SHAPE
+    assert f(FAKE, FAKE, 2, 100, 513, FAKE, FAKE, None, 0, None) == UNSUP
+    assert f(FAKE, FAKE, 2, 262145, 512, FAKE, FAKE, None, 0, None) == UNSUP   # > 1M-token contexts
+    assert L.qsa_topk_workspace_size(2, 100, 512) == 0     # one workgroup per request, no scratch
 
 
 def _attn(L, **kw):
@@ -91,9 +91,7 @@ def test_attention_checks():
     assert _attn(L, Hq=68, Hkv=4) == UNSUP         # group of 17 > 16 MFMA rows
     assert _attn(L, D=64) == UNSUP
     assert _attn(L, k=600) == UNSUP
-    assert _attn(L, ws=None) == WS
-    need = L.qsa_attn_workspace_size(2, 32, 4, 512, 4)
-    assert _attn(L, nbytes=need - 1) == WS
+    assert L.qsa_attn_workspace_size(2, 32, 4, 512, 4) == 0
 
 
 def test_merge_and_decode_checks():
@@ -104,23 +102,23 @@ def test_merge_and_decode_checks():
     assert m(FAKE, FAKE, 2, 0, 32, 128, FAKE, None, None) == SHAPE
     assert m(FAKE, FAKE, 2, 4, 32, 64, FAKE, None, None) == UNSUP
     d = L.qsa_decode
-    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 0, None]
-    assert d(*args) == WS
+    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [None, 0, None]
     bad = list(args)
-    bad[1] = None
+    bad[1] = None                  # q_idx
     assert d(*bad) == NULL
     bad = list(args)
-    bad[8] = 33
+    bad[24] = None                 # out
+    assert d(*bad) == NULL
+    bad = list(args)
+    bad[8] = 33                    # Hq % Hkv
+    assert d(*bad) == SHAPE
+    bad = list(args)
+    bad[15] = 255                  # max_blocks below max_pages * 16
+    assert d(*bad) == SHAPE
+    bad = list(args)
+    bad[17] = 0                    # P
     assert d(*bad) == SHAPE
     assert L.qsa_workspace_clear(None, 0, None) == OK
     assert L.qsa_workspace_clear(None, 64, None) == NULL
     assert L.qsa_workspace_clear(FAKE, 63, None) == SHAPE
-
-
-def test_workspace_sizes_grow_with_the_batch():
-    L = qsa.lib()
-    assert L.qsa_decode_workspace_size(0, 32, 4, 65536, 512, 4) == 0
-    a = L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4)
-    b = L.qsa_decode_workspace_size(8, 32, 4, 65536, 512, 4)
-    assert 0 < a < b
-    assert a >= L.qsa_topk_workspace_size(4, 65536, 512) + L.qsa_attn_workspace_size(4, 32, 4, 512, 4)
+    assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) == 0
