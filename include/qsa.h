@@ -107,8 +107,9 @@ qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache,
  * strict order (higher score first, then lower block index). Exactly one set satisfies
  * this, so the result is deterministic.
  *
- *   block_scores [B, max_blocks] int32 (as written by qsa_index_score)
- *   context_lens [B] int32
+ *   block_scores [B, max_blocks] int32 (as written by qsa_index_score); max_blocks must
+ *                be a multiple of 4 and at most 262144 (contexts up to 1,048,576 tokens)
+ *   context_lens [B] int32, with ceil(L_b/4) <= max_blocks
  *   k            blocks to keep, 1 <= k <= 512
  *   sel_blocks   out [B, k] int32: the kept block ids in ascending order, then -1
  *   sel_count    out [B] int32: K_b

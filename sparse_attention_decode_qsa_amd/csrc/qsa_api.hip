@@ -65,8 +65,10 @@ qsa_status_t check_topk(const int32_t* scores, const int32_t* lens, int B, int m
   if (B < 0 || max_blocks < 1 || k < 1) return QSA_ERR_SHAPE;
   if (k > kMaxK || max_blocks > kMaxSelBlocks) return QSA_ERR_UNSUPPORTED;
   if (B > 65535) return QSA_ERR_UNSUPPORTED;
+  if (max_blocks % 4 != 0) return QSA_ERR_SHAPE;
   if (B == 0) return QSA_OK;
   if (!scores || !lens || !sel || !cnt) return QSA_ERR_NULL;
+  if (misaligned(scores)) return QSA_ERR_SHAPE;
   return QSA_OK;
 }
 

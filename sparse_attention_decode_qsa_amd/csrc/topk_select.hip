@@ -6,44 +6,58 @@
 // block index), so exactly one set of K_b = min(k, n_b) blocks is correct; it is
 // reported in ascending block order.
 //
-// One 1024-thread workgroup per request; nothing is shared between workgroups, so there
-// is no atomic ticket, no device-scope fence and no workspace.
-//   load    thread t holds the order-preserving keys u = uint32(score) ^ 0x80000000 of
-//           blocks j = t + 1024*i (coalesced 4-byte loads; up to 64 per thread in
-//           registers, more are re-read from memory on every pass).
-//   range   [lo, hi] = [min u, max u] by block reduction.
-//   narrow  repeat: histogram the keys inside [lo, hi] into 2048 LDS bins of width
-//           2^shift (shift = bitlen(hi - lo) - 11, at least 0); the bin holding the
-//           need-th largest key becomes the new [lo, hi]; need drops by the keys above
-//           it. Stop when the bin's keys are all needed (then every key >= lo is kept) or
-//           the bin is a single value T (then every key > T is kept plus the first `need`
-//           keys equal to T in block order). Each pass shrinks the range 2^11-fold, so a
-//           32-bit key needs at most 3 passes; adaptive bin widths keep LDS atomic
-//           contention low for wide and for tie-heavy score distributions alike.
-//   output  one ballot per (wave, slot) gives 64 consecutive blocks, so the kept/tie
-//           masks land in LDS as 64-bit words without atomics; a block-wide prefix of
-//           popcounts turns them into ascending ids.
-// Requests with at most k blocks keep all of them.
+// One 1024-thread workgroup per request; nothing is shared between workgroups (no
+// atomic ticket, no device-scope fence, no workspace). Keys are the order-preserving
+// u = uint32(score) ^ 0x80000000. Thread t owns the R chunks c = t + 1024*r of 64
+// consecutive blocks [64c, 64c + 64), so a per-thread 64-bit mask over a chunk is one
+// word of a bitmap in block order.
+//   1. load    the keys (in registers when R = 1, else re-read from memory) and the
+//              range [lo, hi] = [min u, max u] over the request.
+//   2. sample  keys 0, 16, 32, 48 of every chunk are histogrammed over [lo, hi]; the
+//              lower edge of the bin holding their top 2*k*(samples/n) + 8 is a threshold
+//              tau that about 2k keys reach.
+//   3. list    if between k and 4096 keys reach tau, those candidates go to an LDS list
+//              (key, block); otherwise the narrowing below runs over every key.
+//   4. narrow  repeat: histogram the keys inside [lo, hi] into 2048 bins of width
+//              2^shift (shift = bitlen(hi - lo) - 11, at least 0); the bin holding the
+//              need-th largest key becomes [lo, hi]; need drops by the keys above it.
+//              Stop when all keys of the bin are needed (keep every key >= lo) or the bin
+//              is one value T (keep every key > T and the first `need` keys equal to T in
+//              block order). At most 3 passes for 32-bit keys.
+//   5. output  kept and tie masks per chunk; block prefix sums of their popcounts give
+//              the tie ranks and the ascending output positions.
+// Histogram loops over all keys are branch-free: a key that is not counted goes to the
+// lane's own dummy bin. Requests with at most k blocks keep all of them.
 #include "qsa_device.h"
 
 namespace qsa {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kRegSlots = 64;                    // keys held in registers per thread
+constexpr int kChunk = 64;                       // blocks per chunk (one bitmap word)
 constexpr int kSelBins = 2048;
+constexpr int kListCap = 4096;
 constexpr int kMaxSelBlocks = 262144;            // contexts up to 1,048,576 tokens
 
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
 
 struct SelShared {
-  uint32_t hist[kSelBins + 64];   // + one dummy bin per lane for keys that are not counted
+  uint32_t hist[kSelBins + 64];   // + one dummy bin per lane
+  uint32_t list_u[kListCap];
+  int list_j[kListCap];
   int scan[kSelWaves + 1];
   uint32_t red[2][kSelWaves];
   int out[4];
+  int list_n;
 };
 
-// Block-wide min and max of x (every thread must call).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += (uint32_t)__shfl_xor((int)x, d, 64);
+  return x;
+}
+
+// Block-wide min and max (every thread must call).
 __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, uint32_t* gmn,
                                              uint32_t* gmx) {
 #pragma unroll
@@ -62,11 +76,25 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared
   __syncthreads();
 }
 
-// Bin holding the need-th largest key of the histogram: *beta and the number of keys in
-// the bins above it. Every thread must call.
+// Block-wide sum (every thread must call; ends with a barrier).
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, SelShared& sh) {
+  x = wave_sum(x);
+  const int wave = threadIdx.x >> 6;
+  if (lane_id() == 0) sh.red[0][wave] = x;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) s += sh.red[0][w];
+  __syncthreads();
+  return s;
+}
+
+// Bin of the histogram holding the need-th largest key and the number of keys in the bins
+// above it; *beta = -1 when the histogram holds fewer than `need` keys.
 __device__ __forceinline__ void find_bucket(SelShared& sh, uint32_t need, int* beta, uint32_t* above) {
   constexpr int per = kSelBins / kSelThreads;  // 2 bins per thread
   const int t = threadIdx.x;
+  if (t == 0) { sh.out[0] = -1; sh.out[1] = 0; }
   const uint32_t c0 = sh.hist[t * per], c1 = sh.hist[t * per + 1];
   int total;
   const int excl = block_exclusive_scan<kSelThreads>((int)(c0 + c1), sh.scan, &total);
@@ -80,16 +108,37 @@ __device__ __forceinline__ void find_bucket(SelShared& sh, uint32_t need, int* b
   __syncthreads();
 }
 
-template <bool kReg>
+__device__ __forceinline__ int shift_for(uint32_t lo, uint32_t hi) {
+  return max(0, 32 - __builtin_clz(hi - lo) - 11);
+}
+
+// One narrowing step on a complete histogram of the keys in [lo, hi]. Returns true when
+// the bucket's keys are exactly the ones still needed.
+__device__ __forceinline__ bool narrow_step(SelShared& sh, int shift, uint32_t* lo, uint32_t* hi,
+                                            uint32_t* need) {
+  int beta;
+  uint32_t above;
+  find_bucket(sh, *need, &beta, &above);
+  const uint32_t count = sh.hist[beta];
+  const uint32_t nlo = *lo + ((uint32_t)beta << shift);
+  const uint32_t span = (1u << shift) - 1u;
+  *hi = (*hi - nlo < span) ? *hi : nlo + span;
+  *lo = nlo;
+  *need -= above;
+  __syncthreads();
+  return count == *need;
+}
+
+template <int R>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t* __restrict__ scores,
                                                                   const int32_t* __restrict__ lens,
                                                                   int max_blocks, int k,
                                                                   int32_t* __restrict__ sel,
                                                                   int32_t* __restrict__ sel_count) {
-  extern __shared__ uint64_t s_bits[];  // [2][nw_max]: kept mask, tie mask
+  extern __shared__ uint64_t s_words[];  // [2][1024*R]: kept and tie masks per chunk
   __shared__ SelShared sh;
   const int b = blockIdx.x;
-  const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
+  const int t = threadIdx.x, lane = lane_id();
   const int n = (lens[b] + kTokensPerBlock - 1) / kTokensPerBlock;
   int32_t* out = sel + (size_t)b * k;
 
@@ -98,150 +147,207 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     if (t == 0) sel_count[b] = n;
     return;
   }
-  const int K = k;
   const int32_t* s = scores + (size_t)b * max_blocks;
-  const int nslots = (n + kSelThreads - 1) / kSelThreads;   // slots i with t + 1024*i < n
-  const int nw = (n + 63) / 64;
-  uint64_t* keep_bits = s_bits;
-  uint64_t* tie_bits = s_bits + ((max_blocks + 63) / 64);
-
-  // Every slot loop below is branch-free: a key that should not be counted goes to the
-  // lane's own dummy bin, so no per-slot exec masks are kept and lanes never collide on
-  // a dummy address.
-  // Slots past the end (block t + 1024*i >= n) hold key 0. Such a key lies inside the
-  // current range only when lo == 0, and then it lands in bin 0: the passes subtract the
-  // known number of them there, and the kept mask is trimmed to n bits at the end. The
-  // slot loops therefore carry no per-slot validity masks and no branches; a key that
-  // is outside the range goes to the lane's own dummy bin (no address collisions).
+  uint64_t* kept_w = s_words;
+  uint64_t* tie_w = s_words + kSelThreads * R;
   const uint32_t dummy = kSelBins + lane;
-  const int nloop = kReg ? kRegSlots : nslots;
-  const uint32_t n_pad = (uint32_t)(nloop * kSelThreads - n);
-  uint32_t reg[kReg ? kRegSlots : 1];
-  auto for_slots = [&](auto&& f) {
-    if constexpr (kReg) {
+  constexpr int kU = R == 1 ? kChunk : 1;   // full unroll only when the keys sit in registers
+
+  // Valid keys of chunk r of this thread: [0, nv[r]).
+  int nv[R];
 #pragma unroll
-      for (int i = 0; i < kRegSlots; ++i) f(i, reg[i]);
+  for (int r = 0; r < R; ++r) nv[r] = min(kChunk, max(0, n - kChunk * (t + kSelThreads * r)));
+
+  // 1. keys and range.
+  uint32_t reg[R == 1 ? kChunk : 1];
+  auto key = [&](int r, int e) -> uint32_t {
+    if constexpr (R == 1) {
+      (void)r;
+      return reg[e];
     } else {
-      for (int i = 0; i < nslots; ++i) {
-        const int j = t + kSelThreads * i;
-        f(i, j < n ? score_key(s[j]) : 0u);
-      }
+      return score_key(s[min(kChunk * (t + kSelThreads * r) + e, n - 1)]);
     }
   };
-
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  if constexpr (kReg) {
+  if constexpr (R == 1) {
+    // 16 loads of 16 bytes. A vector that starts at or past block n reads the row's last
+    // vector instead (in bounds since max_blocks % 4 == 0); its keys are masked by nv.
+    const int last_vec = (n - 1) & ~3;
 #pragma unroll
-    for (int i = 0; i < kRegSlots; ++i) {
-      const int j = t + kSelThreads * i;
-      const uint32_t u = score_key(s[min(j, n - 1)]);
-      reg[i] = j < n ? u : 0u;
-      mn = min(mn, u);             // the clamped load repeats block n-1: harmless for min/max
-      mx = max(mx, u);
+    for (int m = 0; m < kChunk / 4; ++m) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(s + min(kChunk * t + 4 * m, last_vec));
+      reg[4 * m + 0] = score_key(v.x);
+      reg[4 * m + 1] = score_key(v.y);
+      reg[4 * m + 2] = score_key(v.z);
+      reg[4 * m + 3] = score_key(v.w);
+    }
+#pragma unroll kU
+    for (int e = 0; e < kChunk; ++e) {
+      const bool ok = e < nv[0];
+      mn = min(mn, ok ? reg[e] : 0xFFFFFFFFu);
+      mx = max(mx, ok ? reg[e] : 0u);
     }
   } else {
-    for (int i = 0; i < nslots; ++i) {
-      const uint32_t u = score_key(s[min(t + kSelThreads * i, n - 1)]);
-      mn = min(mn, u);
-      mx = max(mx, u);
-    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      for (int e = 0; e < nv[r]; ++e) { const uint32_t u = key(r, e); mn = min(mn, u); mx = max(mx, u); }
   }
   uint32_t lo, hi;
   block_minmax(mn, mx, sh, &lo, &hi);
-
-  uint32_t need = (uint32_t)K;
+  uint32_t need = (uint32_t)k;
   bool all_of_bucket = false;
-  while (lo != hi) {
-    const int shift = max(0, 32 - __builtin_clz(hi - lo) - 11);
+  bool masks_done = false;
+
+  if (lo != hi) {
+    // 2. sample.
+    int shift = shift_for(lo, hi);
     for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
-    const uint32_t clo = lo, span_all = hi - lo;
-    for_slots([&](int, uint32_t u) {
-      const uint32_t d = u - clo;
-      atomicAdd(&sh.hist[d <= span_all ? d >> shift : dummy], 1u);
-    });
-    __syncthreads();
-    if (t == 0 && clo == 0) sh.hist[0] -= n_pad;
-    __syncthreads();
-    int beta;
-    uint32_t above;
-    find_bucket(sh, need, &beta, &above);
-    const uint32_t count = sh.hist[beta];
-    const uint32_t nlo = lo + ((uint32_t)beta << shift);
-    const uint32_t span = (1u << shift) - 1u;
-    hi = (hi - nlo < span) ? hi : nlo + span;
-    lo = nlo;
-    need -= above;
-    __syncthreads();
-    if (count == need) { all_of_bucket = true; break; }
-  }
-
-  // Kept and tie masks, one ballot per (wave, slot) covering blocks 1024*i + 64*wave ..
-  // +63 (word 16*i + wave). Lane i%64 of the wave keeps the words of slot i (a select,
-  // not a branch) and stores them once. Bits past block n-1 are cleared afterwards.
-  {
-    const uint32_t flo = lo, fhi = hi;
-    const bool fall = all_of_bucket;
-    uint64_t my_keep = 0, my_tie = 0;
-    int my_slot = lane;
-    auto store = [&](int slot) {
-      const int w = kSelWaves * slot + wave;
-      if (slot < nslots && w < nw) { keep_bits[w] = my_keep; tie_bits[w] = my_tie; }
-    };
-    for_slots([&](int i, uint32_t u) {
-      const bool kept = fall ? (u >= flo) : (u > fhi);
-      const bool tie = !fall & (u == flo);
-      const uint64_t mk = __ballot(kept), mt = __ballot(tie);
-      if constexpr (!kReg) {
-        if ((i & 63) == 0 && i > 0) { store(my_slot); my_slot += 64; }
+    uint32_t mine = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < kChunk; e += 16) {
+        const bool ok = e < nv[r];
+        mine += ok;
+        atomicAdd(&sh.hist[ok ? (key(r, e) - lo) >> shift : dummy], 1u);
       }
-      my_keep = (lane == (i & 63)) ? mk : my_keep;
-      my_tie = (lane == (i & 63)) ? mt : my_tie;
-    });
-    store(my_slot);
+    const uint32_t nsamp = block_sum(mine, sh);
+    const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
+    uint32_t tau = lo;
+    if (need_s < nsamp) {
+      int bs;
+      uint32_t ab;
+      find_bucket(sh, need_s, &bs, &ab);
+      if (bs >= 0) tau = lo + ((uint32_t)bs << shift);
+    }
+
+    // 3. candidates u >= tau.
+    uint64_t cand[R];
+    mine = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint64_t m = 0;
+#pragma unroll kU
+      for (int e = 0; e < kChunk; ++e) m |= (uint64_t)((e < nv[r]) & (key(r, e) >= tau)) << e;
+      cand[r] = m;
+      mine += __builtin_popcountll(m);
+    }
+    const uint32_t ncand = block_sum(mine, sh);
+
+    if (ncand >= (uint32_t)k && ncand <= (uint32_t)kListCap) {
+      if (t == 0) sh.list_n = 0;
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint64_t m = cand[r];
+        while (m) {
+          const int j = kChunk * (t + kSelThreads * r) + __builtin_ctzll(m);
+          m &= m - 1;
+          const int slot = atomicAdd(&sh.list_n, 1);
+          sh.list_u[slot] = score_key(s[j]);
+          sh.list_j[slot] = j;
+        }
+      }
+      __syncthreads();
+      // 4. narrow over the list.
+      lo = tau;
+      while (lo != hi) {
+        shift = shift_for(lo, hi);
+        for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+        __syncthreads();
+        for (int i = t; i < (int)ncand; i += kSelThreads) {
+          const uint32_t u = sh.list_u[i];
+          if (u >= lo && u <= hi) atomicAdd(&sh.hist[(u - lo) >> shift], 1u);
+        }
+        __syncthreads();
+        if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
+      }
+      // 5a. masks from the list: every kept key and every tie is a candidate.
+#pragma unroll
+      for (int r = 0; r < R; ++r) { kept_w[t + kSelThreads * r] = 0; tie_w[t + kSelThreads * r] = 0; }
+      __syncthreads();
+      for (int i = t; i < (int)ncand; i += kSelThreads) {
+        const uint32_t u = sh.list_u[i];
+        const int j = sh.list_j[i];
+        const uint64_t bit = 1ull << (j & 63);
+        if (all_of_bucket ? u >= lo : u > hi) atomicOr((unsigned long long*)&kept_w[j >> 6], bit);
+        else if (!all_of_bucket && u == lo) atomicOr((unsigned long long*)&tie_w[j >> 6], bit);
+      }
+      masks_done = true;
+    } else {
+      // 4. narrow over every key.
+      while (lo != hi) {
+        shift = shift_for(lo, hi);
+        for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+        __syncthreads();
+        const uint32_t clo = lo, span_all = hi - lo;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll kU
+          for (int e = 0; e < kChunk; ++e) {
+            const uint32_t d = key(r, e) - clo;
+            atomicAdd(&sh.hist[((e < nv[r]) & (d <= span_all)) ? d >> shift : dummy], 1u);
+          }
+        __syncthreads();
+        if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
+      }
+    }
   }
-  __syncthreads();
-  if (t == 0 && (n & 63)) {
-    const uint64_t live = (1ull << (n & 63)) - 1ull;
-    keep_bits[nw - 1] &= live;
-    tie_bits[nw - 1] &= live;
+
+  if (!masks_done) {  // 5b. masks from every key
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint64_t mk = 0, mt = 0;
+#pragma unroll kU
+      for (int e = 0; e < kChunk; ++e) {
+        const uint32_t u = key(r, e);
+        const bool ok = e < nv[r];
+        mk |= (uint64_t)(ok & (all_of_bucket ? u >= lo : u > hi)) << e;
+        mt |= (uint64_t)(ok & !all_of_bucket & (u == lo)) << e;
+      }
+      kept_w[t + kSelThreads * r] = mk;
+      tie_w[t + kSelThreads * r] = mt;
+    }
   }
   __syncthreads();
 
-  // Contiguous word ranges per thread keep block order through the prefix sums.
-  const int wper = (nw + kSelThreads - 1) / kSelThreads;
-  const int w0 = min(nw, t * wper), w1 = min(nw, w0 + wper);
-  if (!all_of_bucket) {  // take the first `need` ties in block order
-    int mine = 0;
-    for (int w = w0; w < w1; ++w) mine += __builtin_popcountll(tie_bits[w]);
-    int tot;
-    int before = block_exclusive_scan<kSelThreads>(mine, sh.scan, &tot);
-    for (int w = w0; w < w1; ++w) {
-      uint64_t m = tie_bits[w], take = 0;
+  // 5. the first `need` ties in block order join the kept set; then ascending ids.
+  if (!all_of_bucket) {
+    int run = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = t + kSelThreads * r;
+      const uint64_t m0 = tie_w[c];
+      int tot;
+      int before = run + block_exclusive_scan<kSelThreads>(__builtin_popcountll(m0), sh.scan, &tot);
+      uint64_t m = m0, take = 0;
       while (m && before < (int)need) {
         take |= m & (~m + 1);
         m &= m - 1;
         ++before;
       }
-      keep_bits[w] |= take;
+      kept_w[c] |= take;
+      run += tot;
     }
-    __syncthreads();
   }
-  int mine = 0;
-  for (int w = w0; w < w1; ++w) mine += __builtin_popcountll(keep_bits[w]);
-  int tot;
-  int pos = block_exclusive_scan<kSelThreads>(mine, sh.scan, &tot);
-  for (int w = w0; w < w1; ++w) {
-    uint64_t m = keep_bits[w];
+  int run = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = t + kSelThreads * r;
+    uint64_t m = kept_w[c];
+    int tot;
+    int pos = run + block_exclusive_scan<kSelThreads>(__builtin_popcountll(m), sh.scan, &tot);
     while (m) {
-      const int j = w * 64 + __builtin_ctzll(m);
+      const int j = kChunk * c + __builtin_ctzll(m);
       m &= m - 1;
       if (pos < k) out[pos] = j;
       ++pos;
     }
+    run += tot;
   }
-  for (int i = tot + t; i < k; i += kSelThreads) out[i] = -1;
-  if (t == 0) sel_count[b] = min(tot, k);
+  for (int i = run + t; i < k; i += kSelThreads) out[i] = -1;
+  if (t == 0) sel_count[b] = min(run, k);
 }
 
 size_t topk_workspace_bytes(int B, int max_blocks) {
@@ -253,12 +359,17 @@ size_t topk_workspace_bytes(int B, int max_blocks) {
 hipError_t launch_topk_select(const int32_t* scores, const int32_t* lens, int B, int max_blocks, int k,
                               int32_t* sel, int32_t* sel_count, void* workspace, hipStream_t stream) {
   (void)workspace;
-  const size_t lds = 2 * (size_t)((max_blocks + 63) / 64) * sizeof(uint64_t);
-  if (max_blocks <= kRegSlots * kSelThreads)
-    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
+  const int chunks = (max_blocks + kChunk - 1) / kChunk;
+  const int R = chunks <= kSelThreads ? 1 : chunks <= 2 * kSelThreads ? 2 : 4;
+  const size_t lds = 2 * (size_t)kSelThreads * R * sizeof(uint64_t);
+  if (R == 1)
+    hipLaunchKernelGGL(topk_select_kernel<1>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
+                       max_blocks, k, sel, sel_count);
+  else if (R == 2)
+    hipLaunchKernelGGL(topk_select_kernel<2>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
                        max_blocks, k, sel, sel_count);
   else
-    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
+    hipLaunchKernelGGL(topk_select_kernel<4>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
                        max_blocks, k, sel, sel_count);
   return hipGetLastError();
 }

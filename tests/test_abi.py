@@ -68,7 +68,9 @@ def test_topk_checks():
     assert f(FAKE, FAKE, 2, 100, 0, FAKE, FAKE, None, 0, None) == SHAPE
     assert f(FAKE, FAKE, -1, 100, 512, FAKE, FAKE, None, 0, None) == SHAPE
     assert f(FAKE, FAKE, 2, 100, 513, FAKE, FAKE, None, 0, None) == UNSUP
-    assert f(FAKE, FAKE, 2, 262145, 512, FAKE, FAKE, None, 0, None) == UNSUP   # > 1M-token contexts
+    assert f(FAKE, FAKE, 2, 262148, 512, FAKE, FAKE, None, 0, None) == UNSUP   # > 1M-token contexts
+    assert f(FAKE, FAKE, 2, 102, 512, FAKE, FAKE, None, 0, None) == SHAPE      # rows of 4-block vectors
+    assert f(ctypes.c_void_p(0x1004), FAKE, 2, 100, 512, FAKE, FAKE, None, 0, None) == SHAPE
     assert L.qsa_topk_workspace_size(2, 100, 512) == 0     # one workgroup per request, no scratch
 
 

@@ -223,3 +223,56 @@ def test_full_w5_dense_and_sampled():
         extremes = [int(np.argmin(L)), int(np.argmax(L))]
         return sorted(set(dense + extremes + [3, 64]))
     _full("w5", pick)
+
+
+# ------------------------------------------- top-k on crafted score distributions
+
+def _scores(dist, n, rng):
+    if dist == "wide":
+        return rng.normal(0, 1.7e5, n).astype(np.int64)
+    if dist == "narrow":
+        return rng.normal(0, 64, n).astype(np.int64)
+    if dist == "equal":
+        return np.full(n, 42, np.int64)
+    if dist == "increasing":
+        return np.arange(n, dtype=np.int64)
+    if dist == "decreasing":
+        return -np.arange(n, dtype=np.int64)
+    if dist == "extreme":
+        return rng.choice([-2**31, 2**31 - 1, 0, -1, 1], n).astype(np.int64)
+    if dist == "two_values":
+        return rng.choice([5, 7], n).astype(np.int64)
+    if dist == "spikes":          # narrow bulk plus a few huge outliers: the sampled threshold misses
+        s = rng.integers(-3, 4, n).astype(np.int64)
+        s[rng.integers(0, n, 10)] = 2**30
+        return s
+    raise ValueError(dist)
+
+
+@pytest.mark.parametrize("max_blocks", [4096, 65536, 131072, 262144])
+@pytest.mark.parametrize("k", [1, 512])
+def test_topk_select_crafted_scores(max_blocks, k):
+    """qsa_topk_select alone on score rows that reach every branch of the selection."""
+    rng = np.random.default_rng(max_blocks + k)
+    dists = ["wide", "narrow", "equal", "increasing", "decreasing", "extreme", "two_values", "spikes"]
+    ns = [max_blocks, max_blocks - 3, 513, 600, max(513, max_blocks // 3 + 1), 200]
+    rows, lens = [], []
+    for i, d in enumerate(dists):
+        n = ns[i % len(ns)]
+        row = np.zeros(max_blocks, np.int64)
+        row[:n] = _scores(d, n, rng)
+        row[n:] = rng.integers(-2**31, 2**31, max_blocks - n)      # garbage past n must be ignored
+        rows.append(row)
+        lens.append(4 * n - (i % 4))                                 # L need not be a multiple of 4
+    say(f"[topk] max_blocks={max_blocks} k={k} lens={lens}")
+    scores = torch.tensor(np.stack(rows).astype(np.int32), device="cuda")
+    cl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sel, cnt = qsa.topk_select(scores, cl, k)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b, (row, L) in enumerate(zip(rows, lens)):
+        n = (L + 3) // 4
+        ref = oracle.select_blocks(row[:n], k)
+        assert cnt[b] == len(ref), f"{dists[b]}: count"
+        assert np.array_equal(sel[b, :len(ref)], ref), f"{dists[b]}: kept blocks differ"
+        assert np.all(sel[b, len(ref):] == -1)
