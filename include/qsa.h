@@ -40,10 +40,9 @@
  *              (page ids in range, lengths within the page table) are the caller's and
  *              are not checked. No C++ exception crosses this interface.
  *   Workspace  entry points that take a workspace need qsa_*_workspace_size() bytes,
- *              16-byte aligned; when that size is 0 (as it is for every call of this
- *              version: no kernel keeps scratch between workgroups) the pointer may be
- *              NULL. A non-empty workspace must be filled with zero bytes once before its
- *              first use (qsa_workspace_clear). Calls that share a workspace must not
+ *              16-byte aligned; when that size is 0 the pointer may be NULL. No kernel of
+ *              this version keeps scratch between workgroups or between calls, so a
+ *              workspace needs no initialisation. Calls that share a workspace must not
  *              overlap in time.
  *   Threads    stateless and re-entrant apart from the thread-local qsa_last_hip_error.
  */
@@ -91,13 +90,15 @@ int qsa_version(void);
  *   context_lens [B] int32
  *   max_blocks   row stride of block_scores; must be >= max_pages_per_seq*page_size/4
  *   block_scores out [B, max_blocks] int32; entries j >= ceil(L_b/4) are not written
+ *   page_max     out [B, max_pages_per_seq] int32, or NULL: the largest block score of
+ *                each page p < ceil(L_b/64) (a by-product for qsa_topk_select)
  * B == 0 is a no-op.
  */
 qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                              const int32_t* page_table, const int32_t* context_lens,
                              int B, int n_idx_heads, int idx_dim, int page_size,
                              int max_pages_per_seq, int max_blocks,
-                             int32_t* block_scores, void* stream);
+                             int32_t* block_scores, int32_t* page_max, void* stream);
 
 /*
  * qsa_topk_select - keep the best k micro-blocks of each request.
@@ -110,6 +111,10 @@ qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache,
  *   block_scores [B, max_blocks] int32 (as written by qsa_index_score); max_blocks must
  *                be a multiple of 4 and at most 262144 (contexts up to 1,048,576 tokens)
  *   context_lens [B] int32, with ceil(L_b/4) <= max_blocks
+ *   page_max     [B, max_pages_per_seq] int32 as written by qsa_index_score, or NULL. When
+ *                given (then 16*max_pages_per_seq must be >= max_blocks - 15), requests with
+ *                at least k pages read only the scores of the pages whose maximum reaches
+ *                the k-th largest page maximum. The result is the same either way.
  *   k            blocks to keep, 1 <= k <= 512
  *   sel_blocks   out [B, k] int32: the kept block ids in ascending order, then -1
  *   sel_count    out [B] int32: K_b
@@ -117,7 +122,8 @@ qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache,
  */
 size_t qsa_topk_workspace_size(int B, int max_blocks, int k);
 qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context_lens,
-                             int B, int max_blocks, int k,
+                             const int32_t* page_max, int B, int max_blocks,
+                             int max_pages_per_seq, int k,
                              int32_t* sel_blocks, int32_t* sel_count,
                              void* workspace, size_t workspace_bytes, void* stream);
 
@@ -174,7 +180,8 @@ qsa_status_t qsa_lse_merge(const float* partial_out, const float* partial_lse,
  * qsa_decode - the whole chain on one stream, one workspace for everything.
  * Arguments as in the four calls above. block_scores, sel_blocks, sel_count,
  * partial_out and partial_lse are still caller buffers, so the intermediates stay
- * inspectable; out_lse may be NULL.
+ * inspectable; out_lse may be NULL. The workspace (qsa_decode_workspace_size bytes, no
+ * initialisation needed) holds the per-page maxima passed from the scan to the selection.
  */
 size_t qsa_decode_workspace_size(int B, int Hq, int Hkv, int max_blocks, int k, int P);
 qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache,

@@ -21,6 +21,8 @@
 //   over the 256 key bytes of a token, and lanes c = 0..3 of row r4 store the scores of
 //   blocks 4*r4 + c (64 contiguous bytes per page).
 // Rows past L_b of the last page are read (the page is allocated) and masked to zero.
+// Optionally the maximum block score of each page is written too (page_max[b][p]); the
+// selection uses it to skip pages that cannot hold a kept block.
 #include "qsa_device.h"
 
 namespace qsa {
@@ -29,7 +31,7 @@ template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ idx_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages,
-    int max_blocks, int32_t* __restrict__ scores) {
+    int max_blocks, int32_t* __restrict__ scores, int32_t* __restrict__ page_max) {
   const int b = blockIdx.y;
   const int L = lens[b];
   const int npages = (L + kPageSize - 1) / kPageSize;
@@ -76,18 +78,27 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
     const int v = c == 0 ? acc[0] : c == 1 ? acc[1] : c == 2 ? acc[2] : acc[3];
     scores[(size_t)b * max_blocks + blk] = v;
   }
+  if (page_max) {
+    const int first = p * kBlocksPerPage + 4 * r4;   // blocks of this DPP row
+    int m = (int)0x80000000;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = first + r < nblk ? max(m, acc[r]) : m;
+    m = max(m, __shfl_xor(m, 16, 64));
+    m = max(m, __shfl_xor(m, 32, 64));
+    if (lane == 0) page_max[(size_t)b * max_pages + p] = m;
+  }
 }
 
 constexpr int kScoreWaves = 4;
 
 hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                               const int32_t* page_table, const int32_t* lens, int B,
-                              int max_pages, int max_blocks, int32_t* scores, int num_cu,
-                              hipStream_t stream) {
+                              int max_pages, int max_blocks, int32_t* scores, int32_t* page_max,
+                              int num_cu, hipStream_t stream) {
   (void)num_cu;
   const unsigned gx = (unsigned)((max_pages + kScoreWaves - 1) / kScoreWaves);
   hipLaunchKernelGGL(index_score_kernel<kScoreWaves>, dim3(gx, B), dim3(kScoreWaves * 64), 0, stream,
-                     q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores);
+                     q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
   return hipGetLastError();
 }
 

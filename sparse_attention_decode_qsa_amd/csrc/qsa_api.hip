@@ -5,11 +5,11 @@
 
 namespace qsa {
 hipError_t launch_index_score(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int,
-                              int, int32_t*, int, hipStream_t);
+                              int, int32_t*, int32_t*, int, hipStream_t);
 size_t topk_workspace_bytes(int B, int max_blocks);
 constexpr int kMaxSelBlocks = 262144;
-hipError_t launch_topk_select(const int32_t*, const int32_t*, int, int, int, int32_t*, int32_t*, void*,
-                              hipStream_t);
+hipError_t launch_topk_select(const int32_t*, const int32_t*, const int32_t*, int, int, int, int, int32_t*,
+                              int32_t*, hipStream_t);
 size_t attn_workspace_bytes(int B, int Hkv, int k, int P);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const int32_t*, const int32_t*,
                               const int32_t*, const int32_t*, int, int, int, int, int, int, float, float*,
@@ -135,14 +135,14 @@ int qsa_version(void) { return 100; }
 qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
                              const int32_t* context_lens, int B, int n_idx_heads, int idx_dim,
                              int page_size, int max_pages_per_seq, int max_blocks,
-                             int32_t* block_scores, void* stream) {
+                             int32_t* block_scores, int32_t* page_max, void* stream) {
   qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim,
                                 page_size, max_pages_per_seq, max_blocks, block_scores);
   if (st != QSA_OK || B == 0) return st;
   int ncu = 0;
   if ((st = device_cus(&ncu)) != QSA_OK) return st;
   return hip_status(launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
-                                       max_blocks, block_scores, ncu, (hipStream_t)stream));
+                                       max_blocks, block_scores, page_max, ncu, (hipStream_t)stream));
 }
 
 size_t qsa_topk_workspace_size(int B, int max_blocks, int k) {
@@ -151,14 +151,18 @@ size_t qsa_topk_workspace_size(int B, int max_blocks, int k) {
   return topk_workspace_bytes(B, max_blocks);
 }
 
-qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context_lens, int B,
-                             int max_blocks, int k, int32_t* sel_blocks, int32_t* sel_count,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context_lens,
+                             const int32_t* page_max, int B, int max_blocks, int max_pages_per_seq, int k,
+                             int32_t* sel_blocks, int32_t* sel_count, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   qsa_status_t st = check_topk(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count);
+  if (st == QSA_OK && page_max && (max_pages_per_seq < 1 ||
+                                   (long long)max_pages_per_seq * kBlocksPerPage < (long long)max_blocks - 15))
+    st = QSA_ERR_SHAPE;
   if (st != QSA_OK || B == 0) return st;
   if (!workspace_ok(workspace, workspace_bytes, topk_workspace_bytes(B, max_blocks))) return QSA_ERR_WORKSPACE;
-  return hip_status(launch_topk_select(block_scores, context_lens, B, max_blocks, k, sel_blocks,
-                                       sel_count, workspace, (hipStream_t)stream));
+  return hip_status(launch_topk_select(block_scores, context_lens, page_max, B, max_blocks,
+                                       max_pages_per_seq, k, sel_blocks, sel_count, (hipStream_t)stream));
 }
 
 size_t qsa_attn_workspace_size(int B, int Hq, int Hkv, int k, int P) {
@@ -190,9 +194,16 @@ qsa_status_t qsa_lse_merge(const float* partial_out, const float* partial_lse, i
   return hip_status(launch_lse_merge(partial_out, partial_lse, B, P, Hq, out, out_lse, (hipStream_t)stream));
 }
 
+// qsa_decode's workspace: the per-page maxima [B, max_blocks/16] int32 (written by the
+// indexer scan, read by the selection), then the (empty) attention workspace.
+size_t decode_pm_bytes(int B, int max_blocks) {
+  return align256((size_t)B * ((max_blocks + kBlocksPerPage - 1) / kBlocksPerPage) * sizeof(int32_t));
+}
+
 size_t qsa_decode_workspace_size(int B, int Hq, int Hkv, int max_blocks, int k, int P) {
-  if (B <= 0) return 0;
-  return align256(qsa_topk_workspace_size(B, max_blocks, k)) + qsa_attn_workspace_size(B, Hq, Hkv, k, P);
+  if (B <= 0 || max_blocks <= 0) return 0;
+  return decode_pm_bytes(B, max_blocks) + align256(qsa_topk_workspace_size(B, max_blocks, k)) +
+         qsa_attn_workspace_size(B, Hq, Hkv, k, P);
 }
 
 qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const void* k_cache,
@@ -210,16 +221,21 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                     head_dim, page_size, max_pages_per_seq, k, P, partial_out, partial_lse);
   if (st == QSA_OK) st = check_merge(partial_out, partial_lse, B, P, Hq, head_dim, out);
   if (st != QSA_OK || B == 0) return st;
+  const size_t pmb = decode_pm_bytes(B, max_blocks);
   const size_t tb = align256(topk_workspace_bytes(B, max_blocks));
-  char* ws_attn = workspace ? static_cast<char*>(workspace) + tb : nullptr;
-  if (!workspace_ok(workspace, workspace_bytes, tb + attn_workspace_bytes(B, Hkv, k, P))) return QSA_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, pmb + tb + attn_workspace_bytes(B, Hkv, k, P)))
+    return QSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return QSA_ERR_SHAPE;
+  int32_t* page_max = static_cast<int32_t*>(workspace);   // [B, max_pages_per_seq] fits: 16*max_pages <= max_blocks
+  char* ws_attn = static_cast<char*>(workspace) + pmb + tb;
   int ncu = 0;
   if ((st = device_cus(&ncu)) != QSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
-                                    max_blocks, block_scores, ncu, s);
+                                    max_blocks, block_scores, page_max, ncu, s);
   if (e == hipSuccess)
-    e = launch_topk_select(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count, workspace, s);
+    e = launch_topk_select(block_scores, context_lens, page_max, B, max_blocks, max_pages_per_seq, k,
+                           sel_blocks, sel_count, s);
   if (e == hipSuccess)
     e = launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
                            max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse,

@@ -129,10 +129,46 @@ __device__ __forceinline__ bool narrow_step(SelShared& sh, int shift, uint32_t* 
   return count == *need;
 }
 
+// Narrow [lo, hi] over the LDS candidate list (all candidates are >= lo), then write the
+// kept and tie masks of the candidates into the per-chunk words.
+template <int R>
+__device__ __forceinline__ void narrow_list_and_mark(SelShared& sh, uint32_t ncand, uint32_t lo, uint32_t hi,
+                                                     uint32_t* need_io, bool* all_io, uint32_t* lo_out,
+                                                     uint64_t* kept_w, uint64_t* tie_w) {
+  const int t = threadIdx.x;
+  uint32_t need = *need_io;
+  bool all_of_bucket = false;
+  while (lo != hi) {
+    const int shift = shift_for(lo, hi);
+    for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int i = t; i < (int)ncand; i += kSelThreads) {
+      const uint32_t u = sh.list_u[i];
+      if (u >= lo && u <= hi) atomicAdd(&sh.hist[(u - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) { kept_w[t + kSelThreads * r] = 0; tie_w[t + kSelThreads * r] = 0; }
+  __syncthreads();
+  for (int i = t; i < (int)ncand; i += kSelThreads) {
+    const uint32_t u = sh.list_u[i];
+    const int j = sh.list_j[i];
+    const uint64_t bit = 1ull << (j & 63);
+    if (all_of_bucket ? u >= lo : u > hi) atomicOr((unsigned long long*)&kept_w[j >> 6], bit);
+    else if (!all_of_bucket && u == lo) atomicOr((unsigned long long*)&tie_w[j >> 6], bit);
+  }
+  *need_io = need;
+  *all_io = all_of_bucket;
+  *lo_out = lo;
+}
+
 template <int R>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t* __restrict__ scores,
                                                                   const int32_t* __restrict__ lens,
-                                                                  int max_blocks, int k,
+                                                                  const int32_t* __restrict__ page_max,
+                                                                  int max_blocks, int max_pages, int k,
                                                                   int32_t* __restrict__ sel,
                                                                   int32_t* __restrict__ sel_count) {
   extern __shared__ uint64_t s_words[];  // [2][1024*R]: kept and tie masks per chunk
@@ -153,13 +189,85 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   const uint32_t dummy = kSelBins + lane;
   constexpr int kU = R == 1 ? kChunk : 1;   // full unroll only when the keys sit in registers
 
-  // Valid keys of chunk r of this thread: [0, nv[r]).
+  uint32_t need = (uint32_t)k;
+  bool all_of_bucket = false;
+  bool masks_done = false;
+  uint32_t lo = 0, hi = 0;
+
+  // A. Page maxima (when given and there are at least k pages): tau = the k-th largest
+  // page maximum. At least k pages reach it, each with a block >= tau, so the k-th key is
+  // >= tau; only the blocks of pages reaching tau can be candidates.
+  const int np = (n + kBlocksPerPage - 1) / kBlocksPerPage;
+  bool have_list = false;
+  uint32_t ncand = 0;
+  if (page_max != nullptr && np >= k) {
+    constexpr int PV = 4 * R;                    // page maxima per thread (np <= 4096*R)
+    const int32_t* pm = page_max + (size_t)b * max_pages;
+    uint32_t pv[PV];
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+      const int pidx = t + kSelThreads * i;
+      pv[i] = pidx < np ? score_key(pm[pidx]) : 0u;
+      mn = min(mn, pidx < np ? pv[i] : 0xFFFFFFFFu);
+      mx = max(mx, pv[i]);
+    }
+    uint32_t plo, phi;
+    block_minmax(mn, mx, sh, &plo, &phi);
+    hi = phi;                                    // the largest page maximum is the largest key
+    uint32_t pneed = (uint32_t)k;
+    while (plo != phi) {
+      const int shift = shift_for(plo, phi);
+      for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+      __syncthreads();
+      const uint32_t clo = plo, span_all = phi - plo;
+#pragma unroll
+      for (int i = 0; i < PV; ++i) {
+        const uint32_t d = pv[i] - clo;
+        atomicAdd(&sh.hist[((t + kSelThreads * i < np) & (d <= span_all)) ? d >> shift : dummy], 1u);
+      }
+      __syncthreads();
+      if (narrow_step(sh, shift, &plo, &phi, &pneed)) break;
+    }
+    const uint32_t tau = plo;
+    // B. candidate blocks of the pages that reach tau.
+    if (t == 0) sh.list_n = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+      const int pidx = t + kSelThreads * i;
+      if (pidx < np && pv[i] >= tau) {
+        const i32x4* row = reinterpret_cast<const i32x4*>(s + kBlocksPerPage * pidx);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if (kBlocksPerPage * pidx + 4 * m >= n) break;   // vectors past block n stay unread
+          const i32x4 v = row[m];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = kBlocksPerPage * pidx + 4 * m + e;
+            const uint32_t u = score_key(v[e]);
+            if (j < n && u >= tau) {
+              const int slot = atomicAdd(&sh.list_n, 1);
+              if (slot < kListCap) { sh.list_u[slot] = u; sh.list_j[slot] = j; }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    ncand = (uint32_t)sh.list_n;
+    if (ncand <= (uint32_t)kListCap) {
+      have_list = true;
+      lo = tau;
+    }
+    __syncthreads();
+  }
+
+  // Sample path and full fallback over every key.
+  uint32_t reg[R == 1 ? kChunk : 1];
   int nv[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) nv[r] = min(kChunk, max(0, n - kChunk * (t + kSelThreads * r)));
-
-  // 1. keys and range.
-  uint32_t reg[R == 1 ? kChunk : 1];
   auto key = [&](int r, int e) -> uint32_t {
     if constexpr (R == 1) {
       (void)r;
@@ -168,151 +276,129 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       return score_key(s[min(kChunk * (t + kSelThreads * r) + e, n - 1)]);
     }
   };
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  if constexpr (R == 1) {
-    // 16 loads of 16 bytes. A vector that starts at or past block n reads the row's last
-    // vector instead (in bounds since max_blocks % 4 == 0); its keys are masked by nv.
-    const int last_vec = (n - 1) & ~3;
+  if (!have_list) {
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    if constexpr (R == 1) {
+      // 16 loads of 16 bytes. A vector that starts at or past block n reads the row's last
+      // vector instead (in bounds since max_blocks % 4 == 0); its keys are masked by nv.
+      const int last_vec = (n - 1) & ~3;
 #pragma unroll
-    for (int m = 0; m < kChunk / 4; ++m) {
-      const i32x4 v = *reinterpret_cast<const i32x4*>(s + min(kChunk * t + 4 * m, last_vec));
-      reg[4 * m + 0] = score_key(v.x);
-      reg[4 * m + 1] = score_key(v.y);
-      reg[4 * m + 2] = score_key(v.z);
-      reg[4 * m + 3] = score_key(v.w);
-    }
-#pragma unroll kU
-    for (int e = 0; e < kChunk; ++e) {
-      const bool ok = e < nv[0];
-      mn = min(mn, ok ? reg[e] : 0xFFFFFFFFu);
-      mx = max(mx, ok ? reg[e] : 0u);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      for (int e = 0; e < nv[r]; ++e) { const uint32_t u = key(r, e); mn = min(mn, u); mx = max(mx, u); }
-  }
-  uint32_t lo, hi;
-  block_minmax(mn, mx, sh, &lo, &hi);
-  uint32_t need = (uint32_t)k;
-  bool all_of_bucket = false;
-  bool masks_done = false;
-
-  if (lo != hi) {
-    // 2. sample.
-    int shift = shift_for(lo, hi);
-    for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
-    __syncthreads();
-    uint32_t mine = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int e = 0; e < kChunk; e += 16) {
-        const bool ok = e < nv[r];
-        mine += ok;
-        atomicAdd(&sh.hist[ok ? (key(r, e) - lo) >> shift : dummy], 1u);
+      for (int m = 0; m < kChunk / 4; ++m) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(s + min(kChunk * t + 4 * m, last_vec));
+        reg[4 * m + 0] = score_key(v.x);
+        reg[4 * m + 1] = score_key(v.y);
+        reg[4 * m + 2] = score_key(v.z);
+        reg[4 * m + 3] = score_key(v.w);
       }
-    const uint32_t nsamp = block_sum(mine, sh);
-    const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
-    uint32_t tau = lo;
-    if (need_s < nsamp) {
-      int bs;
-      uint32_t ab;
-      find_bucket(sh, need_s, &bs, &ab);
-      if (bs >= 0) tau = lo + ((uint32_t)bs << shift);
-    }
-
-    // 3. candidates u >= tau.
-    uint64_t cand[R];
-    mine = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint64_t m = 0;
-#pragma unroll kU
-      for (int e = 0; e < kChunk; ++e) m |= (uint64_t)((e < nv[r]) & (key(r, e) >= tau)) << e;
-      cand[r] = m;
-      mine += __builtin_popcountll(m);
+      for (int e = 0; e < kChunk; ++e) {
+        const bool ok = e < nv[0];
+        mn = min(mn, ok ? reg[e] : 0xFFFFFFFFu);
+        mx = max(mx, ok ? reg[e] : 0u);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        for (int e = 0; e < nv[r]; ++e) { const uint32_t u = key(r, e); mn = min(mn, u); mx = max(mx, u); }
     }
-    const uint32_t ncand = block_sum(mine, sh);
+    block_minmax(mn, mx, sh, &lo, &hi);
 
-    if (ncand >= (uint32_t)k && ncand <= (uint32_t)kListCap) {
-      if (t == 0) sh.list_n = 0;
+    if (lo != hi) {
+      // sample: keys 0, 16, 32, 48 of every chunk.
+      int shift = shift_for(lo, hi);
+      for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
       __syncthreads();
+      uint32_t mine = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < kChunk; e += 16) {
+          const bool ok = e < nv[r];
+          mine += ok;
+          atomicAdd(&sh.hist[ok ? (key(r, e) - lo) >> shift : dummy], 1u);
+        }
+      const uint32_t nsamp = block_sum(mine, sh);
+      const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
+      uint32_t tau = lo;
+      if (need_s < nsamp) {
+        int bs;
+        uint32_t ab;
+        find_bucket(sh, need_s, &bs, &ab);
+        if (bs >= 0) tau = lo + ((uint32_t)bs << shift);
+      }
+      // candidates u >= tau.
+      uint64_t cand[R];
+      mine = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        uint64_t m = cand[r];
-        while (m) {
-          const int j = kChunk * (t + kSelThreads * r) + __builtin_ctzll(m);
-          m &= m - 1;
-          const int slot = atomicAdd(&sh.list_n, 1);
-          sh.list_u[slot] = score_key(s[j]);
-          sh.list_j[slot] = j;
-        }
+        uint64_t m = 0;
+#pragma unroll kU
+        for (int e = 0; e < kChunk; ++e) m |= (uint64_t)((e < nv[r]) & (key(r, e) >= tau)) << e;
+        cand[r] = m;
+        mine += __builtin_popcountll(m);
       }
-      __syncthreads();
-      // 4. narrow over the list.
-      lo = tau;
-      while (lo != hi) {
-        shift = shift_for(lo, hi);
-        for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+      ncand = block_sum(mine, sh);
+      if (ncand >= (uint32_t)k && ncand <= (uint32_t)kListCap) {
+        if (t == 0) sh.list_n = 0;
         __syncthreads();
-        for (int i = t; i < (int)ncand; i += kSelThreads) {
-          const uint32_t u = sh.list_u[i];
-          if (u >= lo && u <= hi) atomicAdd(&sh.hist[(u - lo) >> shift], 1u);
-        }
-        __syncthreads();
-        if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
-      }
-      // 5a. masks from the list: every kept key and every tie is a candidate.
 #pragma unroll
-      for (int r = 0; r < R; ++r) { kept_w[t + kSelThreads * r] = 0; tie_w[t + kSelThreads * r] = 0; }
-      __syncthreads();
-      for (int i = t; i < (int)ncand; i += kSelThreads) {
-        const uint32_t u = sh.list_u[i];
-        const int j = sh.list_j[i];
-        const uint64_t bit = 1ull << (j & 63);
-        if (all_of_bucket ? u >= lo : u > hi) atomicOr((unsigned long long*)&kept_w[j >> 6], bit);
-        else if (!all_of_bucket && u == lo) atomicOr((unsigned long long*)&tie_w[j >> 6], bit);
+        for (int r = 0; r < R; ++r) {
+          uint64_t m = cand[r];
+          while (m) {
+            const int j = kChunk * (t + kSelThreads * r) + __builtin_ctzll(m);
+            m &= m - 1;
+            const int slot = atomicAdd(&sh.list_n, 1);
+            sh.list_u[slot] = score_key(s[j]);
+            sh.list_j[slot] = j;
+          }
+        }
+        __syncthreads();
+        have_list = true;
+        lo = tau;
+      } else {
+        // narrow over every key (branch-free: uncounted keys go to the lane's dummy bin).
+        while (lo != hi) {
+          shift = shift_for(lo, hi);
+          for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+          __syncthreads();
+          const uint32_t clo = lo, span_all = hi - lo;
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll kU
+            for (int e = 0; e < kChunk; ++e) {
+              const uint32_t d = key(r, e) - clo;
+              atomicAdd(&sh.hist[((e < nv[r]) & (d <= span_all)) ? d >> shift : dummy], 1u);
+            }
+          __syncthreads();
+          if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
+        }
+      }
+    }
+    if (!have_list) {  // masks from every key
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint64_t mk = 0, mt = 0;
+#pragma unroll kU
+        for (int e = 0; e < kChunk; ++e) {
+          const uint32_t u = key(r, e);
+          const bool ok = e < nv[r];
+          mk |= (uint64_t)(ok & (all_of_bucket ? u >= lo : u > hi)) << e;
+          mt |= (uint64_t)(ok & !all_of_bucket & (u == lo)) << e;
+        }
+        kept_w[t + kSelThreads * r] = mk;
+        tie_w[t + kSelThreads * r] = mt;
       }
       masks_done = true;
-    } else {
-      // 4. narrow over every key.
-      while (lo != hi) {
-        shift = shift_for(lo, hi);
-        for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
-        __syncthreads();
-        const uint32_t clo = lo, span_all = hi - lo;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll kU
-          for (int e = 0; e < kChunk; ++e) {
-            const uint32_t d = key(r, e) - clo;
-            atomicAdd(&sh.hist[((e < nv[r]) & (d <= span_all)) ? d >> shift : dummy], 1u);
-          }
-        __syncthreads();
-        if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
-      }
     }
   }
-
-  if (!masks_done) {  // 5b. masks from every key
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint64_t mk = 0, mt = 0;
-#pragma unroll kU
-      for (int e = 0; e < kChunk; ++e) {
-        const uint32_t u = key(r, e);
-        const bool ok = e < nv[r];
-        mk |= (uint64_t)(ok & (all_of_bucket ? u >= lo : u > hi)) << e;
-        mt |= (uint64_t)(ok & !all_of_bucket & (u == lo)) << e;
-      }
-      kept_w[t + kSelThreads * r] = mk;
-      tie_w[t + kSelThreads * r] = mt;
-    }
+  if (have_list && !masks_done) {
+    uint32_t llo = lo;
+    narrow_list_and_mark<R>(sh, ncand, lo, hi, &need, &all_of_bucket, &llo, kept_w, tie_w);
+    lo = llo;
   }
   __syncthreads();
 
-  // 5. the first `need` ties in block order join the kept set; then ascending ids.
+  // The first `need` ties in block order join the kept set; then ascending ids.
   if (!all_of_bucket) {
     int run = 0;
 #pragma unroll
@@ -356,21 +442,21 @@ size_t topk_workspace_bytes(int B, int max_blocks) {
   return 0;
 }
 
-hipError_t launch_topk_select(const int32_t* scores, const int32_t* lens, int B, int max_blocks, int k,
-                              int32_t* sel, int32_t* sel_count, void* workspace, hipStream_t stream) {
-  (void)workspace;
+hipError_t launch_topk_select(const int32_t* scores, const int32_t* lens, const int32_t* page_max, int B,
+                              int max_blocks, int max_pages, int k, int32_t* sel, int32_t* sel_count,
+                              hipStream_t stream) {
   const int chunks = (max_blocks + kChunk - 1) / kChunk;
   const int R = chunks <= kSelThreads ? 1 : chunks <= 2 * kSelThreads ? 2 : 4;
   const size_t lds = 2 * (size_t)kSelThreads * R * sizeof(uint64_t);
   if (R == 1)
     hipLaunchKernelGGL(topk_select_kernel<1>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
-                       max_blocks, k, sel, sel_count);
+                       page_max, max_blocks, max_pages, k, sel, sel_count);
   else if (R == 2)
     hipLaunchKernelGGL(topk_select_kernel<2>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
-                       max_blocks, k, sel, sel_count);
+                       page_max, max_blocks, max_pages, k, sel, sel_count);
   else
     hipLaunchKernelGGL(topk_select_kernel<4>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
-                       max_blocks, k, sel, sel_count);
+                       page_max, max_blocks, max_pages, k, sel, sel_count);
   return hipGetLastError();
 }
 

@@ -31,9 +31,9 @@ SIGNATURES = {
     "qsa_status_string": (ctypes.c_char_p, [_I]),
     "qsa_last_hip_error": (_I, []),
     "qsa_version": (_I, []),
-    "qsa_index_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "qsa_index_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "qsa_topk_workspace_size": (_Z, [_I, _I, _I]),
-    "qsa_topk_select": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "qsa_topk_select": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "qsa_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "qsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                     _P, _P, _P, _Z, _P]),
@@ -98,7 +98,7 @@ def _need(t, dtype, name, dim=None):
 
 
 class Workspace:
-    """A zero-filled device workspace (libqsa leaves it zeroed after every call)."""
+    """A device workspace of the size a libqsa *_workspace_size query returned."""
 
     def __init__(self, nbytes: int, device=None):
         self.nbytes = int(nbytes)
@@ -120,8 +120,11 @@ def decode_workspace_size(B, Hq, Hkv, max_blocks, k=MAX_K, P=1) -> int:
     return int(lib().qsa_decode_workspace_size(B, Hq, Hkv, max_blocks, k, P))
 
 
-def index_score(q_idx, idx_cache, page_table, context_lens, max_blocks=None, out=None):
-    """Block scores [B, max_blocks] int32 (entries past ceil(L_b/4) are left as they are)."""
+def index_score(q_idx, idx_cache, page_table, context_lens, max_blocks=None, out=None, page_max=None):
+    """Block scores [B, max_blocks] int32 (entries past ceil(L_b/4) are left as they are).
+
+    page_max: optional [B, max_pages] int32 output of the largest block score per page.
+    """
     _need(q_idx, torch.int8, "q_idx", 3)
     _need(idx_cache, torch.int8, "idx_cache", 4)
     _need(page_table, torch.int32, "page_table", 2)
@@ -131,23 +134,34 @@ def index_score(q_idx, idx_cache, page_table, context_lens, max_blocks=None, out
     if out is None:
         out = torch.empty((B, max_blocks), dtype=torch.int32, device=q_idx.device)
     _need(out, torch.int32, "out", 2)
+    if page_max is not None:
+        _need(page_max, torch.int32, "page_max", 2)
+        if tuple(page_max.shape) != (B, max_pages):
+            raise ValueError(f"page_max: expected {(B, max_pages)}, got {tuple(page_max.shape)}")
     _check(lib().qsa_index_score(_ptr(q_idx), _ptr(idx_cache), _ptr(page_table), _ptr(context_lens),
                                  B, q_idx.shape[1], q_idx.shape[2], idx_cache.shape[1], max_pages,
-                                 out.shape[1], _ptr(out), _stream()))
+                                 out.shape[1], _ptr(out), _ptr(page_max), _stream()))
     return out
 
 
-def topk_select(block_scores, context_lens, k=MAX_K, workspace=None, sel=None, count=None):
-    """(sel_blocks [B, k] int32 ascending, -1 padded; sel_count [B] int32)."""
+def topk_select(block_scores, context_lens, k=MAX_K, workspace=None, sel=None, count=None, page_max=None):
+    """(sel_blocks [B, k] int32 ascending, -1 padded; sel_count [B] int32).
+
+    page_max: optional [B, max_pages] int32 as written by index_score (same result, fewer reads).
+    """
     _need(block_scores, torch.int32, "block_scores", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     B, max_blocks = block_scores.shape
+    max_pages = 0
+    if page_max is not None:
+        _need(page_max, torch.int32, "page_max", 2)
+        max_pages = page_max.shape[1]
     dev = block_scores.device
     sel = torch.empty((B, k), dtype=torch.int32, device=dev) if sel is None else sel
     count = torch.empty((B,), dtype=torch.int32, device=dev) if count is None else count
     ws = workspace or Workspace(topk_workspace_size(B, max_blocks, k), dev)
-    _check(lib().qsa_topk_select(_ptr(block_scores), _ptr(context_lens), B, max_blocks, k, _ptr(sel),
-                                 _ptr(count), ws.ptr(), ws.nbytes, _stream()))
+    _check(lib().qsa_topk_select(_ptr(block_scores), _ptr(context_lens), _ptr(page_max), B, max_blocks,
+                                 max_pages, k, _ptr(sel), _ptr(count), ws.ptr(), ws.nbytes, _stream()))
     return sel, count
 
 

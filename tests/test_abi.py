@@ -42,7 +42,7 @@ def _index(L, **kw):
     a = dict(q_idx=FAKE, idx=FAKE, pt=FAKE, lens=FAKE, B=2, nh=4, dim=64, ps=64, mp=16, mb=256, out=FAKE)
     a.update(kw)
     return L.qsa_index_score(a["q_idx"], a["idx"], a["pt"], a["lens"], a["B"], a["nh"], a["dim"], a["ps"],
-                             a["mp"], a["mb"], a["out"], None)
+                             a["mp"], a["mb"], a["out"], None, None)
 
 
 def test_index_score_checks():
@@ -61,17 +61,22 @@ def test_index_score_checks():
 
 def test_topk_checks():
     L = qsa.lib()
-    f = L.qsa_topk_select
-    assert f(FAKE, FAKE, 0, 100, 512, FAKE, FAKE, None, 0, None) == OK
-    assert f(None, FAKE, 2, 100, 512, FAKE, FAKE, None, 0, None) == NULL
-    assert f(FAKE, FAKE, 2, 100, 512, None, FAKE, None, 0, None) == NULL
-    assert f(FAKE, FAKE, 2, 100, 0, FAKE, FAKE, None, 0, None) == SHAPE
-    assert f(FAKE, FAKE, -1, 100, 512, FAKE, FAKE, None, 0, None) == SHAPE
-    assert f(FAKE, FAKE, 2, 100, 513, FAKE, FAKE, None, 0, None) == UNSUP
-    assert f(FAKE, FAKE, 2, 262148, 512, FAKE, FAKE, None, 0, None) == UNSUP   # > 1M-token contexts
-    assert f(FAKE, FAKE, 2, 102, 512, FAKE, FAKE, None, 0, None) == SHAPE      # rows of 4-block vectors
-    assert f(ctypes.c_void_p(0x1004), FAKE, 2, 100, 512, FAKE, FAKE, None, 0, None) == SHAPE
-    assert L.qsa_topk_workspace_size(2, 100, 512) == 0     # one workgroup per request, no scratch
+
+    def f(scores=FAKE, lens=FAKE, pm=None, B=2, mb=100, mp=7, k=512, sel=FAKE, cnt=FAKE):
+        return L.qsa_topk_select(scores, lens, pm, B, mb, mp, k, sel, cnt, None, 0, None)
+
+    assert f(B=0) == OK
+    assert f(scores=None) == NULL
+    assert f(sel=None) == NULL
+    assert f(k=0) == SHAPE
+    assert f(B=-1) == SHAPE
+    assert f(k=513) == UNSUP
+    assert f(mb=262148) == UNSUP                         # > 1M-token contexts
+    assert f(mb=102) == SHAPE                            # rows of 4-block vectors
+    assert f(scores=ctypes.c_void_p(0x1004)) == SHAPE    # 16-byte alignment
+    assert f(pm=FAKE, mp=0) == SHAPE                     # page maxima need their row stride
+    assert f(pm=FAKE, mp=5) == SHAPE                     # 16*5 < 100 - 15: rows not covered
+    assert L.qsa_topk_workspace_size(2, 100, 512) == 0   # one workgroup per request, no scratch
 
 
 def _attn(L, **kw):
@@ -104,7 +109,7 @@ def test_merge_and_decode_checks():
     assert m(FAKE, FAKE, 2, 0, 32, 128, FAKE, None, None) == SHAPE
     assert m(FAKE, FAKE, 2, 4, 32, 64, FAKE, None, None) == UNSUP
     d = L.qsa_decode
-    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [None, 0, None]
+    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 20, None]
     bad = list(args)
     bad[1] = None                  # q_idx
     assert d(*bad) == NULL
@@ -120,7 +125,15 @@ def test_merge_and_decode_checks():
     bad = list(args)
     bad[17] = 0                    # P
     assert d(*bad) == SHAPE
+    bad = list(args)
+    bad[26], bad[27] = None, 0     # the per-page maxima need a workspace
+    assert d(*bad) == WS
+    bad = list(args)
+    bad[27] = 100                  # too small
+    assert d(*bad) == WS
     assert L.qsa_workspace_clear(None, 0, None) == OK
     assert L.qsa_workspace_clear(None, 64, None) == NULL
     assert L.qsa_workspace_clear(FAKE, 63, None) == SHAPE
-    assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) == 0
+    # the decode workspace holds the per-page maxima: B * max_blocks/16 int32, 256-byte aligned
+    assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) == 4 * 4096 * 4
+    assert L.qsa_decode_workspace_size(0, 32, 4, 65536, 512, 4) == 0

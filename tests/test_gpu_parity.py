@@ -249,9 +249,10 @@ def _scores(dist, n, rng):
     raise ValueError(dist)
 
 
+@pytest.mark.parametrize("with_page_max", [False, True])
 @pytest.mark.parametrize("max_blocks", [4096, 65536, 131072, 262144])
 @pytest.mark.parametrize("k", [1, 512])
-def test_topk_select_crafted_scores(max_blocks, k):
+def test_topk_select_crafted_scores(max_blocks, k, with_page_max):
     """qsa_topk_select alone on score rows that reach every branch of the selection."""
     rng = np.random.default_rng(max_blocks + k)
     dists = ["wide", "narrow", "equal", "increasing", "decreasing", "extreme", "two_values", "spikes"]
@@ -267,7 +268,15 @@ def test_topk_select_crafted_scores(max_blocks, k):
     say(f"[topk] max_blocks={max_blocks} k={k} lens={lens}")
     scores = torch.tensor(np.stack(rows).astype(np.int32), device="cuda")
     cl = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    sel, cnt = qsa.topk_select(scores, cl, k)
+    pm = None
+    if with_page_max:   # per-page maxima over the valid blocks, as the scan writes them
+        pmax = np.full((len(rows), max_blocks // 16), -2**31, np.int64)
+        for b, (row, L) in enumerate(zip(rows, lens)):
+            n = (L + 3) // 4
+            for p in range((n + 15) // 16):
+                pmax[b, p] = row[16 * p:min(16 * p + 16, n)].max()
+        pm = torch.tensor(pmax.astype(np.int32), device="cuda")
+    sel, cnt = qsa.topk_select(scores, cl, k, page_max=pm)
     torch.cuda.synchronize()
     sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
     for b, (row, L) in enumerate(zip(rows, lens)):
@@ -276,3 +285,26 @@ def test_topk_select_crafted_scores(max_blocks, k):
         assert cnt[b] == len(ref), f"{dists[b]}: count"
         assert np.array_equal(sel[b, :len(ref)], ref), f"{dists[b]}: kept blocks differ"
         assert np.all(sel[b, len(ref):] == -1)
+
+
+@pytest.mark.parametrize("name,lens", [("pm_u127", (70000, 2049, 33000, 65537)),
+                                       ("pm_u2", (70000, 40000, 8192, 8193))])
+def test_page_max_and_both_selection_paths(name, lens):
+    """index_score's per-page maxima are the maxima of the oracle's block scores, and the
+    selection gives the same blocks with and without them."""
+    x = make_inputs(W(name, lens, alphabet="u2" if "u2" in name else "u127"), 13, "cuda")
+    pm = torch.full((x.batch, x.max_pages), 7, dtype=torch.int32, device="cuda")
+    scores = qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, page_max=pm)
+    sel_a, cnt_a = qsa.topk_select(scores, x.context_lens)
+    sel_b, cnt_b = qsa.topk_select(scores, x.context_lens, page_max=pm)
+    torch.cuda.synchronize()
+    refs = oracle_decode(oracle, x)
+    pm_h = pm.cpu().numpy()
+    for b, r in enumerate(refs):
+        s = r["scores"]
+        want = [s[16 * p:16 * p + 16].max() for p in range((len(s) + 15) // 16)]
+        assert np.array_equal(pm_h[b, :len(want)], want), f"page maxima of request {b}"
+        K = len(r["kept"])
+        for sel, cnt in ((sel_a, cnt_a), (sel_b, cnt_b)):
+            assert int(cnt[b]) == K
+            assert np.array_equal(sel[b, :K].cpu().numpy(), r["kept"])
