@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each call from a HIP graph captured once per input set")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,10 +133,28 @@ def main():
     for i in range(args.warmup):
         plans[i % sets].run()
     torch.cuda.synchronize()
+    step = lambda i: plans[i % sets].run()
+    if args.graph:
+        ref = [(p.sel.clone(), p.out.clone()) for p in plans]
+        graphs = []
+        for p in plans:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                p.run()
+            graphs.append(g)
+        for r, g in enumerate(graphs):     # a replay must reproduce the eager call bit for bit
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(plans[r].sel, ref[r][0]) and torch.equal(plans[r].out.view(torch.int32),
+                                                                        ref[r][1].view(torch.int32))
+        step = lambda i: graphs[i % sets].replay()
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        plans[i % sets].run()
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
@@ -182,6 +202,7 @@ def main():
             "seq_len": max(lengths),
             "parallelism": f"1 GPU, P={w.slices} slices merged by LSE",
             "rotated_input_sets": sets,
+            "launch": "hip graph replay" if args.graph else "stream launches (qsa_decode per call)",
         },
         "achieved_GBps": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

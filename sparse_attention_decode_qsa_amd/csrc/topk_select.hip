@@ -42,9 +42,10 @@ constexpr int kMaxSelBlocks = 262144;            // contexts up to 1,048,576 tok
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
 
 struct SelShared {
-  uint32_t hist[kSelBins + 64];   // + one dummy bin per lane
+  uint32_t hbuf[2][kSelBins + 64];  // double-buffered histogram (+ one dummy bin per lane)
   uint32_t list_u[kListCap];
   int list_j[kListCap];
+  int cpages[kListCap];             // candidate page ids of the page-maximum path
   int scan[kSelWaves + 1];
   uint32_t red[2][kSelWaves];
   int out[4];
@@ -89,23 +90,54 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, SelShared& sh) {
   return s;
 }
 
-// Bin of the histogram holding the need-th largest key and the number of keys in the bins
-// above it; *beta = -1 when the histogram holds fewer than `need` keys.
-__device__ __forceinline__ void find_bucket(SelShared& sh, uint32_t need, int* beta, uint32_t* above) {
-  constexpr int per = kSelBins / kSelThreads;  // 2 bins per thread
-  const int t = threadIdx.x;
-  if (t == 0) { sh.out[0] = -1; sh.out[1] = 0; }
-  const uint32_t c0 = sh.hist[t * per], c1 = sh.hist[t * per + 1];
-  int total;
-  const int excl = block_exclusive_scan<kSelThreads>((int)(c0 + c1), sh.scan, &total);
-  uint32_t run = (uint32_t)(total - excl) - (c0 + c1);   // keys in bins above this thread's pair
-  if (run < need && run + c1 >= need) { sh.out[0] = t * per + 1; sh.out[1] = (int)run; }
-  run += c1;
-  if (run < need && run + c0 >= need) { sh.out[0] = t * per; sh.out[1] = (int)run; }
+// Bin of the complete histogram holding the need-th largest key and the number of keys in
+// the bins above it (*beta = -1 when it holds fewer than `need`). Wave 0 searches (each
+// lane sums 32 bins, a reverse wave scan finds the lane, that lane walks its bins) while
+// the other threads clear the other histogram buffer; then the buffers swap. Every
+// thread must call it; it costs two barriers.
+__device__ __forceinline__ void find_bucket(SelShared& sh, int& hsel, uint32_t need, int* beta,
+                                            uint32_t* above) {
+  constexpr int per = kSelBins / 64;
+  const int t = threadIdx.x, lane = lane_id();
+  const uint32_t* h = sh.hbuf[hsel];
+  uint32_t* other = sh.hbuf[hsel ^ 1];
+  if (t < 64) {
+    // Lane l sums bins [32l, 32l + 32), starting at a rotated offset so the 64 lanes read
+    // from distinct banks.
+    uint32_t c = 0;
+#pragma unroll 8
+    for (int i = 0; i < per; ++i) c += h[lane * per + ((i + lane) & (per - 1))];
+    uint32_t suf = c;   // keys in this lane's bins and all bins above
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_down((int)suf, d, 64);
+      if (lane + d < 64) suf += y;
+    }
+    const uint64_t hit = __ballot(suf - c < need && suf >= need);
+    if (hit == 0) {
+      if (lane == 0) { sh.out[0] = -1; sh.out[1] = 0; sh.out[2] = 0; }
+    } else {
+      const int L = __builtin_ctzll(hit);
+      const uint32_t runL = (uint32_t)__shfl((int)(suf - c), L, 64);   // keys in bins above lane L's
+      // The wave walks lane L's 32 bins: lanes 0..31 hold one bin each, suffix sums from the top.
+      const uint32_t v = lane < per ? h[L * per + lane] : 0u;
+      uint32_t sv = v;
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_down((int)sv, d, 64);
+        if (lane + d < per) sv += y;
+      }
+      const bool mine = lane < per && runL + sv - v < need && runL + sv >= need;
+      if (mine) { sh.out[0] = L * per + lane; sh.out[1] = (int)(runL + sv - v); sh.out[2] = (int)v; }
+    }
+  } else {
+    for (int i = t - 64; i < kSelBins + 64; i += kSelThreads - 64) other[i] = 0;
+  }
   __syncthreads();
   *beta = sh.out[0];
   *above = (uint32_t)sh.out[1];
   __syncthreads();
+  hsel ^= 1;   // every thread flips its own copy: the cleared buffer is filled next
 }
 
 __device__ __forceinline__ int shift_for(uint32_t lo, uint32_t hi) {
@@ -114,25 +146,24 @@ __device__ __forceinline__ int shift_for(uint32_t lo, uint32_t hi) {
 
 // One narrowing step on a complete histogram of the keys in [lo, hi]. Returns true when
 // the bucket's keys are exactly the ones still needed.
-__device__ __forceinline__ bool narrow_step(SelShared& sh, int shift, uint32_t* lo, uint32_t* hi,
+__device__ __forceinline__ bool narrow_step(SelShared& sh, int& hsel, int shift, uint32_t* lo, uint32_t* hi,
                                             uint32_t* need) {
   int beta;
   uint32_t above;
-  find_bucket(sh, *need, &beta, &above);
-  const uint32_t count = sh.hist[beta];
+  find_bucket(sh, hsel, *need, &beta, &above);
+  const uint32_t count = (uint32_t)sh.out[2];
   const uint32_t nlo = *lo + ((uint32_t)beta << shift);
   const uint32_t span = (1u << shift) - 1u;
   *hi = (*hi - nlo < span) ? *hi : nlo + span;
   *lo = nlo;
   *need -= above;
-  __syncthreads();
   return count == *need;
 }
 
 // Narrow [lo, hi] over the LDS candidate list (all candidates are >= lo), then write the
 // kept and tie masks of the candidates into the per-chunk words.
 template <int R>
-__device__ __forceinline__ void narrow_list_and_mark(SelShared& sh, uint32_t ncand, uint32_t lo, uint32_t hi,
+__device__ __forceinline__ void narrow_list_and_mark(SelShared& sh, int& hsel, uint32_t ncand, uint32_t lo, uint32_t hi,
                                                      uint32_t* need_io, bool* all_io, uint32_t* lo_out,
                                                      uint64_t* kept_w, uint64_t* tie_w) {
   const int t = threadIdx.x;
@@ -140,14 +171,12 @@ __device__ __forceinline__ void narrow_list_and_mark(SelShared& sh, uint32_t nca
   bool all_of_bucket = false;
   while (lo != hi) {
     const int shift = shift_for(lo, hi);
-    for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
-    __syncthreads();
     for (int i = t; i < (int)ncand; i += kSelThreads) {
       const uint32_t u = sh.list_u[i];
-      if (u >= lo && u <= hi) atomicAdd(&sh.hist[(u - lo) >> shift], 1u);
+      if (u >= lo && u <= hi) atomicAdd(&sh.hbuf[hsel][(u - lo) >> shift], 1u);
     }
     __syncthreads();
-    if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
+    if (narrow_step(sh, hsel, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) { kept_w[t + kSelThreads * r] = 0; tie_w[t + kSelThreads * r] = 0; }
@@ -193,10 +222,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   bool all_of_bucket = false;
   bool masks_done = false;
   uint32_t lo = 0, hi = 0;
+  int hsel = 0;   // histogram buffer being filled; the other one is cleared by find_bucket
+  for (int i = t; i < kSelBins + 64; i += kSelThreads) sh.hbuf[0][i] = 0;
+  __syncthreads();
 
-  // A. Page maxima (when given and there are at least k pages): tau = the k-th largest
-  // page maximum. At least k pages reach it, each with a block >= tau, so the k-th key is
-  // >= tau; only the blocks of pages reaching tau can be candidates.
+  // A. Page maxima (when given and there are at least k pages): one histogram of the page
+  // maxima over [min, max]; tau = the lower edge of the bin holding the k-th largest. At
+  // least k pages reach tau, each with a block >= tau, so the k-th key is >= tau, and only
+  // the blocks of pages reaching tau can be kept.
   const int np = (n + kBlocksPerPage - 1) / kBlocksPerPage;
   bool have_list = false;
   uint32_t ncand = 0;
@@ -215,48 +248,70 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     uint32_t plo, phi;
     block_minmax(mn, mx, sh, &plo, &phi);
     hi = phi;                                    // the largest page maximum is the largest key
-    uint32_t pneed = (uint32_t)k;
-    while (plo != phi) {
+    uint32_t tau = plo;
+    if (plo != phi) {
       const int shift = shift_for(plo, phi);
-      for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
-      __syncthreads();
-      const uint32_t clo = plo, span_all = phi - plo;
 #pragma unroll
-      for (int i = 0; i < PV; ++i) {
-        const uint32_t d = pv[i] - clo;
-        atomicAdd(&sh.hist[((t + kSelThreads * i < np) & (d <= span_all)) ? d >> shift : dummy], 1u);
-      }
+      for (int i = 0; i < PV; ++i)
+        atomicAdd(&sh.hbuf[hsel][t + kSelThreads * i < np ? (pv[i] - plo) >> shift : dummy], 1u);
       __syncthreads();
-      if (narrow_step(sh, shift, &plo, &phi, &pneed)) break;
+      int beta;
+      uint32_t above;
+      find_bucket(sh, hsel, (uint32_t)k, &beta, &above);
+      tau = plo + ((uint32_t)beta << shift);
     }
-    const uint32_t tau = plo;
-    // B. candidate blocks of the pages that reach tau.
+    // B. candidate pages (pm >= tau) in page order, then their candidate blocks: every wave
+    // takes 4 pages per step, 16 lanes per page, one coalesced load per lane, and reserves
+    // list slots with one LDS atomic per step.
+    uint32_t flags = 0;
+#pragma unroll
+    for (int i = 0; i < PV; ++i) flags |= (uint32_t)((t + kSelThreads * i < np) & (pv[i] >= tau)) << i;
+    int ncp;
+    const int cp0 = block_exclusive_scan<kSelThreads>(__builtin_popcount(flags), sh.scan, &ncp);
+    int* cpages = sh.cpages;
+    if (ncp <= kListCap) {
+      int w = cp0;
+#pragma unroll
+      for (int i = 0; i < PV; ++i)
+        if ((flags >> i) & 1u) cpages[w++] = t + kSelThreads * i;
+    }
     if (t == 0) sh.list_n = 0;
     __syncthreads();
+    if (ncp <= kListCap) {
+      // Steps of 4 pages per wave; each batch issues its 8 steps' loads before appending.
+      const int wave = t >> 6, sub = lane >> 4, col = lane & 15;
+      constexpr int kBatch = 8;
+      const int nsteps = (ncp + 4 * kSelWaves - 1) / (4 * kSelWaves);
+      for (int st0 = 0; st0 < nsteps; st0 += kBatch) {
+        int cj[kBatch];
+        uint32_t cu[kBatch];
 #pragma unroll
-    for (int i = 0; i < PV; ++i) {
-      const int pidx = t + kSelThreads * i;
-      if (pidx < np && pv[i] >= tau) {
-        const i32x4* row = reinterpret_cast<const i32x4*>(s + kBlocksPerPage * pidx);
+        for (int q = 0; q < kBatch; ++q) {
+          const int ci = ((st0 + q) * kSelWaves + wave) * 4 + sub;
+          cj[q] = -1;
+          cu[q] = 0;
+          if (st0 + q < nsteps && ci < ncp) {
+            const int j = kBlocksPerPage * cpages[ci] + col;
+            if (j < n) { cj[q] = j; cu[q] = score_key(s[j]); }
+          }
+        }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          if (kBlocksPerPage * pidx + 4 * m >= n) break;   // vectors past block n stay unread
-          const i32x4 v = row[m];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = kBlocksPerPage * pidx + 4 * m + e;
-            const uint32_t u = score_key(v[e]);
-            if (j < n && u >= tau) {
-              const int slot = atomicAdd(&sh.list_n, 1);
-              if (slot < kListCap) { sh.list_u[slot] = u; sh.list_j[slot] = j; }
-            }
+        for (int q = 0; q < kBatch; ++q) {
+          const bool c = cj[q] >= 0 && cu[q] >= tau;
+          const uint64_t m = __ballot(c);
+          int base = 0;
+          if (lane == 0 && m) base = atomicAdd(&sh.list_n, __builtin_popcountll(m));
+          base = __shfl(base, 0, 64);
+          if (c) {
+            const int slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+            if (slot < kListCap) { sh.list_u[slot] = cu[q]; sh.list_j[slot] = cj[q]; }
           }
         }
       }
     }
     __syncthreads();
     ncand = (uint32_t)sh.list_n;
-    if (ncand <= (uint32_t)kListCap) {
+    if (ncp <= kListCap && ncand <= (uint32_t)kListCap) {
       have_list = true;
       lo = tau;
     }
@@ -306,8 +361,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     if (lo != hi) {
       // sample: keys 0, 16, 32, 48 of every chunk.
       int shift = shift_for(lo, hi);
-      for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
-      __syncthreads();
       uint32_t mine = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -315,16 +368,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         for (int e = 0; e < kChunk; e += 16) {
           const bool ok = e < nv[r];
           mine += ok;
-          atomicAdd(&sh.hist[ok ? (key(r, e) - lo) >> shift : dummy], 1u);
+          atomicAdd(&sh.hbuf[hsel][ok ? (key(r, e) - lo) >> shift : dummy], 1u);
         }
       const uint32_t nsamp = block_sum(mine, sh);
       const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
       uint32_t tau = lo;
-      if (need_s < nsamp) {
+      {
         int bs;
         uint32_t ab;
-        find_bucket(sh, need_s, &bs, &ab);
-        if (bs >= 0) tau = lo + ((uint32_t)bs << shift);
+        find_bucket(sh, hsel, need_s, &bs, &ab);   // always: it also clears the next buffer
+        if (need_s < nsamp && bs >= 0) tau = lo + ((uint32_t)bs << shift);
       }
       // candidates u >= tau.
       uint64_t cand[R];
@@ -359,18 +412,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         // narrow over every key (branch-free: uncounted keys go to the lane's dummy bin).
         while (lo != hi) {
           shift = shift_for(lo, hi);
-          for (int i = t; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
-          __syncthreads();
           const uint32_t clo = lo, span_all = hi - lo;
 #pragma unroll
           for (int r = 0; r < R; ++r)
 #pragma unroll kU
             for (int e = 0; e < kChunk; ++e) {
               const uint32_t d = key(r, e) - clo;
-              atomicAdd(&sh.hist[((e < nv[r]) & (d <= span_all)) ? d >> shift : dummy], 1u);
+              atomicAdd(&sh.hbuf[hsel][((e < nv[r]) & (d <= span_all)) ? d >> shift : dummy], 1u);
             }
           __syncthreads();
-          if (narrow_step(sh, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
+          if (narrow_step(sh, hsel, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
         }
       }
     }
@@ -393,7 +444,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   }
   if (have_list && !masks_done) {
     uint32_t llo = lo;
-    narrow_list_and_mark<R>(sh, ncand, lo, hi, &need, &all_of_bucket, &llo, kept_w, tie_w);
+    narrow_list_and_mark<R>(sh, hsel, ncand, lo, hi, &need, &all_of_bucket, &llo, kept_w, tie_w);
     lo = llo;
   }
   __syncthreads();
