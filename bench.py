@@ -14,6 +14,7 @@ own with HIP events on the stream it runs on) and the CPU oracle's rate on the s
 workload.
 
     python bench.py [--steps K] [--warmup W] [--workload w4] [--sets R] [--no-cpu-baseline]
+                    [--graph] [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -99,6 +100,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each call from a HIP graph captured once per input set")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run 3 plain device copies of MIB MiB each, so that hardware "
+                         "byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -219,6 +223,14 @@ def main():
             "bytes_per_launch": k1_bytes,
         },
     }
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: 3 copies of {n} bytes (read {n}, write {n} each)", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on the same workload", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inputs[0])

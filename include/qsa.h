@@ -40,10 +40,11 @@
  *              (page ids in range, lengths within the page table) are the caller's and
  *              are not checked. No C++ exception crosses this interface.
  *   Workspace  entry points that take a workspace need qsa_*_workspace_size() bytes,
- *              16-byte aligned; when that size is 0 the pointer may be NULL. No kernel of
- *              this version keeps scratch between workgroups or between calls, so a
- *              workspace needs no initialisation. Calls that share a workspace must not
- *              overlap in time.
+ *              16-byte aligned; when that size is 0 the pointer may be NULL. A workspace
+ *              carries intermediates from one kernel of a call to the next; every byte a
+ *              kernel reads was written earlier in the same call, so a workspace needs no
+ *              initialisation and keeps nothing between calls. Calls that share a
+ *              workspace must not overlap in time.
  *   Threads    stateless and re-entrant apart from the thread-local qsa_last_hip_error.
  */
 #ifndef QSA_H_
@@ -147,7 +148,12 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
  *   P            slices per request, 1 <= P <= 64
  *   partial_out  out [B, P, Hq, head_dim] float32 (each slice normalised on its own)
  *   partial_lse  out [B, P, Hq] float32, natural log
- *   workspace    qsa_attn_workspace_size(B, Hq, Hkv, k, P) bytes (see Workspace)
+ *   workspace    qsa_attn_workspace_size(B, Hq, Hkv, k, P) bytes (see Workspace). Each
+ *                slice's kept tokens are split into C shares attended in parallel, C the
+ *                largest power of two <= min(8, ceil(512 / (B*Hkv*P))) (at least 1); the
+ *                workspace holds the share partials, B*P*C*Hq*head_dim + B*P*C*Hq floats
+ *                (each part rounded up to 256 bytes), which are merged into the slice
+ *                partials by log-sum-exp.
  */
 size_t qsa_attn_workspace_size(int B, int Hq, int Hkv, int k, int P);
 qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -181,7 +187,11 @@ qsa_status_t qsa_lse_merge(const float* partial_out, const float* partial_lse,
  * Arguments as in the four calls above. block_scores, sel_blocks, sel_count,
  * partial_out and partial_lse are still caller buffers, so the intermediates stay
  * inspectable; out_lse may be NULL. The workspace (qsa_decode_workspace_size bytes, no
- * initialisation needed) holds the per-page maxima passed from the scan to the selection.
+ * initialisation needed) holds the per-page maxima passed from the scan to the selection
+ * (B * ceil(max_blocks/16) int32, rounded up to 256 bytes), then the attention workspace.
+ * The slice partials and the merged output are formed by one kernel, with the same
+ * operations as qsa_lse_merge, so the results equal those of the four separate calls bit
+ * for bit.
  */
 size_t qsa_decode_workspace_size(int B, int Hq, int Hkv, int max_blocks, int k, int P);
 qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache,

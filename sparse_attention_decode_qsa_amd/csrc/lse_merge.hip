@@ -1,4 +1,4 @@
-// lse_merge.hip - K4: log-sum-exp merge of the P slice partials.
+// lse_merge.hip - K4: log-sum-exp merge of partial attention results.
 //
 // Article "Qwen 4 QSA gets decode context parallelism: inside vLLM's draft PR for
 // Qwen3.8-Flash-Next", section "What the pull request actually changes" (bullets) and
@@ -7,10 +7,17 @@
 // finite slice lse and w_p = exp(lse_p - M):
 //     out = sum_p w_p o_p / sum_p w_p,   lse = M + ln(sum_p w_p)
 // Slices with lse = -inf carry no weight; with none finite, out = 0 and lse = -inf.
+//
+// lse_merge_kernel merges given slice partials. slice_merge_kernel first forms every slice
+// partial from the partials of its C shares (the same formula over the shares), writes it,
+// and then merges the slices exactly as lse_merge_kernel does (same operations in the same
+// order), so the fused chain and the separate calls give the same bits.
 // One workgroup per (head, request), one thread per output dim.
 #include "qsa_device.h"
 
 namespace qsa {
+
+constexpr int kMaxShares = 8;   // shares per slice (at most the attention kernel's split)
 
 __global__ __launch_bounds__(kHeadDim) void lse_merge_kernel(const float* __restrict__ po,
                                                              const float* __restrict__ pl, int P,
@@ -22,22 +29,193 @@ __global__ __launch_bounds__(kHeadDim) void lse_merge_kernel(const float* __rest
   for (int p = 0; p < P; ++p) M = fmaxf(M, lse[(size_t)p * Hq]);
   float wsum = 0.f, acc = 0.f;
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int p = 0; p < P; ++p) {
+      const float v = po[(((size_t)b * P + p) * Hq + h) * kHeadDim + d];   // loaded in batches
       const float l = lse[(size_t)p * Hq];
       if (l == -INFINITY) continue;
       const float w = __expf(l - M);
       wsum += w;
-      acc += w * po[(((size_t)b * P + p) * Hq + h) * kHeadDim + d];
+      acc += w * v;
     }
   }
   out[((size_t)b * Hq + h) * kHeadDim + d] = wsum > 0.f ? acc / wsum : 0.f;
   if (out_lse && d == 0) out_lse[(size_t)b * Hq + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
+// so [B, P, C, Hq, 128], sl [B, P, C, Hq] -> part_out [B, P, Hq, 128], part_lse [B, P, Hq];
+// then, when out != NULL, out [B, Hq, 128] and (when out_lse != NULL) out_lse [B, Hq].
+// Slice p: Mp = max_c lse_pc, w_c = exp(lse_pc - Mp) over the finite shares,
+//   part_out = sum_c w_c o_pc / sum_c w_c,  part_lse = Mp + ln(sum_c w_c)   (0, -inf if none)
+// then the slices are merged with the operations of lse_merge_kernel, in the same order.
+constexpr int kFastShares = 32;
+
+// P * C <= kFastShares: each thread loads every share lse (same address in all threads)
+// and every share value of its dim at entry, and combines them in registers.
+template <int C>
+__device__ __forceinline__ void slice_merge_regs(const float* __restrict__ so, const float* __restrict__ sl,
+                                                 int P, int Hq, int h, int b, int d, float* __restrict__ part_out,
+                                                 float* __restrict__ part_lse, float* __restrict__ out,
+                                                 float* __restrict__ out_lse) {
+  constexpr int PM = kFastShares / C;
+  const int n = P * C;
+  const float* col = so + ((size_t)b * n * Hq + h) * kHeadDim + d;   // share i at col[i * Hq * 128]
+  const float* lcol = sl + (size_t)b * n * Hq + h;                   // share i at lcol[i * Hq]
+  const size_t stride = (size_t)Hq * kHeadDim;
+  float lv[kFastShares], v[kFastShares];
+#pragma unroll
+  for (int i = 0; i < kFastShares; ++i) {
+    lv[i] = i < n ? lcol[(size_t)i * Hq] : -INFINITY;
+    v[i] = i < n ? col[i * stride] : 0.f;
+  }
+  float mp[PM], lp[PM];
+#pragma unroll
+  for (int p = 0; p < PM; ++p) {
+    float Mp = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < C; ++c) Mp = fmaxf(Mp, lv[p * C + c]);
+    float ws = 0.f;
+    if (Mp != -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (lv[p * C + c] != -INFINITY) ws += __expf(lv[p * C + c] - Mp);
+    }
+    mp[p] = Mp;
+    lp[p] = ws > 0.f ? Mp + __logf(ws) : -INFINITY;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < PM; ++p) M = fmaxf(M, lp[p]);   // slices past P hold -inf
+  float wsum = 0.f, acc = 0.f;
+#pragma unroll
+  for (int p = 0; p < PM; ++p) {
+    if (p >= P) break;
+    float ws = 0.f, a = 0.f;
+    if (mp[p] != -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const float l = lv[p * C + c];
+        if (l == -INFINITY) continue;
+        const float w = __expf(l - mp[p]);
+        ws += w;
+        a += w * v[p * C + c];
+      }
+    }
+    const float o = ws > 0.f ? a / ws : 0.f;
+    part_out[(((size_t)b * P + p) * Hq + h) * kHeadDim + d] = o;
+    if (d == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp[p];
+    if (M != -INFINITY && lp[p] != -INFINITY) {
+      const float w = __expf(lp[p] - M);
+      wsum += w;
+      acc += w * o;
+    }
+  }
+  if (out) {
+    out[((size_t)b * Hq + h) * kHeadDim + d] = wsum > 0.f ? acc / wsum : 0.f;
+    if (out_lse && d == 0) out_lse[(size_t)b * Hq + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+  }
+}
+
+// Any P * C: the share lse values go through LDS, and slice p+1's share values are loaded
+// while slice p is combined.
+__device__ __forceinline__ void slice_merge_lds(const float* __restrict__ so, const float* __restrict__ sl,
+                                                int P, int C, int Hq, int h, int b, int d,
+                                                float* __restrict__ part_out, float* __restrict__ part_lse,
+                                                float* __restrict__ out, float* __restrict__ out_lse) {
+  const int n = P * C;
+  const float* col = so + ((size_t)b * n * Hq + h) * kHeadDim + d;
+  const size_t stride = (size_t)Hq * kHeadDim;
+  __shared__ float s_share_lse[kMaxSlices * kMaxShares];
+  __shared__ float s_slice_max[kMaxSlices];
+  __shared__ float s_slice_lse[kMaxSlices];
+  for (int i = d; i < n; i += kHeadDim) s_share_lse[i] = sl[((size_t)b * n + i) * Hq + h];
+  __syncthreads();
+  if (d < P) {
+    float Mp = -INFINITY;
+    for (int c = 0; c < C; ++c) Mp = fmaxf(Mp, s_share_lse[d * C + c]);
+    float ws = 0.f;
+    if (Mp != -INFINITY)
+      for (int c = 0; c < C; ++c) {
+        const float l = s_share_lse[d * C + c];
+        if (l != -INFINITY) ws += __expf(l - Mp);
+      }
+    s_slice_max[d] = Mp;
+    s_slice_lse[d] = ws > 0.f ? Mp + __logf(ws) : -INFINITY;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, s_slice_lse[p]);
+  float cur[kMaxShares], nxt[kMaxShares];
+#pragma unroll
+  for (int c = 0; c < kMaxShares; ++c) cur[c] = c < C ? col[c * stride] : 0.f;
+  float wsum = 0.f, acc = 0.f;
+  for (int p = 0; p < P; ++p) {
+    if (p + 1 < P) {
+#pragma unroll
+      for (int c = 0; c < kMaxShares; ++c) nxt[c] = c < C ? col[((size_t)(p + 1) * C + c) * stride] : 0.f;
+    }
+    const float Mp = s_slice_max[p];
+    float ws = 0.f, a = 0.f;
+    if (Mp != -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < kMaxShares; ++c) {
+        if (c >= C) break;
+        const float l = s_share_lse[p * C + c];
+        if (l == -INFINITY) continue;
+        const float w = __expf(l - Mp);
+        ws += w;
+        a += w * cur[c];
+      }
+    }
+    const float o = ws > 0.f ? a / ws : 0.f;
+    const float lp = s_slice_lse[p];
+    part_out[(((size_t)b * P + p) * Hq + h) * kHeadDim + d] = o;
+    if (d == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp;
+    if (M != -INFINITY && lp != -INFINITY) {
+      const float w = __expf(lp - M);
+      wsum += w;
+      acc += w * o;
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxShares; ++c) cur[c] = nxt[c];
+  }
+  if (out) {
+    out[((size_t)b * Hq + h) * kHeadDim + d] = wsum > 0.f ? acc / wsum : 0.f;
+    if (out_lse && d == 0) out_lse[(size_t)b * Hq + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+  }
+}
+
+// C is 1, 2, 4 or 8.
+__global__ __launch_bounds__(kHeadDim) void slice_merge_kernel(const float* __restrict__ so,
+                                                               const float* __restrict__ sl, int P, int C,
+                                                               int Hq, float* __restrict__ part_out,
+                                                               float* __restrict__ part_lse,
+                                                               float* __restrict__ out,
+                                                               float* __restrict__ out_lse) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  if (P * C <= kFastShares) {
+    switch (C) {
+      case 1: slice_merge_regs<1>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
+      case 2: slice_merge_regs<2>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
+      case 4: slice_merge_regs<4>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
+      default: slice_merge_regs<8>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
+    }
+  }
+  slice_merge_lds(so, sl, P, C, Hq, h, b, d, part_out, part_lse, out, out_lse);
+}
+
 hipError_t launch_lse_merge(const float* po, const float* pl, int B, int P, int Hq, float* out,
                             float* out_lse, hipStream_t stream) {
   hipLaunchKernelGGL(lse_merge_kernel, dim3(Hq, B), dim3(kHeadDim), 0, stream, po, pl, P, Hq, out,
                      out_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_slice_merge(const float* so, const float* sl, int B, int P, int C, int Hq, float* part_out,
+                              float* part_lse, float* out, float* out_lse, hipStream_t stream) {
+  if ((C != 1 && C != 2 && C != 4 && C != 8) || P > kMaxSlices) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(slice_merge_kernel, dim3(Hq, B), dim3(kHeadDim), 0, stream, so, sl, P, C, Hq, part_out,
+                     part_lse, out, out_lse);
   return hipGetLastError();
 }
 

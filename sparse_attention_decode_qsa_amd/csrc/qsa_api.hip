@@ -10,10 +10,10 @@ size_t topk_workspace_bytes(int B, int max_blocks);
 constexpr int kMaxSelBlocks = 262144;
 hipError_t launch_topk_select(const int32_t*, const int32_t*, const int32_t*, int, int, int, int, int32_t*,
                               int32_t*, hipStream_t);
-size_t attn_workspace_bytes(int B, int Hkv, int k, int P);
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int P);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const int32_t*, const int32_t*,
                               const int32_t*, const int32_t*, int, int, int, int, int, int, float, float*,
-                              float*, void*, hipStream_t);
+                              float*, float*, float*, void*, hipStream_t);
 hipError_t launch_lse_merge(const float*, const float*, int, int, int, float*, float*, hipStream_t);
 
 namespace {
@@ -97,8 +97,6 @@ qsa_status_t check_merge(const float* po, const float* pl, int B, int P, int Hq,
   return QSA_OK;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 // A workspace of `need` bytes: may be NULL when nothing is needed.
 bool workspace_ok(const void* ws, size_t have, size_t need) {
   return need == 0 || (ws != nullptr && have >= need);
@@ -166,9 +164,8 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
 }
 
 size_t qsa_attn_workspace_size(int B, int Hq, int Hkv, int k, int P) {
-  (void)Hq;
-  if (B <= 0 || Hkv <= 0 || k <= 0 || P <= 0) return 0;
-  return attn_workspace_bytes(B, Hkv, k, P);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || k <= 0 || P <= 0) return 0;
+  return attn_workspace_bytes(B, Hq, Hkv, P);
 }
 
 qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -181,10 +178,12 @@ qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const vo
                                Hq, Hkv, head_dim, page_size, max_pages_per_seq, k, P, partial_out,
                                partial_lse);
   if (st != QSA_OK || B == 0) return st;
-  if (!workspace_ok(workspace, workspace_bytes, attn_workspace_bytes(B, Hkv, k, P))) return QSA_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, attn_workspace_bytes(B, Hq, Hkv, P))) return QSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return QSA_ERR_SHAPE;
   return hip_status(launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks,
                                        sel_count, B, Hq, Hkv, max_pages_per_seq, k, P, softmax_scale,
-                                       partial_out, partial_lse, workspace, (hipStream_t)stream));
+                                       partial_out, partial_lse, nullptr, nullptr, workspace,
+                                       (hipStream_t)stream));
 }
 
 qsa_status_t qsa_lse_merge(const float* partial_out, const float* partial_lse, int B, int P, int Hq,
@@ -195,7 +194,8 @@ qsa_status_t qsa_lse_merge(const float* partial_out, const float* partial_lse, i
 }
 
 // qsa_decode's workspace: the per-page maxima [B, max_blocks/16] int32 (written by the
-// indexer scan, read by the selection), then the (empty) attention workspace.
+// indexer scan, read by the selection), then the attention workspace (partials of the
+// shares of every slice, written by the attention kernel, read by the merge).
 size_t decode_pm_bytes(int B, int max_blocks) {
   return align256((size_t)B * ((max_blocks + kBlocksPerPage - 1) / kBlocksPerPage) * sizeof(int32_t));
 }
@@ -223,7 +223,7 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
   if (st != QSA_OK || B == 0) return st;
   const size_t pmb = decode_pm_bytes(B, max_blocks);
   const size_t tb = align256(topk_workspace_bytes(B, max_blocks));
-  if (!workspace_ok(workspace, workspace_bytes, pmb + tb + attn_workspace_bytes(B, Hkv, k, P)))
+  if (!workspace_ok(workspace, workspace_bytes, pmb + tb + attn_workspace_bytes(B, Hq, Hkv, P)))
     return QSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return QSA_ERR_SHAPE;
   int32_t* page_max = static_cast<int32_t*>(workspace);   // [B, max_pages_per_seq] fits: 16*max_pages <= max_blocks
@@ -238,9 +238,8 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                            sel_blocks, sel_count, s);
   if (e == hipSuccess)
     e = launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
-                           max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse,
+                           max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse, out, out_lse,
                            ws_attn, s);
-  if (e == hipSuccess) e = launch_lse_merge(partial_out, partial_lse, B, P, Hq, out, out_lse, s);
   return hip_status(e);
 }
 

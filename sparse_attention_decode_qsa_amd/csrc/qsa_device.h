@@ -20,6 +20,9 @@ constexpr int kMaxK = 512;                    // kept blocks
 constexpr int kMaxGroup = 16;                 // query heads per KV head (MFMA rows)
 constexpr int kMaxSlices = 64;
 
+// Host-side: byte counts of workspace regions are rounded up to 256.
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

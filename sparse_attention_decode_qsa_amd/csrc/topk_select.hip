@@ -260,52 +260,84 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       find_bucket(sh, hsel, (uint32_t)k, &beta, &above);
       tau = plo + ((uint32_t)beta << shift);
     }
-    // B. candidate pages (pm >= tau) in page order, then their candidate blocks: every wave
-    // takes 4 pages per step, 16 lanes per page, one coalesced load per lane, and reserves
-    // list slots with one LDS atomic per step.
+    // B. candidate pages (pm >= tau), then their candidate blocks: each page is read by 4
+    // lanes with one 16-byte load each, a wave takes 16 pages per step, and all steps' loads
+    // (up to 1024 pages) are issued before any key is appended; a wave reserves list slots
+    // with one LDS atomic per key position. Order in the list does not matter.
     uint32_t flags = 0;
 #pragma unroll
     for (int i = 0; i < PV; ++i) flags |= (uint32_t)((t + kSelThreads * i < np) & (pv[i] >= tau)) << i;
-    int ncp;
-    const int cp0 = block_exclusive_scan<kSelThreads>(__builtin_popcount(flags), sh.scan, &ncp);
-    int* cpages = sh.cpages;
-    if (ncp <= kListCap) {
-      int w = cp0;
-#pragma unroll
-      for (int i = 0; i < PV; ++i)
-        if ((flags >> i) & 1u) cpages[w++] = t + kSelThreads * i;
-    }
-    if (t == 0) sh.list_n = 0;
+    if (t == 0) { sh.list_n = 0; sh.out[3] = 0; }
     __syncthreads();
+    {
+      // compact the candidate page ids: one LDS reservation per wave and page slot
+#pragma unroll
+      for (int i = 0; i < PV; ++i) {
+        const bool c = (flags >> i) & 1u;
+        const uint64_t m = __ballot(c);
+        int base = 0;
+        if (lane == 0 && m) base = atomicAdd(&sh.out[3], __builtin_popcountll(m));
+        base = __shfl(base, 0, 64);
+        const int slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+        if (c && slot < kListCap) sh.cpages[slot] = t + kSelThreads * i;
+      }
+    }
+    __syncthreads();
+    const int ncp = sh.out[3];
     if (ncp <= kListCap) {
-      // Steps of 4 pages per wave; each batch issues its 8 steps' loads before appending.
-      const int wave = t >> 6, sub = lane >> 4, col = lane & 15;
-      constexpr int kBatch = 8;
-      const int nsteps = (ncp + 4 * kSelWaves - 1) / (4 * kSelWaves);
+      const int wave = t >> 6, sub = lane >> 2, q4 = lane & 3;
+      constexpr int kPagesPerStep = 16 * kSelWaves;
+      constexpr int kBatch = 4;
+      const int nsteps = (ncp + kPagesPerStep - 1) / kPagesPerStep;
       for (int st0 = 0; st0 < nsteps; st0 += kBatch) {
-        int cj[kBatch];
-        uint32_t cu[kBatch];
+        int j0[kBatch];
+        i32x4 v[kBatch];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-          const int ci = ((st0 + q) * kSelWaves + wave) * 4 + sub;
-          cj[q] = -1;
-          cu[q] = 0;
+          const int ci = (st0 + q) * kPagesPerStep + wave * 16 + sub;
+          j0[q] = -1;
+          v[q] = i32x4{0, 0, 0, 0};
           if (st0 + q < nsteps && ci < ncp) {
-            const int j = kBlocksPerPage * cpages[ci] + col;
-            if (j < n) { cj[q] = j; cu[q] = score_key(s[j]); }
+            const int j = kBlocksPerPage * sh.cpages[ci] + 4 * q4;
+            if (j < n) { j0[q] = j; v[q] = *reinterpret_cast<const i32x4*>(s + j); }
           }
         }
+        // Lane candidates (0..4 per load) -> wave prefix from the 3 bits of each count,
+        // then one list reservation per wave for the whole batch.
+        uint32_t cm[kBatch];
+        int pre[kBatch], tot[kBatch], all = 0;
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-          const bool c = cj[q] >= 0 && cu[q] >= tau;
-          const uint64_t m = __ballot(c);
-          int base = 0;
-          if (lane == 0 && m) base = atomicAdd(&sh.list_n, __builtin_popcountll(m));
-          base = __shfl(base, 0, 64);
-          if (c) {
-            const int slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
-            if (slot < kListCap) { sh.list_u[slot] = cu[q]; sh.list_j[slot] = cj[q]; }
+          uint32_t m4 = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            m4 |= (uint32_t)(j0[q] >= 0 && j0[q] + e < n && score_key(v[q][e]) >= tau) << e;
+          cm[q] = m4;
+          const int cnt = __builtin_popcount(m4);
+          int pf = 0, tt = 0;
+#pragma unroll
+          for (int bit = 0; bit < 3; ++bit) {
+            const uint64_t bm = __ballot((cnt >> bit) & 1);
+            pf += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << bit;
+            tt += __builtin_popcountll(bm) << bit;
           }
+          pre[q] = pf;
+          tot[q] = tt;
+          all += tt;
+        }
+        int base = 0;
+        if (lane == 0 && all) base = atomicAdd(&sh.list_n, all);
+        base = __shfl(base, 0, 64);
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          int slot = base + pre[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((cm[q] >> e) & 1u) {
+              if (slot < kListCap) { sh.list_u[slot] = score_key(v[q][e]); sh.list_j[slot] = j0[q] + e; }
+              ++slot;
+            }
+          base += tot[q];
         }
       }
     }

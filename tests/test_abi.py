@@ -98,7 +98,31 @@ def test_attention_checks():
     assert _attn(L, Hq=68, Hkv=4) == UNSUP         # group of 17 > 16 MFMA rows
     assert _attn(L, D=64) == UNSUP
     assert _attn(L, k=600) == UNSUP
-    assert L.qsa_attn_workspace_size(2, 32, 4, 512, 4) == 0
+    assert _attn(L, ws=None, nbytes=0) == WS       # the share partials need a workspace
+    assert _attn(L, nbytes=attn_ws(2, 32, 4, 4) - 1) == WS
+    # share partials of C shares per slice
+    assert [attn_split(B, 4, 4) for B in (1, 2, 3, 5, 8, 16, 32, 128)] == [8, 8, 8, 4, 4, 2, 1, 1]
+    assert L.qsa_attn_workspace_size(2, 32, 4, 512, 4) == attn_ws(2, 32, 4, 4)
+    assert L.qsa_attn_workspace_size(128, 32, 4, 512, 4) == attn_ws(128, 32, 4, 4)   # C = 1
+    assert L.qsa_attn_workspace_size(0, 32, 4, 512, 4) == 0
+
+
+def align256(n):
+    return (n + 255) // 256 * 256
+
+
+def attn_split(B, Hkv, P):
+    """Shares per slice: largest power of two <= min(8, ceil(512 / (B*Hkv*P))), at least 1."""
+    want = min(8, -(-512 // (B * Hkv * P)))
+    c = 1
+    while 2 * c <= want:
+        c *= 2
+    return c
+
+
+def attn_ws(B, Hq, Hkv, P):
+    C = attn_split(B, Hkv, P)
+    return align256(B * P * C * Hq * 128 * 4) + align256(B * P * C * Hq * 4)
 
 
 def test_merge_and_decode_checks():
@@ -109,7 +133,7 @@ def test_merge_and_decode_checks():
     assert m(FAKE, FAKE, 2, 0, 32, 128, FAKE, None, None) == SHAPE
     assert m(FAKE, FAKE, 2, 4, 32, 64, FAKE, None, None) == UNSUP
     d = L.qsa_decode
-    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 20, None]
+    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 24, None]
     bad = list(args)
     bad[1] = None                  # q_idx
     assert d(*bad) == NULL
@@ -134,6 +158,7 @@ def test_merge_and_decode_checks():
     assert L.qsa_workspace_clear(None, 0, None) == OK
     assert L.qsa_workspace_clear(None, 64, None) == NULL
     assert L.qsa_workspace_clear(FAKE, 63, None) == SHAPE
-    # the decode workspace holds the per-page maxima: B * max_blocks/16 int32, 256-byte aligned
-    assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) == 4 * 4096 * 4
+    # the decode workspace: per-page maxima (B * max_blocks/16 int32, 256-byte aligned), then
+    # the attention workspace
+    assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) == 4 * 4096 * 4 + attn_ws(4, 32, 4, 4)
     assert L.qsa_decode_workspace_size(0, 32, 4, 65536, 512, 4) == 0

@@ -150,6 +150,37 @@ def test_slice_counts(P):
     check_whole(make_inputs(W("P", (50000, 9000, 129)), 9, "cuda"), P=P, what=f"P{P}")
 
 
+@pytest.mark.parametrize("B,hkv,P,C", [(64, 4, 2, 1), (32, 4, 2, 2), (13, 4, 2, 4), (3, 4, 3, 8), (1, 4, 8, 8)])
+def test_share_counts(B, hkv, P, C):
+    """Batch shapes whose attention launch splits every slice into C = 1, 2, 4, 8 shares (the
+    last one, P*C = 64, merges the shares through LDS instead of registers)."""
+    want = min(8, -(-512 // (B * hkv * P)))
+    assert max(c for c in (1, 2, 4, 8) if c <= want) == C
+    rng = random.Random(B)
+    lens = tuple(rng.choice([0, 5, 2048, 2049, 2600, 4100, 9000, 20000]) for _ in range(B))
+    check_whole(make_inputs(W("shares", lens, 32, hkv, P), 11, "cuda"), P=P, what=f"C{C}")
+
+
+@pytest.mark.parametrize("P", [1, 4])
+def test_fused_call_equals_separate_calls(P):
+    """qsa_decode and the four separate entry points give the same bits."""
+    x = make_inputs(W("fused", (70000, 3000, 20000, 2049, 0)), 12, "cuda")
+    g = run_chain(x, P)
+    plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, P)
+    plan.run()
+    torch.cuda.synchronize()
+    f = dict(scores=plan.scores, sel=plan.sel, cnt=plan.sel_count, po=plan.partial_out, pl=plan.partial_lse,
+             out=plan.out, lse=plan.out_lse)
+    for key, v in f.items():
+        a = v.cpu().numpy()
+        if key == "scores":
+            a = np.concatenate([a[b, :(L + 3) // 4] for b, L in enumerate(x.lengths)])
+            ref = np.concatenate([g[key][b, :(L + 3) // 4] for b, L in enumerate(x.lengths)])
+        else:
+            ref = g[key]
+        assert np.array_equal(a.view(np.int32), ref.view(np.int32)), f"{key} differs (P={P})"
+
+
 def test_repeat_is_bitwise_and_workspace_is_reusable():
     x = make_inputs(W("rep", (70000, 3000, 20000), P=4), 10, "cuda")
     plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4)
