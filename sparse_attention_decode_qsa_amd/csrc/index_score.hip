@@ -89,7 +89,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
   }
 }
 
-constexpr int kScoreWaves = 4;
+constexpr int kScoreWaves = 16;
 
 hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                               const int32_t* page_table, const int32_t* lens, int B,

@@ -39,15 +39,38 @@ __device__ __forceinline__ int row16_sum(int x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP: a Hillis-Steele scan inside
+// each 16-lane row (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read 0), then
+// row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and row_bcast:31 adds the
+// total of rows 0-1 to rows 2-3.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return x;
 }
+
+// Sum over the wave, returned in every lane (lane 63 of the inclusive scan).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_scan((int)x), 63);
+}
+
+// Unsigned maximum over the wave, returned in every lane: the same DPP pattern with max,
+// whose lane 63 sees every lane.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) { return ~wave_max(~x); }
 
 // Exclusive scan over the threads of a block of NT threads (NT a multiple of 64, <= 1024).
 // `tmp` holds at least NT/64 + 1 ints of LDS. Returns the exclusive prefix and writes

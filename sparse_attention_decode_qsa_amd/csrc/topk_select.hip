@@ -52,20 +52,12 @@ struct SelShared {
   int list_n;
 };
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += (uint32_t)__shfl_xor((int)x, d, 64);
-  return x;
-}
 
 // Block-wide min and max (every thread must call).
 __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, uint32_t* gmn,
                                              uint32_t* gmx) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
-  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   const int wave = threadIdx.x >> 6;
   if (lane_id() == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
   __syncthreads();
@@ -102,33 +94,26 @@ __device__ __forceinline__ void find_bucket(SelShared& sh, int& hsel, uint32_t n
   const uint32_t* h = sh.hbuf[hsel];
   uint32_t* other = sh.hbuf[hsel ^ 1];
   if (t < 64) {
-    // Lane l sums bins [32l, 32l + 32), starting at a rotated offset so the 64 lanes read
-    // from distinct banks.
+    // Lane l sums the 32 bins of group g = 63 - l, starting at a rotated offset so the 64
+    // lanes read from distinct banks; a prefix sum over the lanes is then the number of
+    // keys in group g and every group above it.
+    const int g = 63 - lane;
     uint32_t c = 0;
 #pragma unroll 8
-    for (int i = 0; i < per; ++i) c += h[lane * per + ((i + lane) & (per - 1))];
-    uint32_t suf = c;   // keys in this lane's bins and all bins above
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_down((int)suf, d, 64);
-      if (lane + d < 64) suf += y;
-    }
+    for (int i = 0; i < per; ++i) c += h[g * per + ((i + g) & (per - 1))];
+    const uint32_t suf = (uint32_t)wave_inclusive_scan((int)c);
     const uint64_t hit = __ballot(suf - c < need && suf >= need);
     if (hit == 0) {
       if (lane == 0) { sh.out[0] = -1; sh.out[1] = 0; sh.out[2] = 0; }
     } else {
       const int L = __builtin_ctzll(hit);
-      const uint32_t runL = (uint32_t)__shfl((int)(suf - c), L, 64);   // keys in bins above lane L's
-      // The wave walks lane L's 32 bins: lanes 0..31 hold one bin each, suffix sums from the top.
-      const uint32_t v = lane < per ? h[L * per + lane] : 0u;
-      uint32_t sv = v;
-#pragma unroll
-      for (int d = 1; d < 32; d <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_down((int)sv, d, 64);
-        if (lane + d < per) sv += y;
-      }
-      const bool mine = lane < per && runL + sv - v < need && runL + sv >= need;
-      if (mine) { sh.out[0] = L * per + lane; sh.out[1] = (int)(runL + sv - v); sh.out[2] = (int)v; }
+      const int G = 63 - L;
+      const uint32_t runG = (uint32_t)__builtin_amdgcn_readlane((int)(suf - c), L);   // keys above group G
+      // The wave walks group G's 32 bins from the top: lane l < 32 holds bin 32G + 31 - l.
+      const uint32_t v = lane < per ? h[G * per + (per - 1 - lane)] : 0u;
+      const uint32_t sv = (uint32_t)wave_inclusive_scan((int)v);
+      const bool mine = lane < per && runG + sv - v < need && runG + sv >= need;
+      if (mine) { sh.out[0] = G * per + (per - 1 - lane); sh.out[1] = (int)(runG + sv - v); sh.out[2] = (int)v; }
     }
   } else {
     for (int i = t - 64; i < kSelBins + 64; i += kSelThreads - 64) other[i] = 0;
@@ -270,17 +255,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     if (t == 0) { sh.list_n = 0; sh.out[3] = 0; }
     __syncthreads();
     {
-      // compact the candidate page ids: one LDS reservation per wave and page slot
+      // compact the candidate page ids: one LDS reservation per wave
+      const int cnt = __builtin_popcount(flags);
+      const int incl = wave_inclusive_scan(cnt);
+      int base = 0;
+      if (lane == 63 && incl) base = atomicAdd(&sh.out[3], incl);
+      int slot = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
 #pragma unroll
-      for (int i = 0; i < PV; ++i) {
-        const bool c = (flags >> i) & 1u;
-        const uint64_t m = __ballot(c);
-        int base = 0;
-        if (lane == 0 && m) base = atomicAdd(&sh.out[3], __builtin_popcountll(m));
-        base = __shfl(base, 0, 64);
-        const int slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
-        if (c && slot < kListCap) sh.cpages[slot] = t + kSelThreads * i;
-      }
+      for (int i = 0; i < PV; ++i)
+        if ((flags >> i) & 1u) {
+          if (slot < kListCap) sh.cpages[slot] = t + kSelThreads * i;
+          ++slot;
+        }
     }
     __syncthreads();
     const int ncp = sh.out[3];
