@@ -101,8 +101,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay each call from a HIP graph captured once per input set")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="after timing, run 3 plain device copies of MIB MiB each, so that hardware "
-                         "byte counters can be scaled against a kernel of known traffic")
+                    help="after timing, run 3 copies of MIB MiB each with qsa_calib_copy (the scan's "
+                         "kind of loads and stores), so that hardware byte counters can be scaled "
+                         "against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -186,6 +187,12 @@ def main():
     k1_bytes = index_bytes(lengths)
     k1_gbs = k1_bytes / (ms_k1 * 1e-3) / 1e9
 
+    # HBM bytes per launch of the scan from the committed counter runs, while the scan's
+    # sources are the ones those runs measured (same workload); otherwise unknown.
+    from sparse_attention_decode_qsa_amd import profiling
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"index_score_{args.workload}_traffic.md"))
+    traffic = tr["traffic_bytes"] if tr and tr.get("source_hash") == profiling.scan_source_hash() else None
+
     result = {
         "metric": METRIC,
         "value": round(1000.0 / ms_step, 2),
@@ -218,18 +225,20 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_launch_us": round(ms_k1 * 1000, 3),
             "bytes_per_launch": k1_bytes,
         },
     }
     if args.copy_calibration:
+        from sparse_attention_decode_qsa_amd import calib
         n = args.copy_calibration << 20
         src = torch.ones(n // 4, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            calib.copy(dst, src)
         torch.cuda.synchronize()
+        assert torch.equal(dst, src)
         print(f"# copy calibration: 3 copies of {n} bytes (read {n}, write {n} each)", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on the same workload", file=sys.stderr, flush=True)

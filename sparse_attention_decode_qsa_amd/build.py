@@ -1,4 +1,5 @@
-"""Build libqsa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libqsa.so (HIP kernels + C ABI) and libqsa_calib.so (the counter-calibration copy)
+for gfx950 with hipcc, in-tree.
 
     python -m sparse_attention_decode_qsa_amd.build
 """
@@ -16,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 SOURCES = ["index_score.hip", "topk_select.hip", "sparse_attn.hip", "lse_merge.hip", "qsa_api.hip"]
+CALIB_LIB = os.path.join(PKG, "libqsa_calib.so")
+CALIB_SOURCES = ["calib_copy.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -36,19 +39,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every kernel source and link libqsa.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel source and link libqsa.so and libqsa_calib.so; returns libqsa's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(CALIB_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + CALIB_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

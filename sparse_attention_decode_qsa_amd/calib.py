@@ -1,0 +1,34 @@
+"""ctypes binding of libqsa_calib (include/qsa_calib.h): the counter-calibration copy.
+
+Not part of the decode path: bench.py runs it under a hardware-counter profiler so that the
+indexer scan's counted bytes can be scaled to real bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa_calib.so")
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError(f"{_LIB} is missing: build it with `python -m sparse_attention_decode_qsa_amd.build`")
+        _lib = ctypes.CDLL(_LIB)
+        _lib.qsa_calib_copy.restype = ctypes.c_int
+        _lib.qsa_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    return _lib
+
+
+def copy(dst, src) -> None:
+    """dst[:] = src for two contiguous device tensors of the same size in bytes (a multiple of 16)."""
+    import torch
+    n = src.numel() * src.element_size()
+    if not (dst.is_contiguous() and src.is_contiguous()) or dst.numel() * dst.element_size() != n:
+        raise ValueError("calib.copy needs two contiguous tensors of the same byte size")
+    rc = lib().qsa_calib_copy(dst.data_ptr(), src.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"qsa_calib_copy failed with status {rc}")

@@ -162,3 +162,16 @@ def test_merge_and_decode_checks():
     # the attention workspace
     assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) == 4 * 4096 * 4 + attn_ws(4, 32, 4, 4)
     assert L.qsa_decode_workspace_size(0, 32, 4, 65536, 512, 4) == 0
+
+
+def test_calibration_library():
+    """libqsa_calib exports what include/qsa_calib.h declares; its host checks need no GPU."""
+    from sparse_attention_decode_qsa_amd import calib
+    text = open(os.path.join(ROOT, "include", "qsa_calib.h")).read()
+    names = sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+    assert names == ["qsa_calib_copy"]
+    C = calib.lib()
+    assert C.qsa_calib_copy(None, None, 0, None) == 0
+    assert C.qsa_calib_copy(None, FAKE.value, 16, None) == 1
+    assert C.qsa_calib_copy(FAKE.value, FAKE.value, 15, None) == 2
+    assert C.qsa_calib_copy(FAKE.value + 4, FAKE.value, 16, None) == 2

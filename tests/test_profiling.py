@@ -1,0 +1,35 @@
+"""The counter arithmetic behind the bench's traffic figure, on synthetic rocprofv3 CSV rows."""
+import csv
+
+from sparse_attention_decode_qsa_amd import profiling
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, FIELDS)
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow(dict(Dispatch_Id=i, Kernel_Name=k, Counter_Name=c, Counter_Value=v))
+
+
+def test_traffic_scaling(tmp_path):
+    scan = "void qsa::index_score_kernel<16>(signed char const*, ...)"
+    cal = "qsa_calib::calib_copy_kernel(int __vector(4)*, int __vector(4) const*, unsigned long)"
+    other = "void at::native::vectorized_elementwise_kernel<4, ...>"
+    mib = 1 << 20
+    # the copy moves 1 MiB each way; its counters read half the reads and all the writes
+    _csv(tmp_path / "f.csv", [(cal, "FETCH_SIZE", 512.0), (cal, "FETCH_SIZE", 512.0), (scan, "FETCH_SIZE", 100.0),
+                              (scan, "FETCH_SIZE", 300.0), (other, "FETCH_SIZE", 9e9)])
+    _csv(tmp_path / "w.csv", [(cal, "WRITE_SIZE", 1024.0), (scan, "WRITE_SIZE", 10.0), (other, "WRITE_SIZE", 7.0)])
+    r = profiling.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), mib)
+    assert r["read_factor"] == 0.5 and r["write_factor"] == 1.0
+    assert r["read_bytes"] == 200 * 1024 * 2          # mean 200 KiB counted, 2 bytes per counted byte
+    assert r["write_bytes"] == 10 * 1024
+    assert r["traffic_bytes"] == r["read_bytes"] + r["write_bytes"]
+    out = tmp_path / "t.md"
+    profiling.write_traffic(r, "cmd f", "cmd w", str(out), "title", algorithmic_bytes=409600)
+    back = profiling.read_traffic(str(out))
+    assert back == r and back["source_hash"] == profiling.scan_source_hash()
+    assert profiling.read_traffic(str(tmp_path / "missing.md")) is None
