@@ -8,10 +8,10 @@ in HBM before timing starts. Default workload: w4, the 256K-context batch (B=4, 
 uniform in [65536, 262144] drawn with seed 0, Hq/Hkv=32/4, head_dim 128, shuffled 64-token
 pages, P=4 slices).
 
-Prints one JSON line. `value` is decode calls/s; it also reports the algorithmic GB/s of
-the whole call, a roofline entry for the dominant kernel (the indexer scan, timed on its
-own with HIP events on the stream it runs on) and the CPU oracle's rate on the same
-workload.
+Prints one JSON line. `value` is decode calls/s; it also reports per-call latency
+percentiles, the algorithmic GB/s of the whole call, measured device copy and read ceilings, a
+roofline entry for the dominant kernel (the indexer scan, timed on its own with HIP events on
+the stream it runs on) and the CPU oracle's rate on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload w4] [--sets R] [--no-cpu-baseline]
                     [--graph] [--copy-calibration MIB]
@@ -164,6 +164,18 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
+    # ---- per-call latency (event pair around each call; a separate pass so the events do not
+    # touch the headline timing)
+    n_lat = min(args.steps, 200)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_lat)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    lat = sorted(a.elapsed_time(b) * 1000.0 for a, b in pairs)
+    pct = lambda q: round(lat[min(len(lat) - 1, int(q * len(lat)))], 2)
+
     # ---- the dominant kernel alone (indexer scan), same stream, same inputs
     k_iters = max(args.steps, 100)
     for i in range(10):
@@ -177,6 +189,27 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_k1 = e0.elapsed_time(e1) / k_iters
+
+    # ---- measured device ceilings, same stream: qsa_calib_copy of 1 GiB (read + write) and
+    # qsa_calib_read of 1 GiB (the scan's kind of loads, read only)
+    from sparse_attention_decode_qsa_amd import calib
+    csrc_t = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    cdst_t = torch.empty_like(csrc_t)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def _rate(fn, nbytes, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    copy_gbs = _rate(lambda: calib.copy(cdst_t, csrc_t), 2 << 30)
+    read_gbs = _rate(lambda: calib.read(csrc_t, sink), 1 << 30)
+    del csrc_t, cdst_t
 
     sel = plans[0].sel.cpu().numpy()
     T_exact = kept_tokens_exact(sel, lengths)
@@ -215,8 +248,11 @@ def main():
             "rotated_input_sets": sets,
             "launch": "hip graph replay" if args.graph else "stream launches (qsa_decode per call)",
         },
+        "call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": n_lat},
         "achieved_GBps": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "copy_ceiling_GBps": round(copy_gbs, 1),
+        "read_ceiling_GBps": round(read_gbs, 1),
         "algorithmic_bytes_per_call": algo,
         "roofline": {
             "kernel": "index_score_kernel (indexer scan + pooling + scores)",
@@ -226,6 +262,7 @@ def main():
             "unit": "GB/s",
             "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "frac_of_read_ceiling": round(k1_gbs / read_gbs, 4),
             "avg_launch_us": round(ms_k1 * 1000, 3),
             "bytes_per_launch": k1_bytes,
         },

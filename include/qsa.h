@@ -38,7 +38,8 @@
  *              a failing check returns its code and launches nothing. Launch failures
  *              return QSA_ERR_HIP (see qsa_last_hip_error). Device-side preconditions
  *              (page ids in range, lengths within the page table) are the caller's and
- *              are not checked. No C++ exception crosses this interface.
+ *              are not checked by the compute calls; qsa_check_pages checks them on
+ *              request. No C++ exception crosses this interface.
  *   Workspace  entry points that take a workspace need qsa_*_workspace_size() bytes,
  *              16-byte aligned; when that size is 0 the pointer may be NULL. A workspace
  *              carries intermediates from one kernel of a call to the next; every byte a
@@ -203,6 +204,27 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
                         float* partial_out, float* partial_lse, float* out, float* out_lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qsa_check_pages - check, on the device, the preconditions the compute calls do not check.
+ *
+ * The page table is the article's one cache group (section "What the pull request actually
+ * changes", bullets): token t of request b lives in page page_table[b][t / page_size] of all
+ * three caches, which hold num_pages pages. The compute calls trust the table; a page id out
+ * of range there is an out-of-bounds read. This call reads only page_table and context_lens
+ * (never a cache row, so a bad table cannot make it fault) and writes one verdict per request:
+ *   verdict[b] = -1   valid: 0 <= L_b <= max_pages_per_seq*page_size and every id
+ *                     page_table[b][p], p < ceil(L_b/page_size), lies in [0, num_pages)
+ *   verdict[b] = -2   L_b < 0 or L_b > max_pages_per_seq*page_size
+ *   verdict[b] = p    the first page slot p whose id lies outside [0, num_pages)
+ *
+ *   page_table   [B, max_pages_per_seq] int32;  context_lens [B] int32
+ *   verdict      out [B] int32 (device)
+ * Host checks: B >= 0 (B <= 65535), max_pages_per_seq >= 1, page_size >= 1, num_pages >= 0.
+ */
+qsa_status_t qsa_check_pages(const int32_t* page_table, const int32_t* context_lens, int B,
+                             int max_pages_per_seq, int page_size, int num_pages, int32_t* verdict,
+                             void* stream);
 
 /* Fill a workspace with zero bytes on `stream` (for its first use). */
 qsa_status_t qsa_workspace_clear(void* workspace, size_t workspace_bytes, void* stream);

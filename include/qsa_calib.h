@@ -1,7 +1,7 @@
 /*
  * qsa_calib.h - C ABI of libqsa_calib, a measurement aid that is not part of the decode
  * path: a plain device copy whose loads are issued like the indexer scan's (16-byte
- * nontemporal loads, plain stores). Running it next to the scan under a hardware-counter
+ * nontemporal loads, plain stores), and a read of the same kind. Running it next to the scan under a hardware-counter
  * profiler gives the factor between a read or write counter and the bytes actually moved
  * by that kind of load, so the scan's counted traffic can be converted to bytes.
  *
@@ -24,6 +24,13 @@ extern "C" {
  * alignment outside the above, 5 if the launch failed.
  */
 int qsa_calib_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/*
+ * Read `bytes` bytes of src on `stream` with the same loads and write nothing but one int32
+ * to *sink (device), and only if the data happen to fold to a fixed value: the read ceiling
+ * of the GPU for that kind of load. Same conditions and return codes as qsa_calib_copy.
+ */
+int qsa_calib_read(const void* src, size_t bytes, int* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,8 @@ def lib() -> ctypes.CDLL:
         _lib = ctypes.CDLL(_LIB)
         _lib.qsa_calib_copy.restype = ctypes.c_int
         _lib.qsa_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        _lib.qsa_calib_read.restype = ctypes.c_int
+        _lib.qsa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     return _lib
 
 
@@ -32,3 +34,15 @@ def copy(dst, src) -> None:
     rc = lib().qsa_calib_copy(dst.data_ptr(), src.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
     if rc != 0:
         raise RuntimeError(f"qsa_calib_copy failed with status {rc}")
+
+
+def read(src, sink) -> None:
+    """Read every byte of the contiguous device tensor src (a multiple of 16 bytes); sink is a
+    device int32 tensor that is written only in the unlikely case the data fold to a fixed value."""
+    import torch
+    if not src.is_contiguous():
+        raise ValueError("calib.read needs a contiguous tensor")
+    rc = lib().qsa_calib_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"qsa_calib_read failed with status {rc}")

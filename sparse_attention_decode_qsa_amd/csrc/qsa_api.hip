@@ -15,6 +15,7 @@ hipError_t launch_sparse_attn(const void*, const void*, const void*, const int32
                               const int32_t*, const int32_t*, int, int, int, int, int, int, float, float*,
                               float*, float*, float*, void*, hipStream_t);
 hipError_t launch_lse_merge(const float*, const float*, int, int, int, float*, float*, hipStream_t);
+hipError_t launch_check_pages(const int32_t*, const int32_t*, int, int, int, int, int32_t*, hipStream_t);
 
 namespace {
 
@@ -241,6 +242,17 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                            max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse, out, out_lse,
                            ws_attn, s);
   return hip_status(e);
+}
+
+qsa_status_t qsa_check_pages(const int32_t* page_table, const int32_t* context_lens, int B,
+                             int max_pages_per_seq, int page_size, int num_pages, int32_t* verdict,
+                             void* stream) {
+  if (B < 0 || max_pages_per_seq < 1 || page_size < 1 || num_pages < 0) return QSA_ERR_SHAPE;
+  if (B > 65535) return QSA_ERR_UNSUPPORTED;
+  if (B == 0) return QSA_OK;
+  if (!page_table || !context_lens || !verdict) return QSA_ERR_NULL;
+  return hip_status(launch_check_pages(page_table, context_lens, B, max_pages_per_seq, page_size, num_pages,
+                                       verdict, (hipStream_t)stream));
 }
 
 qsa_status_t qsa_workspace_clear(void* workspace, size_t workspace_bytes, void* stream) {

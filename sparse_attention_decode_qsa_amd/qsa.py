@@ -42,6 +42,7 @@ SIGNATURES = {
     "qsa_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                         _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "qsa_workspace_clear": (_I, [_P, _Z, _P]),
+    "qsa_check_pages": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -244,6 +245,19 @@ class DecodePlan:
         s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
         _check(self._fn(*self._args, s))
         return self.out, self.out_lse
+
+
+def check_pages(page_table, context_lens, num_pages, verdict=None):
+    """Per-request verdict [B] int32: -1 valid, -2 length out of range, p = first bad page slot."""
+    _need(page_table, torch.int32, "page_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, max_pages = page_table.shape
+    if verdict is None:
+        verdict = torch.empty((B,), dtype=torch.int32, device=page_table.device)
+    _need(verdict, torch.int32, "verdict", 1)
+    _check(lib().qsa_check_pages(_ptr(page_table), _ptr(context_lens), B, max_pages, PAGE_SIZE, int(num_pages),
+                                 _ptr(verdict), _stream()))
+    return verdict
 
 
 def decode(q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P=1, k=MAX_K,

@@ -169,9 +169,25 @@ def test_calibration_library():
     from sparse_attention_decode_qsa_amd import calib
     text = open(os.path.join(ROOT, "include", "qsa_calib.h")).read()
     names = sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
-    assert names == ["qsa_calib_copy"]
+    assert names == ["qsa_calib_copy", "qsa_calib_read"]
     C = calib.lib()
     assert C.qsa_calib_copy(None, None, 0, None) == 0
     assert C.qsa_calib_copy(None, FAKE.value, 16, None) == 1
     assert C.qsa_calib_copy(FAKE.value, FAKE.value, 15, None) == 2
     assert C.qsa_calib_copy(FAKE.value + 4, FAKE.value, 16, None) == 2
+    assert C.qsa_calib_read(None, 0, None, None) == 0
+    assert C.qsa_calib_read(FAKE.value, 16, None, None) == 1
+    assert C.qsa_calib_read(FAKE.value, 24, FAKE.value, None) == 2
+
+
+def test_check_pages_host_checks():
+    L = qsa.lib()
+    c = L.qsa_check_pages
+    assert c(None, None, 0, 16, 64, 100, None, None) == OK
+    assert c(FAKE, None, 2, 16, 64, 100, FAKE, None) == NULL
+    assert c(FAKE, FAKE, 2, 16, 64, 100, None, None) == NULL
+    assert c(FAKE, FAKE, -1, 16, 64, 100, FAKE, None) == SHAPE
+    assert c(FAKE, FAKE, 2, 0, 64, 100, FAKE, None) == SHAPE
+    assert c(FAKE, FAKE, 2, 16, 0, 100, FAKE, None) == SHAPE
+    assert c(FAKE, FAKE, 2, 16, 64, -1, FAKE, None) == SHAPE
+    assert c(FAKE, FAKE, 70000, 16, 64, 100, FAKE, None) == UNSUP

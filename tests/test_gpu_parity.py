@@ -181,6 +181,23 @@ def test_fused_call_equals_separate_calls(P):
         assert np.array_equal(a.view(np.int32), ref.view(np.int32)), f"{key} differs (P={P})"
 
 
+def test_check_pages_verdicts():
+    """The precondition check reports bad lengths and the first out-of-range page id."""
+    x = make_inputs(W("chk", (5000, 9000, 130, 70, 0)), 13, "cuda")
+    num_pages = x.idx_cache.shape[0]
+    pt = x.page_table.clone()
+    lens = x.context_lens.clone()
+    assert qsa.check_pages(pt, lens, num_pages).tolist() == [-1] * 5
+    cap = pt.shape[1] * PAGE_SIZE
+    lens[0] = cap + 1                  # length beyond the table
+    pt[1, 100] = num_pages             # slot 100 of request 1 (141 pages in use)
+    pt[1, 120] = -3
+    pt[2, 0] = -7                      # first slot of request 2
+    pt[3, 5] = num_pages + 9           # past request 3's 2 pages: not checked
+    lens[4] = -1
+    assert qsa.check_pages(pt, lens, num_pages).tolist() == [-2, 100, 0, -1, -2]
+
+
 def test_repeat_is_bitwise_and_workspace_is_reusable():
     x = make_inputs(W("rep", (70000, 3000, 20000), P=4), 10, "cuda")
     plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4)
