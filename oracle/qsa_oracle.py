@@ -46,6 +46,17 @@ Readings where the pages leave a step open (each is repeated in the design notes
   R9 partials     a slice's partial is (slice-normalised output, lse = max + ln sum);
                   an empty slice is (0, -inf). The merge skips -inf partials.
   R10 empty       a request of length 0 keeps nothing; its output is 0 and its lse -inf.
+  R11 side cache  the side cache the indexer maintains ([QSA] paragraph: besides the main
+                  cache there are selector and side caches the indexer keeps) holds the
+                  pooled key (R1) of every micro-block, page-aligned like the main cache:
+                  block j of a request sits in page page_table[j // (page/4)], slot
+                  j % (page/4). Scores read from it are R2 on the stored keys.
+  R12 append      a decode step writes its token at position L-1 (L counts the new token):
+                  the K, V and indexer rows go there, and the side-cache entry of block
+                  (L-1)//4 becomes the sum of that block's indexer rows at positions < L.
+                  A request whose write flag is 0 writes nothing (section "What the pull
+                  request actually changes", bullets: synthetic batches must not write the
+                  side caches); neither does a request of length 0.
 """
 from __future__ import annotations
 
@@ -124,6 +135,57 @@ def kept_tokens(kept_blocks: np.ndarray, length: int) -> np.ndarray:
     toks = (np.asarray(kept_blocks, dtype=np.int64)[:, None] * TOKENS_PER_BLOCK
             + np.arange(TOKENS_PER_BLOCK)[None]).reshape(-1)
     return toks[toks < length]
+
+
+# ------------------------------------------------------ side cache and cache writes [QSA]
+
+def side_cache(idx_cache: np.ndarray, page_table: np.ndarray, lengths) -> np.ndarray:
+    """R11: side cache [pages, page_size/4, heads, dim] (int64) holding the pooled key of
+    every block of every request; entries that belong to no block are 0."""
+    pages, page_size = idx_cache.shape[:2]
+    bpp = page_size // TOKENS_PER_BLOCK
+    out = np.zeros((pages, bpp) + idx_cache.shape[2:], dtype=np.int64)
+    for b, L in enumerate(lengths):
+        pooled = pooled_keys(request_rows(idx_cache, page_table[b], int(L)))
+        for j in range(pooled.shape[0]):
+            out[int(page_table[b][j // bpp]), j % bpp] = pooled[j]
+    return out
+
+
+def side_scores(q_idx, side: np.ndarray, page_table_row, length: int) -> np.ndarray:
+    """Block scores of one request read from the side cache (R2 on the stored keys)."""
+    bpp = side.shape[1]
+    nblk = -(-int(length) // TOKENS_PER_BLOCK)
+    pooled = np.zeros((nblk,) + side.shape[2:], dtype=np.int64)
+    for j in range(nblk):
+        pooled[j] = side[int(page_table_row[j // bpp]), j % bpp]
+    return block_scores(np.asarray(q_idx), pooled)
+
+
+def append_token(k_cache, v_cache, idx_cache, side, page_table, lengths, k_new, v_new, idx_new,
+                 write=None):
+    """R12 on copies of the caches; returns the new (k_cache, v_cache, idx_cache, side).
+
+    k_new, v_new [B, Hkv, D] (bf16 bits), idx_new [B, heads, dim] int8; write [B] or None.
+    """
+    k2, v2, i2, s2 = (np.array(a, copy=True) for a in (k_cache, v_cache, idx_cache, side))
+    page_size = idx_cache.shape[1]
+    bpp = page_size // TOKENS_PER_BLOCK
+    for b, L in enumerate(lengths):
+        L = int(L)
+        if L == 0 or (write is not None and not write[b]):
+            continue
+        t = L - 1
+        page, row = int(page_table[b][t // page_size]), t % page_size
+        k2[page, row] = k_new[b]
+        v2[page, row] = v_new[b]
+        i2[page, row] = idx_new[b]
+        j = t // TOKENS_PER_BLOCK
+        total = np.zeros(idx_cache.shape[2:], dtype=np.int64)
+        for u in range(TOKENS_PER_BLOCK * j, L):
+            total += i2[int(page_table[b][u // page_size]), u % page_size].astype(np.int64)
+        s2[int(page_table[b][j // bpp]), j % bpp] = total
+    return k2, v2, i2, s2
 
 
 # ---------------------------------------------------------------------- attention [QSA]

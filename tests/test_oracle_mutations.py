@@ -9,6 +9,7 @@ import pytest
 import oracle
 import oracle.qsa_oracle as Q
 from tests import test_oracle as pins
+from tests import test_oracle_side as side_pins
 
 
 def _patch(monkeypatch, name, fn):
@@ -77,6 +78,37 @@ def _rows_ignore_table(cache, page_table_row, length):
     return Q.__dict__["_orig_rows"](cache, np.arange(len(page_table_row)), length)
 
 
+def _side_slot_shift(idx_cache, page_table, lengths):   # block j stored one slot late
+    s = Q.__dict__["_orig_side"](idx_cache, page_table, lengths)
+    return np.roll(s, 1, axis=1)
+
+
+def _append_whole_block(k_cache, v_cache, idx_cache, side, page_table, lengths, k_new, v_new, idx_new,
+                        write=None):                      # pools all 4 rows of the block, even past L
+    k2, v2, i2, s2 = Q.__dict__["_orig_append"](k_cache, v_cache, idx_cache, side, page_table, lengths,
+                                                k_new, v_new, idx_new, write)
+    for b, L in enumerate(lengths):
+        if L == 0:
+            continue
+        j = (L - 1) // 4
+        total = sum(i2[int(page_table[b][u // 64]), u % 64].astype(np.int64) for u in range(4 * j, 4 * j + 4))
+        s2[int(page_table[b][j // 16]), j % 16] = total
+    return k2, v2, i2, s2
+
+
+def _append_new_row_only(k_cache, v_cache, idx_cache, side, page_table, lengths, k_new, v_new, idx_new,
+                         write=None):                     # forgets the block's earlier tokens
+    k2, v2, i2, s2 = Q.__dict__["_orig_append"](k_cache, v_cache, idx_cache, side, page_table, lengths,
+                                                k_new, v_new, idx_new, write)
+    for b, L in enumerate(lengths):
+        if L:
+            j = (L - 1) // 4
+            s2[int(page_table[b][j // 16]), j % 16] = idx_new[b].astype(np.int64)
+    return k2, v2, i2, s2
+
+
+Q._orig_side = Q.side_cache
+Q._orig_append = Q.append_token
 Q._orig_pooled = Q.pooled_keys
 Q._orig_attend = Q.attend
 Q._orig_rows = Q.request_rows
@@ -92,6 +124,9 @@ MUTATIONS = [
     ("slice_ranges", _slices_token_split, pins.test_slice_ranges_table),
     ("lse_merge", _merge_unnormalised, pins.test_merge_independent_of_slice_count),
     ("request_rows", _rows_ignore_table, lambda: pins.test_scores_brute_force((257, 200))),
+    ("side_cache", _side_slot_shift, lambda: side_pins.test_side_cache_brute_force((5, 70))),
+    ("append_token", _append_whole_block, lambda: side_pins.test_append_reproduces_full_caches((6, 130))),
+    ("append_token", _append_new_row_only, lambda: side_pins.test_append_reproduces_full_caches((7, 64))),
 ]
 
 
