@@ -14,7 +14,9 @@
  *
  * One decode step of one QSA layer is the chain
  *     qsa_index_score -> qsa_topk_select -> qsa_sparse_attn_decode -> qsa_lse_merge
- * (or qsa_decode, which runs the four on one stream).
+ * (or qsa_decode, which runs the four on one stream). The indexer's side cache of pooled keys
+ * (qsa_pool_build, qsa_cache_append, qsa_index_score_pooled, qsa_decode_pooled) gives the
+ * same chain with a scan that reads half the bytes.
  *
  * Conventions for every entry point
  *   Memory     every pointer is device memory of the current HIP device, unless noted.
@@ -204,6 +206,65 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
                         float* partial_out, float* partial_lse, float* out, float* out_lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The indexer's side cache of pooled keys.
+ *
+ * Article, section "What the pull request actually changes": besides the main cache the
+ * indexer keeps selector and side caches (second paragraph), in one cache group with the
+ * main cache, and synthetic batches must not write the side caches (bullets). The side cache
+ * here holds the pooled key of every micro-block - the int sum of the int8 indexer keys of
+ * its up to 4 tokens (|sum| <= 512), as int16 - so the scan reads 512 bytes per block instead
+ * of 1024:
+ *   pooled_cache [num_pages, page_size/4, n_idx_heads, idx_dim] int16, page-aligned with the
+ *   main caches: block j of request b lives in page page_table[b][j / 16], slot j % 16.
+ * Entries of blocks past ceil(L_b/4) are never read.
+ */
+
+/* Build the side-cache entries of every block of every request (the prefill-time path):
+ * entry of block j = sum of the indexer rows of tokens 4j .. min(4j+3, L_b-1). Other entries
+ * are left as they are. Checks as qsa_index_score; pooled_cache 16-byte aligned. */
+qsa_status_t qsa_pool_build(const int8_t* idx_cache, const int32_t* page_table,
+                            const int32_t* context_lens, int B, int n_idx_heads, int idx_dim,
+                            int page_size, int max_pages_per_seq, int16_t* pooled_cache,
+                            void* stream);
+
+/* The decode step's cache writes. context_lens counts the new token, which sits at
+ * t = L_b - 1: its rows k_new[b] ([Hkv, head_dim] bf16), v_new[b] and idx_new[b]
+ * ([n_idx_heads, idx_dim] int8) are written to row t % page_size of page
+ * page_table[b][t / page_size] of k_cache, v_cache and idx_cache, and, when pooled_cache is
+ * not NULL, the side-cache entry of block t / 4 becomes the sum of that block's indexer rows
+ * at positions <= t. write ([B] int32, NULL = every request writes): a request with
+ * write[b] == 0 (a padding or synthetic entry of the batch) writes nothing, main or side;
+ * neither does a request with L_b == 0. Requests of one call must not share a page row. */
+qsa_status_t qsa_cache_append(const void* k_new, const void* v_new, const int8_t* idx_new,
+                              const int32_t* write, void* k_cache, void* v_cache, int8_t* idx_cache,
+                              int16_t* pooled_cache, const int32_t* page_table,
+                              const int32_t* context_lens, int B, int Hkv, int head_dim,
+                              int n_idx_heads, int idx_dim, int page_size, int max_pages_per_seq,
+                              void* stream);
+
+/* qsa_index_score reading the side cache: the same block scores (bit for bit) and optional
+ * per-page maxima, from half the bytes. Arguments as qsa_index_score, with pooled_cache in
+ * place of idx_cache. */
+qsa_status_t qsa_index_score_pooled(const int8_t* q_idx, const int16_t* pooled_cache,
+                                    const int32_t* page_table, const int32_t* context_lens, int B,
+                                    int n_idx_heads, int idx_dim, int page_size,
+                                    int max_pages_per_seq, int max_blocks, int32_t* block_scores,
+                                    int32_t* page_max, void* stream);
+
+/* qsa_decode with the scan reading the side cache instead of the int8 keys; every other
+ * argument, the workspace and every result are as qsa_decode's (the results are the same
+ * bits). */
+qsa_status_t qsa_decode_pooled(const void* q, const int8_t* q_idx, const int16_t* pooled_cache,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* context_lens,
+                               int B, int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim,
+                               int page_size, int max_pages_per_seq, int max_blocks, int k, int P,
+                               float softmax_scale,
+                               int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
+                               float* partial_out, float* partial_lse, float* out, float* out_lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * qsa_check_pages - check, on the device, the preconditions the compute calls do not check.

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 SOURCES = ["index_score.hip", "topk_select.hip", "sparse_attn.hip", "lse_merge.hip", "check_pages.hip",
-           "qsa_api.hip"]
+           "side_cache.hip", "qsa_api.hip"]
 CALIB_LIB = os.path.join(PKG, "libqsa_calib.so")
 CALIB_SOURCES = ["calib_copy.hip"]
 ARCH = "gfx950"

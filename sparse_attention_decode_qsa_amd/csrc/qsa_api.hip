@@ -16,6 +16,11 @@ hipError_t launch_sparse_attn(const void*, const void*, const void*, const int32
                               float*, float*, float*, void*, hipStream_t);
 hipError_t launch_lse_merge(const float*, const float*, int, int, int, float*, float*, hipStream_t);
 hipError_t launch_check_pages(const int32_t*, const int32_t*, int, int, int, int, int32_t*, hipStream_t);
+hipError_t launch_pool_build(const int8_t*, const int32_t*, const int32_t*, int, int, int16_t*, hipStream_t);
+hipError_t launch_cache_append(const void*, const void*, const int8_t*, const int32_t*, void*, void*, int8_t*,
+                               int16_t*, const int32_t*, const int32_t*, int, int, int, hipStream_t);
+hipError_t launch_index_score_pooled(const int8_t*, const int16_t*, const int32_t*, const int32_t*, int, int, int,
+                                     int32_t*, int32_t*, hipStream_t);
 
 namespace {
 
@@ -207,15 +212,20 @@ size_t qsa_decode_workspace_size(int B, int Hq, int Hkv, int max_blocks, int k, 
          qsa_attn_workspace_size(B, Hq, Hkv, k, P);
 }
 
-qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const void* k_cache,
-                        const void* v_cache, const int32_t* page_table, const int32_t* context_lens, int B,
-                        int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim, int page_size,
-                        int max_pages_per_seq, int max_blocks, int k, int P, float softmax_scale,
-                        int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count, float* partial_out,
-                        float* partial_lse, float* out, float* out_lse, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim,
-                                page_size, max_pages_per_seq, max_blocks, block_scores);
+namespace {
+
+// The chain of qsa_decode / qsa_decode_pooled: the scan reads idx_cache (int8 keys) or, when
+// pooled is given, the side cache of pooled keys; the rest is shared.
+qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const int16_t* pooled,
+                          const void* k_cache, const void* v_cache, const int32_t* page_table,
+                          const int32_t* context_lens, int B, int Hq, int Hkv, int head_dim, int n_idx_heads,
+                          int idx_dim, int page_size, int max_pages_per_seq, int max_blocks, int k, int P,
+                          float softmax_scale, int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
+                          float* partial_out, float* partial_lse, float* out, float* out_lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const int8_t* keys = pooled ? reinterpret_cast<const int8_t*>(pooled) : idx_cache;
+  qsa_status_t st = check_index(q_idx, keys, page_table, context_lens, B, n_idx_heads, idx_dim, page_size,
+                                max_pages_per_seq, max_blocks, block_scores);
   if (st == QSA_OK) st = check_topk(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count);
   if (st == QSA_OK)
     st = check_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
@@ -232,8 +242,10 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
   int ncu = 0;
   if ((st = device_cus(&ncu)) != QSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
-                                    max_blocks, block_scores, page_max, ncu, s);
+  hipError_t e = pooled ? launch_index_score_pooled(q_idx, pooled, page_table, context_lens, B, max_pages_per_seq,
+                                                    max_blocks, block_scores, page_max, s)
+                        : launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
+                                             max_blocks, block_scores, page_max, ncu, s);
   if (e == hipSuccess)
     e = launch_topk_select(block_scores, context_lens, page_max, B, max_blocks, max_pages_per_seq, k,
                            sel_blocks, sel_count, s);
@@ -242,6 +254,77 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                            max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse, out, out_lse,
                            ws_attn, s);
   return hip_status(e);
+}
+
+}  // namespace
+
+qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const void* k_cache,
+                        const void* v_cache, const int32_t* page_table, const int32_t* context_lens, int B,
+                        int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim, int page_size,
+                        int max_pages_per_seq, int max_blocks, int k, int P, float softmax_scale,
+                        int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count, float* partial_out,
+                        float* partial_lse, float* out, float* out_lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return decode_chain(q, q_idx, idx_cache, nullptr, k_cache, v_cache, page_table, context_lens, B, Hq, Hkv,
+                      head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
+                      block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, workspace,
+                      workspace_bytes, stream);
+}
+
+qsa_status_t qsa_decode_pooled(const void* q, const int8_t* q_idx, const int16_t* pooled_cache, const void* k_cache,
+                               const void* v_cache, const int32_t* page_table, const int32_t* context_lens, int B,
+                               int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim, int page_size,
+                               int max_pages_per_seq, int max_blocks, int k, int P, float softmax_scale,
+                               int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count, float* partial_out,
+                               float* partial_lse, float* out, float* out_lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (B > 0 && !pooled_cache) return QSA_ERR_NULL;
+  return decode_chain(q, q_idx, nullptr, pooled_cache, k_cache, v_cache, page_table, context_lens, B, Hq, Hkv,
+                      head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
+                      block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, workspace,
+                      workspace_bytes, stream);
+}
+
+qsa_status_t qsa_pool_build(const int8_t* idx_cache, const int32_t* page_table, const int32_t* context_lens, int B,
+                            int n_idx_heads, int idx_dim, int page_size, int max_pages_per_seq,
+                            int16_t* pooled_cache, void* stream) {
+  if (B < 0 || max_pages_per_seq < 1) return QSA_ERR_SHAPE;
+  if (n_idx_heads != kIdxHeads || idx_dim != kIdxDim || page_size != kPageSize) return QSA_ERR_UNSUPPORTED;
+  if (B > 65535) return QSA_ERR_UNSUPPORTED;
+  if (B == 0) return QSA_OK;
+  if (!idx_cache || !page_table || !context_lens || !pooled_cache) return QSA_ERR_NULL;
+  if (misaligned(idx_cache) || misaligned(pooled_cache)) return QSA_ERR_SHAPE;
+  return hip_status(launch_pool_build(idx_cache, page_table, context_lens, B, max_pages_per_seq, pooled_cache,
+                                      (hipStream_t)stream));
+}
+
+qsa_status_t qsa_cache_append(const void* k_new, const void* v_new, const int8_t* idx_new, const int32_t* write,
+                              void* k_cache, void* v_cache, int8_t* idx_cache, int16_t* pooled_cache,
+                              const int32_t* page_table, const int32_t* context_lens, int B, int Hkv, int head_dim,
+                              int n_idx_heads, int idx_dim, int page_size, int max_pages_per_seq, void* stream) {
+  if (B < 0 || Hkv < 1 || max_pages_per_seq < 1) return QSA_ERR_SHAPE;
+  if (head_dim != kHeadDim || n_idx_heads != kIdxHeads || idx_dim != kIdxDim || page_size != kPageSize)
+    return QSA_ERR_UNSUPPORTED;
+  if (B > 65535 || Hkv > 64) return QSA_ERR_UNSUPPORTED;
+  if (B == 0) return QSA_OK;
+  if (!k_new || !v_new || !idx_new || !k_cache || !v_cache || !idx_cache || !page_table || !context_lens)
+    return QSA_ERR_NULL;
+  if (misaligned(k_new) || misaligned(v_new) || misaligned(k_cache) || misaligned(v_cache) ||
+      misaligned(idx_cache) || (pooled_cache && misaligned(pooled_cache)))
+    return QSA_ERR_SHAPE;
+  return hip_status(launch_cache_append(k_new, v_new, idx_new, write, k_cache, v_cache, idx_cache, pooled_cache,
+                                        page_table, context_lens, B, Hkv, max_pages_per_seq, (hipStream_t)stream));
+}
+
+qsa_status_t qsa_index_score_pooled(const int8_t* q_idx, const int16_t* pooled_cache, const int32_t* page_table,
+                                    const int32_t* context_lens, int B, int n_idx_heads, int idx_dim, int page_size,
+                                    int max_pages_per_seq, int max_blocks, int32_t* block_scores, int32_t* page_max,
+                                    void* stream) {
+  qsa_status_t st = check_index(q_idx, reinterpret_cast<const int8_t*>(pooled_cache), page_table, context_lens, B,
+                                n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, block_scores);
+  if (st != QSA_OK || B == 0) return st;
+  return hip_status(launch_index_score_pooled(q_idx, pooled_cache, page_table, context_lens, B, max_pages_per_seq,
+                                              max_blocks, block_scores, page_max, (hipStream_t)stream));
 }
 
 qsa_status_t qsa_check_pages(const int32_t* page_table, const int32_t* context_lens, int B,

@@ -43,6 +43,11 @@ SIGNATURES = {
                         _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "qsa_workspace_clear": (_I, [_P, _Z, _P]),
     "qsa_check_pages": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
+    "qsa_pool_build": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "qsa_cache_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "qsa_index_score_pooled": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "qsa_decode_pooled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                               _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
 }
 
 
@@ -212,7 +217,9 @@ class DecodePlan:
     """
 
     def __init__(self, q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P, k=MAX_K,
-                 softmax_scale=None, max_blocks=None):
+                 softmax_scale=None, max_blocks=None, pooled=None):
+        """pooled: optional side cache of pooled keys (int16); the scan then reads it
+        (qsa_decode_pooled) instead of idx_cache, for the same results."""
         for t, dt, n in ((q, torch.bfloat16, "q"), (q_idx, torch.int8, "q_idx"),
                          (idx_cache, torch.int8, "idx_cache"), (k_cache, torch.bfloat16, "k_cache"),
                          (v_cache, torch.bfloat16, "v_cache"), (page_table, torch.int32, "page_table"),
@@ -233,9 +240,12 @@ class DecodePlan:
         self.out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
         self.workspace = Workspace(decode_workspace_size(B, Hq, Hkv, self.max_blocks, k, P), dev)
         scale = D ** -0.5 if softmax_scale is None else softmax_scale
-        self._fn = lib().qsa_decode
+        if pooled is not None:
+            _need(pooled, torch.int16, "pooled", 4)
+        self._fn = lib().qsa_decode if pooled is None else lib().qsa_decode_pooled
         self._args = [
-            _ptr(q), _ptr(q_idx), _ptr(idx_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+            _ptr(q), _ptr(q_idx), _ptr(idx_cache if pooled is None else pooled), _ptr(k_cache), _ptr(v_cache),
+            _ptr(page_table),
             _ptr(context_lens), B, Hq, Hkv, D, q_idx.shape[1], q_idx.shape[2], k_cache.shape[1],
             max_pages, self.max_blocks, k, P, ctypes.c_float(scale), _ptr(self.scores), _ptr(self.sel),
             _ptr(self.sel_count), _ptr(self.partial_out), _ptr(self.partial_lse), _ptr(self.out),
@@ -245,6 +255,66 @@ class DecodePlan:
         s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
         _check(self._fn(*self._args, s))
         return self.out, self.out_lse
+
+
+def new_pooled_cache(idx_cache):
+    """A zeroed side cache [num_pages, 16, 4, 64] int16 matching the int8 indexer cache."""
+    _need(idx_cache, torch.int8, "idx_cache", 4)
+    n, ps, h, d = idx_cache.shape
+    return torch.zeros((n, ps // 4, h, d), dtype=torch.int16, device=idx_cache.device)
+
+
+def pool_build(idx_cache, page_table, context_lens, pooled=None):
+    """Side-cache entries of every block of every request (entries of no block untouched)."""
+    _need(idx_cache, torch.int8, "idx_cache", 4)
+    _need(page_table, torch.int32, "page_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    pooled = new_pooled_cache(idx_cache) if pooled is None else pooled
+    _need(pooled, torch.int16, "pooled", 4)
+    B, max_pages = page_table.shape
+    _check(lib().qsa_pool_build(_ptr(idx_cache), _ptr(page_table), _ptr(context_lens), B, idx_cache.shape[2],
+                                idx_cache.shape[3], idx_cache.shape[1], max_pages, _ptr(pooled), _stream()))
+    return pooled
+
+
+def cache_append(k_new, v_new, idx_new, k_cache, v_cache, idx_cache, page_table, context_lens, pooled=None,
+                 write=None):
+    """Write each request's new token (at L_b - 1) into the caches and refresh its block's
+    side-cache entry; requests with write[b] == 0 write nothing."""
+    for t, dt, n in ((k_new, torch.bfloat16, "k_new"), (v_new, torch.bfloat16, "v_new"), (idx_new, torch.int8, "idx_new"),
+                     (k_cache, torch.bfloat16, "k_cache"), (v_cache, torch.bfloat16, "v_cache"),
+                     (idx_cache, torch.int8, "idx_cache"), (page_table, torch.int32, "page_table"),
+                     (context_lens, torch.int32, "context_lens")):
+        _need(t, dt, n)
+    if pooled is not None:
+        _need(pooled, torch.int16, "pooled", 4)
+    if write is not None:
+        _need(write, torch.int32, "write", 1)
+    B, max_pages = page_table.shape
+    Hkv = k_cache.shape[2]
+    _check(lib().qsa_cache_append(_ptr(k_new), _ptr(v_new), _ptr(idx_new), _ptr(write), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(idx_cache), _ptr(pooled), _ptr(page_table), _ptr(context_lens), B, Hkv,
+                                  k_cache.shape[3], idx_cache.shape[2], idx_cache.shape[3], k_cache.shape[1],
+                                  max_pages, _stream()))
+
+
+def index_score_pooled(q_idx, pooled, page_table, context_lens, max_blocks=None, out=None, page_max=None):
+    """index_score reading the side cache: the same block scores [B, max_blocks] int32."""
+    _need(q_idx, torch.int8, "q_idx", 3)
+    _need(pooled, torch.int16, "pooled", 4)
+    _need(page_table, torch.int32, "page_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, max_pages = page_table.shape
+    max_blocks = max_pages * PAGE_SIZE // 4 if max_blocks is None else max_blocks
+    if out is None:
+        out = torch.empty((B, max_blocks), dtype=torch.int32, device=q_idx.device)
+    _need(out, torch.int32, "out", 2)
+    if page_max is not None:
+        _need(page_max, torch.int32, "page_max", 2)
+    _check(lib().qsa_index_score_pooled(_ptr(q_idx), _ptr(pooled), _ptr(page_table), _ptr(context_lens), B,
+                                        q_idx.shape[1], q_idx.shape[2], PAGE_SIZE, max_pages, out.shape[1], _ptr(out),
+                                        _ptr(page_max), _stream()))
+    return out
 
 
 def check_pages(page_table, context_lens, num_pages, verdict=None):

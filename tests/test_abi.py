@@ -191,3 +191,31 @@ def test_check_pages_host_checks():
     assert c(FAKE, FAKE, 2, 16, 0, 100, FAKE, None) == SHAPE
     assert c(FAKE, FAKE, 2, 16, 64, -1, FAKE, None) == SHAPE
     assert c(FAKE, FAKE, 70000, 16, 64, 100, FAKE, None) == UNSUP
+
+
+def test_side_cache_host_checks():
+    L = qsa.lib()
+    assert L.qsa_pool_build(None, None, None, 0, 4, 64, 64, 16, None, None) == OK
+    assert L.qsa_pool_build(FAKE, FAKE, FAKE, 2, 4, 64, 64, 16, None, None) == NULL
+    assert L.qsa_pool_build(FAKE, FAKE, FAKE, 2, 4, 32, 64, 16, FAKE, None) == UNSUP
+    assert L.qsa_pool_build(FAKE, FAKE, FAKE, 2, 4, 64, 64, 0, FAKE, None) == SHAPE
+    ap = L.qsa_cache_append
+    args = [FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, 4, 128, 4, 64, 64, 16, None]
+    assert ap(*args[:10], 0, *args[11:]) == OK
+    bad = list(args); bad[0] = None
+    assert ap(*bad) == NULL
+    bad = list(args); bad[12] = 64
+    assert ap(*bad) == UNSUP
+    bad = list(args); bad[11] = 0
+    assert ap(*bad) == SHAPE
+    bad = list(args); bad[7] = FAKE.value + 8
+    assert ap(*bad) == SHAPE                       # misaligned side cache
+    sp = L.qsa_index_score_pooled
+    assert sp(FAKE, None, FAKE, FAKE, 2, 4, 64, 64, 16, 256, FAKE, None, None) == NULL
+    assert sp(FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 64, 16, 255, FAKE, None, None) == SHAPE
+    d = L.qsa_decode_pooled
+    dargs = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 24, None]
+    bad = list(dargs); bad[2] = None
+    assert d(*bad) == NULL
+    bad = list(dargs); bad[8] = 33
+    assert d(*bad) == SHAPE
