@@ -100,6 +100,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each call from a HIP graph captured once per input set")
+    ap.add_argument("--pooled", action="store_true",
+                    help="the side-cache variant: each call writes the step's token into the caches "
+                         "(qsa_cache_append, side cache included) and runs qsa_decode_pooled, whose scan "
+                         "reads the pooled int16 keys instead of the int8 keys")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 copies of MIB MiB each with qsa_calib_copy (the scan's "
                          "kind of loads and stores), so that hardware byte counters can be scaled "
@@ -123,29 +127,45 @@ def main():
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
-    plans, inputs = [], []
+    plans, inputs, appends, pooled = [], [], [], []
     for r in range(sets):
         x = make_inputs(wl, args.seed + 1000 * r, dev)
         inputs.append(x)
+        side = None
+        if args.pooled:
+            # the side cache as prefill leaves it, and the step's new rows = the rows at L-1 (so
+            # every call rewrites the same values and the inputs stay fixed)
+            side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens)
+            pt = x.page_table.cpu()
+            pages = torch.tensor([int(pt[b, (L - 1) // 64]) for b, L in enumerate(lengths)], device=dev)
+            rows = torch.tensor([(L - 1) % 64 for L in lengths], device=dev)
+            appends.append(qsa.AppendPlan(x.k_cache[pages, rows].contiguous(), x.v_cache[pages, rows].contiguous(),
+                                          x.idx_cache[pages, rows].contiguous(), x.k_cache, x.v_cache, x.idx_cache,
+                                          x.page_table, x.context_lens, pooled=side))
+            pooled.append(side)
         plans.append(qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
-                                    x.context_lens, w.slices))
+                                    x.context_lens, w.slices, pooled=side))
     torch.cuda.synchronize()
     print(f"# workload {args.workload}: B={len(lengths)} lengths={lengths[:8]}{'...' if len(lengths) > 8 else ''} "
           f"sets={sets}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     # ---- whole path
-    for i in range(args.warmup):
+    def step(i):
+        if args.pooled:
+            appends[i % sets].run()
         plans[i % sets].run()
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    step = lambda i: plans[i % sets].run()
     if args.graph:
         ref = [(p.sel.clone(), p.out.clone()) for p in plans]
         graphs = []
-        for p in plans:
+        for r in range(sets):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                p.run()
+                step(r)
             graphs.append(g)
         for r, g in enumerate(graphs):     # a replay must reproduce the eager call bit for bit
             g.replay()
@@ -178,14 +198,20 @@ def main():
 
     # ---- the dominant kernel alone (indexer scan), same stream, same inputs
     k_iters = max(args.steps, 100)
-    for i in range(10):
+
+    def scan(i):
         x = inputs[i % sets]
-        qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
+        if args.pooled:
+            qsa.index_score_pooled(x.q_idx, pooled[i % sets], x.page_table, x.context_lens, out=plans[i % sets].scores)
+        else:
+            qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
+
+    for i in range(10):
+        scan(i)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(k_iters):
-        x = inputs[i % sets]
-        qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
+        scan(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_k1 = e0.elapsed_time(e1) / k_iters
@@ -216,15 +242,24 @@ def main():
     algo = algorithmic_bytes(lengths, w.hq, w.hkv)
     # replace the |T| upper bound by the exact kept count of set 0
     algo += (T_exact - sum(min(4 * min(512, (L + 3) // 4), L) for L in lengths)) * w.hkv * 512
-    gbs = algo / (ms_step * 1e-3) / 1e9
     k1_bytes = index_bytes(lengths)
+    if args.pooled:
+        # the scan reads 512 B per block instead of 256 B per token; the append writes the K/V
+        # rows (2*Hkv*256 B), the indexer row (256 B) and one side-cache entry (512 B) per request
+        # and reads up to 3 earlier indexer rows
+        pooled_keys = sum(512 * ((L + 3) // 4) for L in lengths)
+        algo += pooled_keys - IDX_TOKEN_BYTES * sum(lengths)
+        algo += sum(2 * w.hkv * 256 + 256 + 512 + 256 * ((L - 1) % 4) for L in lengths if L)
+        k1_bytes += pooled_keys - IDX_TOKEN_BYTES * sum(lengths)
+    gbs = algo / (ms_step * 1e-3) / 1e9
     k1_gbs = k1_bytes / (ms_k1 * 1e-3) / 1e9
 
     # HBM bytes per launch of the scan from the committed counter runs, while the scan's
     # sources are the ones those runs measured (same workload); otherwise unknown.
     from sparse_attention_decode_qsa_amd import profiling
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"index_score_{args.workload}_traffic.md"))
-    traffic = tr["traffic_bytes"] if tr and tr.get("source_hash") == profiling.scan_source_hash() else None
+    traffic = (tr["traffic_bytes"] if tr and tr.get("source_hash") == profiling.scan_source_hash() and not args.pooled
+               else None)
 
     result = {
         "metric": METRIC,
@@ -246,7 +281,9 @@ def main():
             "seq_len": max(lengths),
             "parallelism": f"1 GPU, P={w.slices} slices merged by LSE",
             "rotated_input_sets": sets,
-            "launch": "hip graph replay" if args.graph else "stream launches (qsa_decode per call)",
+            "launch": ("hip graph replay" if args.graph else "stream launches") +
+                      (" (qsa_cache_append + qsa_decode_pooled per call)" if args.pooled else " (qsa_decode per call)"),
+            "indexer_keys": "pooled int16 side cache" if args.pooled else "int8 per token, pooled in the scan",
         },
         "call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": n_lat},
         "achieved_GBps": round(gbs, 1),
@@ -255,7 +292,8 @@ def main():
         "read_ceiling_GBps": round(read_gbs, 1),
         "algorithmic_bytes_per_call": algo,
         "roofline": {
-            "kernel": "index_score_kernel (indexer scan + pooling + scores)",
+            "kernel": ("index_score_pooled_kernel (side-cache scan + scores)" if args.pooled
+                       else "index_score_kernel (indexer scan + pooling + scores)"),
             "bound": "hbm",
             "achieved": round(k1_gbs, 1),
             "peak": HBM_PEAK_GBS,

@@ -112,8 +112,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 }
 
 // ------------------------------------------------------------------------ scan of the side
-// Grid (page groups, B), WAVES waves per workgroup, one 8 KiB side-cache page = 16 blocks per
-// wave. Lane l = 32*hf + c: load i (i = 0..7) reads bytes [1024*i + 16*l, +16) of the page,
+// Grid (page groups, B), WAVES waves per workgroup, PPW consecutive 8 KiB side-cache pages
+// (16 blocks each) per wave, all their loads issued first. Lane l = 32*hf + c: load i (i = 0..7) reads bytes [1024*i + 16*l, +16) of the page,
 // i.e. int16 keys 8c .. 8c+7 (head c/8, dims 8*(c%8) .. +7) of block 2i + hf; the lane keeps
 // the matching 8 query values as int16 pairs, so v_dot2 over its 4 dwords gives its part of
 // the block's score and a sum over the 32 lanes of each half (DPP inside the 16-lane rows,
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 // counted in the page maximum.
 typedef short short2v __attribute__((ext_vector_type(2)));
 
-template <int WAVES>
+template <int WAVES, int PPW>
 __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
     const int8_t* __restrict__ q_idx, const int16_t* __restrict__ pooled, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ lens, int max_pages, int max_blocks, int32_t* __restrict__ scores,
@@ -129,11 +129,10 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
   const int b = blockIdx.y, lane = lane_id(), wave = threadIdx.x >> 6;
   const int L = lens[b];
   const int npages = (L + kPageSize - 1) / kPageSize;
-  const int p = blockIdx.x * WAVES + wave;
-  if (p >= npages) return;
+  const int p0 = (blockIdx.x * WAVES + wave) * PPW;   // the wave's PPW consecutive pages
+  if (p0 >= npages) return;
   const int hf = lane >> 5, c = lane & 31;
   const int nblk = (L + kTokensPerBlock - 1) / kTokensPerBlock;
-  const int page = page_table[(size_t)b * max_pages + p];
   // query values 8c .. 8c+7 as int16 pairs
   const int2 qw = *reinterpret_cast<const int2*>(q_idx + (size_t)b * kIdxTokenBytes + 8 * c);
   short2v qd[4];
@@ -143,35 +142,46 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
     const int k0 = 2 * (e & 1);
     qd[e] = short2v{(short)sbyte(w, k0), (short)sbyte(w, k0 + 1)};
   }
-  const int8_t* base = reinterpret_cast<const int8_t*>(pooled) + (size_t)page * kPooledPageBytes + 16 * lane;
-  i32x4 v[8];
+  // every load of the wave's pages is issued before any arithmetic
+  i32x4 v[PPW][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + 1024 * i));
-  int tot[8];
+  for (int k = 0; k < PPW; ++k) {
+    if (p0 + k >= npages) break;
+    const int page = page_table[(size_t)b * max_pages + p0 + k];
+    const int8_t* base = reinterpret_cast<const int8_t*>(pooled) + (size_t)page * kPooledPageBytes + 16 * lane;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int a = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int w = v[i][e];   // a plain int first: a bit cast of the subscript itself read element 0
-      a = __builtin_amdgcn_sdot2(__builtin_bit_cast(short2v, w), qd[e], a, false);
-    }
-    a = row16_sum(a);
-    tot[i] = a + __shfl_xor(a, 16, 64);   // the half's other row
+    for (int i = 0; i < 8; ++i) v[k][i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + 1024 * i));
   }
-  // lane c < 8 of each half writes block 2c + hf
-  const int first = p * kSlotsPerPage;
-  int mine = tot[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) mine = c == i ? tot[i] : mine;
-  const int blk = first + 2 * c + hf;
-  if (c < 8 && blk < nblk) scores[(size_t)b * max_blocks + blk] = mine;
-  if (page_max != nullptr) {
-    int m = (int)0x80000000;
+  for (int k = 0; k < PPW; ++k) {
+    const int p = p0 + k;
+    if (p >= npages) break;
+    int tot[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = first + 2 * i + hf < nblk ? max(m, tot[i]) : m;
-    m = max(m, __shfl_xor(m, 32, 64));
-    if (lane == 0) page_max[(size_t)b * max_pages + p] = m;
+    for (int i = 0; i < 8; ++i) {
+      int a = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = v[k][i][e];   // a plain int first: a bit cast of the subscript itself read element 0
+        a = __builtin_amdgcn_sdot2(__builtin_bit_cast(short2v, w), qd[e], a, false);
+      }
+      a = row16_sum(a);
+      tot[i] = a + __shfl_xor(a, 16, 64);   // the half's other row
+    }
+    // lane c < 8 of each half writes block 2c + hf
+    const int first = p * kSlotsPerPage;
+    int mine = tot[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mine = c == i ? tot[i] : mine;
+    const int blk = first + 2 * c + hf;
+    if (c < 8 && blk < nblk) scores[(size_t)b * max_blocks + blk] = mine;
+    if (page_max != nullptr) {
+      int m = (int)0x80000000;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = first + 2 * i + hf < nblk ? max(m, tot[i]) : m;
+      m = max(m, __shfl_xor(m, 32, 64));
+      if (lane == 0) page_max[(size_t)b * max_pages + p] = m;
+    }
   }
 }
 
@@ -198,9 +208,10 @@ hipError_t launch_cache_append(const void* k_new, const void* v_new, const int8_
 hipError_t launch_index_score_pooled(const int8_t* q_idx, const int16_t* pooled, const int32_t* page_table,
                                      const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                                      int32_t* page_max, hipStream_t stream) {
-  const unsigned gx = (unsigned)((max_pages + kSideWaves - 1) / kSideWaves);
-  hipLaunchKernelGGL(index_score_pooled_kernel<kSideWaves>, dim3(gx, B), dim3(kSideWaves * 64), 0, stream, q_idx,
-                     pooled, page_table, lens, max_pages, max_blocks, scores, page_max);
+  constexpr int kPagesPerWave = 1;
+  const unsigned gx = (unsigned)((max_pages + kSideWaves * kPagesPerWave - 1) / (kSideWaves * kPagesPerWave));
+  hipLaunchKernelGGL((index_score_pooled_kernel<kSideWaves, kPagesPerWave>), dim3(gx, B), dim3(kSideWaves * 64), 0,
+                     stream, q_idx, pooled, page_table, lens, max_pages, max_blocks, scores, page_max);
   return hipGetLastError();
 }
 

@@ -25,8 +25,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SCAN_SOURCES = ("csrc/index_score.hip", "csrc/qsa_device.h")
 SCAN_KERNEL = "index_score_kernel"
 CALIB_KERNEL = "calib_copy_kernel"
-CHAIN = ("index_score_kernel", "topk_select_kernel", "sparse_attn_kernel", "slice_merge_kernel",
-         "lse_merge_kernel")
+CHAIN = ("cache_append_kernel", "index_score_kernel", "index_score_pooled_kernel", "topk_select_kernel",
+         "sparse_attn_kernel", "slice_merge_kernel", "lse_merge_kernel")
 
 
 def scan_source_hash() -> str:
@@ -51,20 +51,27 @@ def stats_table(stats_csv: str) -> list[dict]:
                              min_us=float(r["MinNs"]) / 1e3, max_us=float(r["MaxNs"]) / 1e3,
                              share=float(r["Percentage"])))
     order = {k: i for i, k in enumerate(CHAIN)}
-    rows.sort(key=lambda r: min(order[k] for k in CHAIN if k in r["kernel"]))
+    rows.sort(key=lambda r: min(order[k] for k in CHAIN if k + "<" in r["kernel"] or r["kernel"].endswith(k)))
     return rows
 
 
 def chain_span_us(trace_csv: str, skip: int = 20) -> float | None:
-    """Median span (first start to last end) of the consecutive 4-kernel chains in the trace."""
+    """Median span of one whole call in the trace: from the start of the first kernel of a
+    call (the cache append when there is one, else the scan) to the end of the merge."""
     tr = [r for r in csv.DictReader(open(trace_csv)) if "qsa::" in r["Kernel_Name"]]
     tr.sort(key=lambda r: int(r["Start_Timestamp"]))
     spans = []
     for i in range(len(tr) - 3):
-        names = [tr[i + j]["Kernel_Name"] for j in range(4)]
-        if (SCAN_KERNEL in names[0] and "topk_select" in names[1] and "sparse_attn" in names[2]
-                and "merge" in names[3]):
-            spans.append((int(tr[i + 3]["End_Timestamp"]) - int(tr[i]["Start_Timestamp"])) / 1e3)
+        n0 = tr[i]["Kernel_Name"]
+        j = i + 1 if "cache_append" in n0 else i          # the scan
+        if j + 3 >= len(tr) + 0 and j + 3 > len(tr) - 1:
+            break
+        names = [tr[j + d]["Kernel_Name"] for d in range(4)]
+        if ("index_score" in names[0] and "topk_select" in names[1] and "sparse_attn" in names[2]
+                and "merge" in names[3]) and (j == i or "cache_append" in n0):
+            if j == i and i > 0 and "cache_append" in tr[i - 1]["Kernel_Name"]:
+                continue                                    # counted from its append
+            spans.append((int(tr[j + 3]["End_Timestamp"]) - int(tr[i]["Start_Timestamp"])) / 1e3)
     spans = spans[skip:] or spans
     if not spans:
         return None
@@ -82,7 +89,7 @@ def write_stats(dir_: str, prefix: str, command: str, out: str, title: str, note
                      f"{r['max_us']:.2f} | {r['share']:.1f} |")
     lines.append("")
     if span is not None:
-        lines.append(f"Median span of one whole call (start of the scan to the end of the merge): {span:.2f} us.")
+        lines.append(f"Median span of one whole call (start of its first kernel to the end of the merge): {span:.2f} us.")
     if note:
         lines += ["", note]
     open(out, "w").write("\n".join(lines) + "\n")

@@ -330,6 +330,32 @@ def check_pages(page_table, context_lens, num_pages, verdict=None):
     return verdict
 
 
+class AppendPlan:
+    """One qsa_cache_append call per run() with fixed buffers (the decode step's cache writes)."""
+
+    def __init__(self, k_new, v_new, idx_new, k_cache, v_cache, idx_cache, page_table, context_lens, pooled=None,
+                 write=None):
+        for t, dt, n in ((k_new, torch.bfloat16, "k_new"), (v_new, torch.bfloat16, "v_new"),
+                         (idx_new, torch.int8, "idx_new"), (k_cache, torch.bfloat16, "k_cache"),
+                         (v_cache, torch.bfloat16, "v_cache"), (idx_cache, torch.int8, "idx_cache"),
+                         (page_table, torch.int32, "page_table"), (context_lens, torch.int32, "context_lens")):
+            _need(t, dt, n)
+        if pooled is not None:
+            _need(pooled, torch.int16, "pooled", 4)
+        if write is not None:
+            _need(write, torch.int32, "write", 1)
+        self.keep = (k_new, v_new, idx_new, k_cache, v_cache, idx_cache, page_table, context_lens, pooled, write)
+        B, max_pages = page_table.shape
+        self._fn = lib().qsa_cache_append
+        self._args = [_ptr(k_new), _ptr(v_new), _ptr(idx_new), _ptr(write), _ptr(k_cache), _ptr(v_cache),
+                      _ptr(idx_cache), _ptr(pooled), _ptr(page_table), _ptr(context_lens), B, k_cache.shape[2],
+                      k_cache.shape[3], idx_cache.shape[2], idx_cache.shape[3], k_cache.shape[1], max_pages]
+
+    def run(self, stream=None):
+        s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
+        _check(self._fn(*self._args, s))
+
+
 def decode(q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P=1, k=MAX_K,
            softmax_scale=None):
     """The whole path; returns the DecodePlan holding the outputs and intermediates."""
