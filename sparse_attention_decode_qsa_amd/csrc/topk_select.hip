@@ -208,25 +208,34 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   bool masks_done = false;
   uint32_t lo = 0, hi = 0;
   int hsel = 0;   // histogram buffer being filled; the other one is cleared by find_bucket
-  for (int i = t; i < kSelBins + 64; i += kSelThreads) sh.hbuf[0][i] = 0;
-  __syncthreads();
 
   // A. Page maxima (when given and there are at least k pages): one histogram of the page
   // maxima over [min, max]; tau = the lower edge of the bin holding the k-th largest. At
   // least k pages reach tau, each with a block >= tau, so the k-th key is >= tau, and only
-  // the blocks of pages reaching tau can be kept.
+  // the blocks of pages reaching tau can be kept. Their loads are issued before the
+  // histogram is cleared, so the two overlap.
   const int np = (n + kBlocksPerPage - 1) / kBlocksPerPage;
-  bool have_list = false;
-  uint32_t ncand = 0;
-  if (page_max != nullptr && np >= k) {
-    constexpr int PV = 4 * R;                    // page maxima per thread (np <= 4096*R)
+  const bool use_pm = page_max != nullptr && np >= k;
+  constexpr int PV = 4 * R;                      // page maxima per thread (np <= 4096*R)
+  uint32_t pv[PV];
+  if (use_pm) {
     const int32_t* pm = page_max + (size_t)b * max_pages;
-    uint32_t pv[PV];
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
     for (int i = 0; i < PV; ++i) {
       const int pidx = t + kSelThreads * i;
       pv[i] = pidx < np ? score_key(pm[pidx]) : 0u;
+    }
+  }
+  for (int i = t; i < kSelBins + 64; i += kSelThreads) sh.hbuf[0][i] = 0;
+  __syncthreads();
+
+  bool have_list = false;
+  uint32_t ncand = 0;
+  if (use_pm) {
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+      const int pidx = t + kSelThreads * i;
       mn = min(mn, pidx < np ? pv[i] : 0xFFFFFFFFu);
       mx = max(mx, pv[i]);
     }

@@ -181,6 +181,18 @@ def test_fused_call_equals_separate_calls(P):
         assert np.array_equal(a.view(np.int32), ref.view(np.int32)), f"{key} differs (P={P})"
 
 
+def test_w5_shape_whole_batch():
+    """w5's recipe (128 requests, lognormal lengths, indexer values in {-2..2} so that ties
+    decide the 512th place, P = 4) at a median of 2048 tokens, so the oracle checks every
+    request whole; the short requests must equal dense attention (the oracle pins that)."""
+    w = Workload("w5s", 128, ("lognormal", 2048, 1.5, 64, 32768), 32, 4, 4, alphabet="u2")
+    x = make_inputs(w, 0, "cuda")
+    short = sum(L <= 2048 for L in x.lengths)
+    assert 0 < short < 128
+    g, _ = check_whole(x, what="w5s")
+    check_properties(x, g)
+
+
 def test_check_pages_verdicts():
     """The precondition check reports bad lengths and the first out-of-range page id."""
     x = make_inputs(W("chk", (5000, 9000, 130, 70, 0)), 13, "cuda")
