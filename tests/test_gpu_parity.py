@@ -210,6 +210,53 @@ def test_check_pages_verdicts():
     assert qsa.check_pages(pt, lens, num_pages).tolist() == [-2, 100, 0, -1, -2]
 
 
+@pytest.mark.parametrize("pooled", [False, True])
+def test_graph_replay_equals_eager(pooled):
+    """qsa_decode (or the side-cache step: append + qsa_decode_pooled) captured in a HIP graph:
+    every replay, with eager work and synchronisations in between, gives the eager bits."""
+    x = make_inputs(W("graph", (70000, 3000, 20000, 2049), P=4), 14, "cuda")
+    side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens) if pooled else None
+    plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4,
+                          pooled=side)
+    app = None
+    if pooled:
+        pt = x.page_table.cpu()
+        pages = torch.tensor([int(pt[b, (L - 1) // 64]) for b, L in enumerate(x.lengths)], device="cuda")
+        rows = torch.tensor([(L - 1) % 64 for L in x.lengths], device="cuda")
+        app = qsa.AppendPlan(x.k_cache[pages, rows].contiguous(), x.v_cache[pages, rows].contiguous(),
+                             x.idx_cache[pages, rows].contiguous(), x.k_cache, x.v_cache, x.idx_cache,
+                             x.page_table, x.context_lens, pooled=side)
+
+    def step():
+        if app is not None:
+            app.run()
+        plan.run()
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (plan.scores, plan.sel, plan.sel_count, plan.partial_out, plan.out, plan.out_lse)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # warm up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        for t in (plan.sel, plan.partial_out, plan.out, plan.out_lse):
+            t.fill_(-7)                 # eager work between the replays
+        junk.mul_(1.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (plan.scores, plan.sel, plan.sel_count, plan.partial_out, plan.out, plan.out_lse)
+        for name, u, v in zip(("scores", "sel", "count", "partial_out", "out", "lse"), ref, got):
+            assert torch.equal(u.view(torch.int32), v.view(torch.int32)), (rep, name)
+
+
 def test_repeat_is_bitwise_and_workspace_is_reusable():
     x = make_inputs(W("rep", (70000, 3000, 20000), P=4), 10, "cuda")
     plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4)
