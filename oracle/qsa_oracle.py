@@ -57,6 +57,11 @@ Readings where the pages leave a step open (each is repeated in the design notes
                   A request whose write flag is 0 writes nothing (section "What the pull
                   request actually changes", bullets: synthetic batches must not write the
                   side caches); neither does a request of length 0.
+  R13 draft       multi-token decode (speculative drafts of T <= 4 tokens): the T new tokens
+                  are the last T positions of the cache (L counts them all); draft token t
+                  sits at position L-T+t and is decoded exactly as a single token at length
+                  L-T+1+t - its own indexer query and selection, attention over its own kept
+                  tokens, slices of that length - so it sees itself and the tokens before it.
 """
 from __future__ import annotations
 
@@ -292,3 +297,20 @@ def decode(q, q_idx, idx_cache, k_cache, v_cache, page_table, lengths, P: int,
     """decode_request for every request of a batch."""
     return [decode_request(q[b], q_idx[b], idx_cache, k_cache, v_cache, page_table[b],
                            int(lengths[b]), P, scale, k) for b in range(len(lengths))]
+
+
+def draft_length(length: int, T: int, t: int) -> int:
+    """R13: the context seen by draft token t of T (itself included)."""
+    return max(0, int(length) - (T - 1 - t))
+
+
+def decode_multi(q, q_idx, idx_cache, k_cache, v_cache, page_table, lengths, T: int, P: int,
+                 scale: float, k: int = TOP_BLOCKS) -> list:
+    """R13: q [B, T, Hq, D], q_idx [B, T, 4, 64]; one result per (request, draft token), in
+    the order b*T + t, each a single-token decode at length L_b - T + 1 + t."""
+    out = []
+    for b in range(len(lengths)):
+        for t in range(T):
+            out.append(decode_request(q[b][t], q_idx[b][t], idx_cache, k_cache, v_cache, page_table[b],
+                                      draft_length(lengths[b], T, t), P, scale, k))
+    return out

@@ -215,6 +215,26 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> DecodeInputs:
         lengths=lens, planted=planted)
 
 
+def draft_queries(x: DecodeInputs, T: int, seed: int = 0):
+    """Queries of T draft tokens per request: (q [B, T, Hq, 128] bf16, q_idx [B, T, 4, 64] int8),
+    drawn like the single query (bf16 of N(0,1); indexer values from the workload's alphabet)
+    from one generator per request."""
+    w = x.workload
+    device = x.q.device
+    B = x.batch
+    q = torch.empty((B, T, w.hq, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    q_idx = torch.empty((B, T, IDX_HEADS, IDX_DIM), dtype=torch.int8, device=device)
+    alphabet = "u127" if w.alphabet == "zero_q" else w.alphabet
+    for b in range(B):
+        g = _gen(device, _request_seed(seed ^ 0x7D1F, b))
+        q[b] = torch.randn((T, w.hq, HEAD_DIM), generator=g, device=device).to(torch.bfloat16)
+        qi = _int_values((T, IDX_HEADS, IDX_DIM), alphabet, g, device)
+        if w.alphabet == "zero_q":
+            qi.zero_()
+        q_idx[b] = qi
+    return q, q_idx
+
+
 def bf16_bits(t: torch.Tensor):
     """Raw bf16 bit patterns as a host numpy uint16 array (exact, no rounding)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")

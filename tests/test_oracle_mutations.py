@@ -9,6 +9,7 @@ import pytest
 import oracle
 import oracle.qsa_oracle as Q
 from tests import test_oracle as pins
+from tests import test_oracle_multi as multi_pins
 from tests import test_oracle_side as side_pins
 
 
@@ -107,6 +108,14 @@ def _append_new_row_only(k_cache, v_cache, idx_cache, side, page_table, lengths,
     return k2, v2, i2, s2
 
 
+def _draft_one_short(length, T, t):              # draft token t misses itself
+    return max(0, int(length) - (T - t))
+
+
+def _draft_sees_all(length, T, t):               # no causality inside the draft
+    return int(length)
+
+
 Q._orig_side = Q.side_cache
 Q._orig_append = Q.append_token
 Q._orig_pooled = Q.pooled_keys
@@ -127,6 +136,8 @@ MUTATIONS = [
     ("side_cache", _side_slot_shift, lambda: side_pins.test_side_cache_brute_force((5, 70))),
     ("append_token", _append_whole_block, lambda: side_pins.test_append_reproduces_full_caches((6, 130))),
     ("append_token", _append_new_row_only, lambda: side_pins.test_append_reproduces_full_caches((7, 64))),
+    ("draft_length", _draft_one_short, lambda: multi_pins.test_last_draft_token_sees_the_whole_context(2)),
+    ("draft_length", _draft_sees_all, lambda: multi_pins.test_draft_tokens_are_causal(2)),
 ]
 
 
