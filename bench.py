@@ -104,6 +104,9 @@ def main():
                     help="the side-cache variant: each call writes the step's token into the caches "
                          "(qsa_cache_append, side cache included) and runs qsa_decode_pooled, whose scan "
                          "reads the pooled int16 keys instead of the int8 keys")
+    ap.add_argument("--draft", type=int, default=1, metavar="T",
+                    help="multi-token decode: T draft tokens per request (qsa_decode_multi); a call then "
+                         "decodes B*T tokens")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 copies of MIB MiB each with qsa_calib_copy (the scan's "
                          "kind of loads and stores), so that hardware byte counters can be scaled "
@@ -117,7 +120,7 @@ def main():
 
     import torch
     from sparse_attention_decode_qsa_amd import qsa
-    from sparse_attention_decode_qsa_amd.inputs import WORKLOADS, draw_lengths, make_inputs
+    from sparse_attention_decode_qsa_amd.inputs import WORKLOADS, draft_queries, draw_lengths, make_inputs
 
     w = WORKLOADS[args.workload]
     lengths = draw_lengths(w, args.seed)
@@ -143,8 +146,15 @@ def main():
                                           x.idx_cache[pages, rows].contiguous(), x.k_cache, x.v_cache, x.idx_cache,
                                           x.page_table, x.context_lens, pooled=side))
             pooled.append(side)
-        plans.append(qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
-                                    x.context_lens, w.slices, pooled=side))
+        if args.draft > 1:
+            if args.pooled:
+                raise SystemExit("--draft and --pooled do not combine")
+            dq, dqi = draft_queries(x, args.draft, args.seed + 1000 * r)
+            plans.append(qsa.MultiDecodePlan(dq, dqi, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
+                                             x.context_lens, w.slices))
+        else:
+            plans.append(qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
+                                        x.context_lens, w.slices, pooled=side))
     torch.cuda.synchronize()
     print(f"# workload {args.workload}: B={len(lengths)} lengths={lengths[:8]}{'...' if len(lengths) > 8 else ''} "
           f"sets={sets}", file=sys.stderr, flush=True)
@@ -201,7 +211,10 @@ def main():
 
     def scan(i):
         x = inputs[i % sets]
-        if args.pooled:
+        if args.draft > 1:
+            qsa.index_score_multi(plans[i % sets].inputs[1], x.idx_cache, x.page_table, x.context_lens,
+                                  out=plans[i % sets].scores)
+        elif args.pooled:
             qsa.index_score_pooled(x.q_idx, pooled[i % sets], x.page_table, x.context_lens, out=plans[i % sets].scores)
         else:
             qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
@@ -238,11 +251,16 @@ def main():
     del csrc_t, cdst_t
 
     sel = plans[0].sel.cpu().numpy()
-    T_exact = kept_tokens_exact(sel, lengths)
+    D = args.draft
+    # per (request, draft token) the context length it sees
+    vlens = [max(0, L - (D - 1 - t)) for L in lengths for t in range(D)]
+    T_exact = kept_tokens_exact(sel, vlens)
     algo = algorithmic_bytes(lengths, w.hq, w.hkv)
-    # replace the |T| upper bound by the exact kept count of set 0
-    algo += (T_exact - sum(min(4 * min(512, (L + 3) // 4), L) for L in lengths)) * w.hkv * 512
-    k1_bytes = index_bytes(lengths)
+    # the indexer keys are read once for all draft tokens; kept K/V rows, q and the output
+    # count per (request, draft token): replace the single-token |T| bound by the exact count
+    algo += (D - 1) * sum(256 * (w.hq + 1) + 512 * w.hq for _ in lengths)
+    algo += T_exact * w.hkv * 512 - sum(min(4 * min(512, (L + 3) // 4), L) for L in lengths) * w.hkv * 512
+    k1_bytes = index_bytes(lengths) + (D - 1) * sum(256 + 4 * ((L + 3) // 4) for L in lengths)
     if args.pooled:
         # the scan reads 512 B per block instead of 256 B per token; the append writes the K/V
         # rows (2*Hkv*256 B), the indexer row (256 B) and one side-cache entry (512 B) per request
@@ -259,7 +277,7 @@ def main():
     from sparse_attention_decode_qsa_amd import profiling
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"index_score_{args.workload}_traffic.md"))
     traffic = (tr["traffic_bytes"] if tr and tr.get("source_hash") == profiling.scan_source_hash() and not args.pooled
-               else None)
+               and args.draft == 1 else None)
 
     result = {
         "metric": METRIC,
@@ -282,8 +300,11 @@ def main():
             "parallelism": f"1 GPU, P={w.slices} slices merged by LSE",
             "rotated_input_sets": sets,
             "launch": ("hip graph replay" if args.graph else "stream launches") +
-                      (" (qsa_cache_append + qsa_decode_pooled per call)" if args.pooled else " (qsa_decode per call)"),
+                      (" (qsa_cache_append + qsa_decode_pooled per call)" if args.pooled else
+                       f" (qsa_decode_multi, T={D}, per call)" if D > 1 else " (qsa_decode per call)"),
             "indexer_keys": "pooled int16 side cache" if args.pooled else "int8 per token, pooled in the scan",
+            "draft_tokens_per_request": D,
+            "tokens_per_s": round(1000.0 / ms_step * len(lengths) * D, 1),
         },
         "call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": n_lat},
         "achieved_GBps": round(gbs, 1),
@@ -293,7 +314,8 @@ def main():
         "algorithmic_bytes_per_call": algo,
         "roofline": {
             "kernel": ("index_score_pooled_kernel (side-cache scan + scores)" if args.pooled
-                       else "index_score_kernel (indexer scan + pooling + scores)"),
+                       else f"index_score_kernel<T={D}> (indexer scan + pooling + scores of {D} draft tokens)"
+                       if D > 1 else "index_score_kernel (indexer scan + pooling + scores)"),
             "bound": "hbm",
             "achieved": round(k1_gbs, 1),
             "peak": HBM_PEAK_GBS,

@@ -208,6 +208,44 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qsa_decode_multi - multi-token decode: T draft tokens per request (speculative decoding with
+ * a multi-token-prediction head), 1 <= T <= 4, B*T <= 65535.
+ *
+ * The T new tokens are the last T positions of each request's cache (context_lens counts them
+ * all). Draft token t, at position L_b - T + t, is decoded exactly as qsa_decode decodes a
+ * single token at length L_b - T + 1 + t (its own indexer query and top-k selection, attention
+ * over its own kept tokens, slices of that length), so it sees itself and the tokens before
+ * it; a length that would be below 0 is 0. The indexer keys are read once for all T queries.
+ *   q        [B, T, Hq, head_dim] bf16;  q_idx [B, T, n_idx_heads, idx_dim] int8
+ *   results  for virtual request r = b*T + t: block_scores [B*T, max_blocks],
+ *            sel_blocks [B*T, k], sel_count [B*T], partial_out [B*T, P, Hq, head_dim],
+ *            partial_lse [B*T, P, Hq], out [B*T, Hq, head_dim], out_lse [B*T, Hq]
+ *   workspace qsa_decode_multi_workspace_size(B, T, ...) bytes (= qsa_decode's for B*T).
+ * Everything else as qsa_decode; T = 1 gives qsa_decode's results.
+ */
+size_t qsa_decode_multi_workspace_size(int B, int T, int Hq, int Hkv, int max_blocks, int k, int P);
+
+/* The multi-token decode's indexer scan on its own: scores (and, if page_max is not NULL,
+ * per-page maxima [B*T, max_pages_per_seq]) of all T draft tokens of every request, from one
+ * read of the indexer keys. q_idx [B, T, n_idx_heads, idx_dim]; block_scores [B*T, max_blocks];
+ * row b*T + t holds draft token t's scores for blocks < ceil((L_b - T + 1 + t) / 4). Checks as
+ * qsa_index_score, plus 1 <= T <= 4 and B*T <= 65535. */
+qsa_status_t qsa_index_score_multi(const int8_t* q_idx, const int8_t* idx_cache,
+                                   const int32_t* page_table, const int32_t* context_lens, int B,
+                                   int T, int n_idx_heads, int idx_dim, int page_size,
+                                   int max_pages_per_seq, int max_blocks, int32_t* block_scores,
+                                   int32_t* page_max, void* stream);
+qsa_status_t qsa_decode_multi(const void* q, const int8_t* q_idx, const int8_t* idx_cache,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* context_lens,
+                              int B, int T, int Hq, int Hkv, int head_dim, int n_idx_heads,
+                              int idx_dim, int page_size, int max_pages_per_seq, int max_blocks,
+                              int k, int P, float softmax_scale,
+                              int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
+                              float* partial_out, float* partial_lse, float* out, float* out_lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The indexer's side cache of pooled keys.
  *
  * Article, section "What the pull request actually changes": besides the main cache the

@@ -23,11 +23,14 @@
 // Rows past L_b of the last page are read (the page is allocated) and masked to zero.
 // Optionally the maximum block score of each page is written too (page_max[b][p]); the
 // selection uses it to skip pages that cannot hold a kept block.
+// Multi-token decode (T draft tokens per request, T <= 4): the page is read once and scored
+// against the T indexer queries q_idx[b][t]; draft token t sees the first L_b - (T-1-t)
+// tokens, and its scores and page maxima go to row b*T + t.
 #include "qsa_device.h"
 
 namespace qsa {
 
-template <int WAVES>
+template <int WAVES, int T>
 __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ idx_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages,
@@ -42,7 +45,10 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
   const int r4 = lane >> 4, c = lane & 15;
 
   const int page = page_table[(size_t)b * max_pages + p];
-  const i32x4 qv = *reinterpret_cast<const i32x4*>(q_idx + (size_t)b * kIdxTokenBytes + 16 * c);
+  i32x4 qv[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    qv[t] = *reinterpret_cast<const i32x4*>(q_idx + ((size_t)b * T + t) * kIdxTokenBytes + 16 * c);
   const int8_t* base = idx_cache + (size_t)page * kIdxPageBytes + r4 * (16 * kIdxTokenBytes) + 16 * c;
 
   i32x4 x[16];
@@ -57,35 +63,67 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
       if (16 * r4 + i >= valid) x[i] = i32x4{0, 0, 0, 0};
   }
 
-  int acc[4];
+  // acc[t][r]: this lane's part of the score of block 4*r4 + r for draft token t, which sees
+  // the first valid - (T-1-t) tokens of the page. Only a page within T-1 tokens of L holds
+  // positions some draft token must not see; every other page takes the unmasked path.
+  int acc[T][4];
+  const bool masked = T > 1 && valid < kPageSize + T - 1;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int a = 0;
+  for (int t = 0; t < T; ++t) {
+    const int vt = valid - (T - 1 - t);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const i32x4 v = x[4 * r + t];
-      a = __builtin_amdgcn_sdot4(v.x, qv.x, a, false);
-      a = __builtin_amdgcn_sdot4(v.y, qv.y, a, false);
-      a = __builtin_amdgcn_sdot4(v.z, qv.z, a, false);
-      a = __builtin_amdgcn_sdot4(v.w, qv.w, a, false);
+    for (int r = 0; r < 4; ++r) {
+      int a = 0;
+      if (!masked) {   // one accumulation chain over the block's 4 tokens
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const i32x4 v = x[4 * r + u];
+          a = __builtin_amdgcn_sdot4(v.x, qv[t].x, a, false);
+          a = __builtin_amdgcn_sdot4(v.y, qv[t].y, a, false);
+          a = __builtin_amdgcn_sdot4(v.z, qv[t].z, a, false);
+          a = __builtin_amdgcn_sdot4(v.w, qv[t].w, a, false);
+        }
+      } else {         // each token's dot product, kept when draft token t sees it
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const i32x4 v = x[4 * r + u];
+          int d = __builtin_amdgcn_sdot4(v.x, qv[t].x, 0, false);
+          d = __builtin_amdgcn_sdot4(v.y, qv[t].y, d, false);
+          d = __builtin_amdgcn_sdot4(v.z, qv[t].z, d, false);
+          d = __builtin_amdgcn_sdot4(v.w, qv[t].w, d, false);
+          a += 16 * r4 + 4 * r + u < vt ? d : 0;
+        }
+      }
+      acc[t][r] = row16_sum(a);
     }
-    acc[r] = row16_sum(a);
   }
 
-  const int nblk = (L + kTokensPerBlock - 1) / kTokensPerBlock;
-  const int blk = p * kBlocksPerPage + 4 * r4 + c;
-  if (c < 4 && blk < nblk) {
-    const int v = c == 0 ? acc[0] : c == 1 ? acc[1] : c == 2 ? acc[2] : acc[3];
-    scores[(size_t)b * max_blocks + blk] = v;
+  // Lane c of each 16-lane row writes draft token c/4, block 4*r4 + c%4 (T*4 <= 16 lanes).
+  const int tq = c >> 2, rq = c & 3;
+  if (tq < T) {
+    int v = acc[0][0];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v = (tq == t && rq == r) ? acc[t][r] : v;
+    const int Lt = L - (T - 1 - tq);
+    const int nblk = (Lt + kTokensPerBlock - 1) / kTokensPerBlock;
+    const int blk = p * kBlocksPerPage + 4 * r4 + rq;
+    if (Lt > 0 && blk < nblk) scores[((size_t)b * T + tq) * max_blocks + blk] = v;
   }
   if (page_max) {
     const int first = p * kBlocksPerPage + 4 * r4;   // blocks of this DPP row
-    int m = (int)0x80000000;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) m = first + r < nblk ? max(m, acc[r]) : m;
-    m = max(m, __shfl_xor(m, 16, 64));
-    m = max(m, __shfl_xor(m, 32, 64));
-    if (lane == 0) page_max[(size_t)b * max_pages + p] = m;
+    for (int t = 0; t < T; ++t) {
+      const int Lt = L - (T - 1 - t);
+      const int nblk = Lt > 0 ? (Lt + kTokensPerBlock - 1) / kTokensPerBlock : 0;
+      int m = (int)0x80000000;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = first + r < nblk ? max(m, acc[t][r]) : m;
+      m = max(m, __shfl_xor(m, 16, 64));
+      m = max(m, __shfl_xor(m, 32, 64));
+      if (lane == 0) page_max[((size_t)b * T + t) * max_pages + p] = m;
+    }
   }
 }
 
@@ -94,11 +132,19 @@ constexpr int kScoreWaves = 16;
 hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                               const int32_t* page_table, const int32_t* lens, int B,
                               int max_pages, int max_blocks, int32_t* scores, int32_t* page_max,
-                              int num_cu, hipStream_t stream) {
-  (void)num_cu;
+                              int T, hipStream_t stream) {
   const unsigned gx = (unsigned)((max_pages + kScoreWaves - 1) / kScoreWaves);
-  hipLaunchKernelGGL(index_score_kernel<kScoreWaves>, dim3(gx, B), dim3(kScoreWaves * 64), 0, stream,
-                     q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
+#define QSA_SCAN(TT)                                                                                      \
+  hipLaunchKernelGGL((index_score_kernel<kScoreWaves, TT>), dim3(gx, B), dim3(kScoreWaves * 64), 0, stream, \
+                     q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max)
+  switch (T) {
+    case 1: QSA_SCAN(1); break;
+    case 2: QSA_SCAN(2); break;
+    case 3: QSA_SCAN(3); break;
+    case 4: QSA_SCAN(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QSA_SCAN
   return hipGetLastError();
 }
 

@@ -5,15 +5,15 @@
 
 namespace qsa {
 hipError_t launch_index_score(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int,
-                              int, int32_t*, int32_t*, int, hipStream_t);
+                              int, int32_t*, int32_t*, int, hipStream_t);   // ..., T, stream
 size_t topk_workspace_bytes(int B, int max_blocks);
 constexpr int kMaxSelBlocks = 262144;
 hipError_t launch_topk_select(const int32_t*, const int32_t*, const int32_t*, int, int, int, int, int32_t*,
-                              int32_t*, hipStream_t);
+                              int32_t*, int, hipStream_t);                  // ..., T, stream
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int P);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const int32_t*, const int32_t*,
                               const int32_t*, const int32_t*, int, int, int, int, int, int, float, float*,
-                              float*, float*, float*, void*, hipStream_t);
+                              float*, float*, float*, void*, int, hipStream_t);  // ..., workspace, T, stream
 hipError_t launch_lse_merge(const float*, const float*, int, int, int, float*, float*, hipStream_t);
 hipError_t launch_check_pages(const int32_t*, const int32_t*, int, int, int, int, int32_t*, hipStream_t);
 hipError_t launch_pool_build(const int8_t*, const int32_t*, const int32_t*, int, int, int16_t*, hipStream_t);
@@ -32,24 +32,6 @@ qsa_status_t hip_status(hipError_t e) {
   return QSA_ERR_HIP;
 }
 
-constexpr int kMaxDevices = 64;
-int g_num_cu[kMaxDevices];
-
-// Compute units of the current device (queried once per device).
-qsa_status_t device_cus(int* out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e);
-  if (dev < 0 || dev >= kMaxDevices) return QSA_ERR_UNSUPPORTED;
-  int n = __atomic_load_n(&g_num_cu[dev], __ATOMIC_RELAXED);
-  if (n <= 0) {
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_status(e);
-    __atomic_store_n(&g_num_cu[dev], n, __ATOMIC_RELAXED);
-  }
-  *out = n;
-  return QSA_OK;
-}
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -143,10 +125,8 @@ qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache, const
   qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim,
                                 page_size, max_pages_per_seq, max_blocks, block_scores);
   if (st != QSA_OK || B == 0) return st;
-  int ncu = 0;
-  if ((st = device_cus(&ncu)) != QSA_OK) return st;
   return hip_status(launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
-                                       max_blocks, block_scores, page_max, ncu, (hipStream_t)stream));
+                                       max_blocks, block_scores, page_max, 1, (hipStream_t)stream));
 }
 
 size_t qsa_topk_workspace_size(int B, int max_blocks, int k) {
@@ -166,7 +146,7 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
   if (st != QSA_OK || B == 0) return st;
   if (!workspace_ok(workspace, workspace_bytes, topk_workspace_bytes(B, max_blocks))) return QSA_ERR_WORKSPACE;
   return hip_status(launch_topk_select(block_scores, context_lens, page_max, B, max_blocks,
-                                       max_pages_per_seq, k, sel_blocks, sel_count, (hipStream_t)stream));
+                                       max_pages_per_seq, k, sel_blocks, sel_count, 1, (hipStream_t)stream));
 }
 
 size_t qsa_attn_workspace_size(int B, int Hq, int Hkv, int k, int P) {
@@ -188,7 +168,7 @@ qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const vo
   if (misaligned(workspace)) return QSA_ERR_SHAPE;
   return hip_status(launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks,
                                        sel_count, B, Hq, Hkv, max_pages_per_seq, k, P, softmax_scale,
-                                       partial_out, partial_lse, nullptr, nullptr, workspace,
+                                       partial_out, partial_lse, nullptr, nullptr, workspace, 1,
                                        (hipStream_t)stream));
 }
 
@@ -218,41 +198,42 @@ namespace {
 // pooled is given, the side cache of pooled keys; the rest is shared.
 qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const int16_t* pooled,
                           const void* k_cache, const void* v_cache, const int32_t* page_table,
-                          const int32_t* context_lens, int B, int Hq, int Hkv, int head_dim, int n_idx_heads,
+                          const int32_t* context_lens, int B, int T, int Hq, int Hkv, int head_dim, int n_idx_heads,
                           int idx_dim, int page_size, int max_pages_per_seq, int max_blocks, int k, int P,
                           float softmax_scale, int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
                           float* partial_out, float* partial_lse, float* out, float* out_lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
   const int8_t* keys = pooled ? reinterpret_cast<const int8_t*>(pooled) : idx_cache;
+  if (T < 1 || (pooled && T != 1)) return QSA_ERR_SHAPE;
+  if (T > kMaxDraft) return QSA_ERR_UNSUPPORTED;
+  const int BT = B * T;   // virtual requests (request, draft token)
   qsa_status_t st = check_index(q_idx, keys, page_table, context_lens, B, n_idx_heads, idx_dim, page_size,
                                 max_pages_per_seq, max_blocks, block_scores);
-  if (st == QSA_OK) st = check_topk(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count);
+  if (st == QSA_OK) st = check_topk(block_scores, context_lens, BT, max_blocks, k, sel_blocks, sel_count);
   if (st == QSA_OK)
-    st = check_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
+    st = check_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, BT, Hq, Hkv,
                     head_dim, page_size, max_pages_per_seq, k, P, partial_out, partial_lse);
-  if (st == QSA_OK) st = check_merge(partial_out, partial_lse, B, P, Hq, head_dim, out);
+  if (st == QSA_OK) st = check_merge(partial_out, partial_lse, BT, P, Hq, head_dim, out);
   if (st != QSA_OK || B == 0) return st;
-  const size_t pmb = decode_pm_bytes(B, max_blocks);
-  const size_t tb = align256(topk_workspace_bytes(B, max_blocks));
-  if (!workspace_ok(workspace, workspace_bytes, pmb + tb + attn_workspace_bytes(B, Hq, Hkv, P)))
+  const size_t pmb = decode_pm_bytes(BT, max_blocks);
+  const size_t tb = align256(topk_workspace_bytes(BT, max_blocks));
+  if (!workspace_ok(workspace, workspace_bytes, pmb + tb + attn_workspace_bytes(BT, Hq, Hkv, P)))
     return QSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return QSA_ERR_SHAPE;
-  int32_t* page_max = static_cast<int32_t*>(workspace);   // [B, max_pages_per_seq] fits: 16*max_pages <= max_blocks
+  int32_t* page_max = static_cast<int32_t*>(workspace);   // [BT, max_pages_per_seq] fits: 16*max_pages <= max_blocks
   char* ws_attn = static_cast<char*>(workspace) + pmb + tb;
-  int ncu = 0;
-  if ((st = device_cus(&ncu)) != QSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = pooled ? launch_index_score_pooled(q_idx, pooled, page_table, context_lens, B, max_pages_per_seq,
                                                     max_blocks, block_scores, page_max, s)
                         : launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
-                                             max_blocks, block_scores, page_max, ncu, s);
+                                             max_blocks, block_scores, page_max, T, s);
   if (e == hipSuccess)
-    e = launch_topk_select(block_scores, context_lens, page_max, B, max_blocks, max_pages_per_seq, k,
-                           sel_blocks, sel_count, s);
+    e = launch_topk_select(block_scores, context_lens, page_max, BT, max_blocks, max_pages_per_seq, k,
+                           sel_blocks, sel_count, T, s);
   if (e == hipSuccess)
-    e = launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv,
+    e = launch_sparse_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, BT, Hq, Hkv,
                            max_pages_per_seq, k, P, softmax_scale, partial_out, partial_lse, out, out_lse,
-                           ws_attn, s);
+                           ws_attn, T, s);
   return hip_status(e);
 }
 
@@ -265,7 +246,7 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count, float* partial_out,
                         float* partial_lse, float* out, float* out_lse, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return decode_chain(q, q_idx, idx_cache, nullptr, k_cache, v_cache, page_table, context_lens, B, Hq, Hkv,
+  return decode_chain(q, q_idx, idx_cache, nullptr, k_cache, v_cache, page_table, context_lens, B, 1, Hq, Hkv,
                       head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
                       block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, workspace,
                       workspace_bytes, stream);
@@ -279,7 +260,39 @@ qsa_status_t qsa_decode_pooled(const void* q, const int8_t* q_idx, const int16_t
                                float* partial_lse, float* out, float* out_lse, void* workspace,
                                size_t workspace_bytes, void* stream) {
   if (B > 0 && !pooled_cache) return QSA_ERR_NULL;
-  return decode_chain(q, q_idx, nullptr, pooled_cache, k_cache, v_cache, page_table, context_lens, B, Hq, Hkv,
+  return decode_chain(q, q_idx, nullptr, pooled_cache, k_cache, v_cache, page_table, context_lens, B, 1, Hq, Hkv,
+                      head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
+                      block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, workspace,
+                      workspace_bytes, stream);
+}
+
+qsa_status_t qsa_index_score_multi(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
+                                   const int32_t* context_lens, int B, int T, int n_idx_heads, int idx_dim,
+                                   int page_size, int max_pages_per_seq, int max_blocks, int32_t* block_scores,
+                                   int32_t* page_max, void* stream) {
+  if (T < 1) return QSA_ERR_SHAPE;
+  if (T > kMaxDraft || (long long)B * T > 65535) return QSA_ERR_UNSUPPORTED;
+  qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim, page_size,
+                                max_pages_per_seq, max_blocks, block_scores);
+  if (st != QSA_OK || B == 0) return st;
+  return hip_status(launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
+                                       max_blocks, block_scores, page_max, T, (hipStream_t)stream));
+}
+
+size_t qsa_decode_multi_workspace_size(int B, int T, int Hq, int Hkv, int max_blocks, int k, int P) {
+  if (B <= 0 || T <= 0 || T > kMaxDraft) return 0;
+  return qsa_decode_workspace_size(B * T, Hq, Hkv, max_blocks, k, P);
+}
+
+qsa_status_t qsa_decode_multi(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const void* k_cache,
+                              const void* v_cache, const int32_t* page_table, const int32_t* context_lens, int B,
+                              int T, int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim, int page_size,
+                              int max_pages_per_seq, int max_blocks, int k, int P, float softmax_scale,
+                              int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count, float* partial_out,
+                              float* partial_lse, float* out, float* out_lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (B > 0 && T > 0 && (long long)B * T > 65535) return QSA_ERR_UNSUPPORTED;
+  return decode_chain(q, q_idx, idx_cache, nullptr, k_cache, v_cache, page_table, context_lens, B, T, Hq, Hkv,
                       head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
                       block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, workspace,
                       workspace_bytes, stream);

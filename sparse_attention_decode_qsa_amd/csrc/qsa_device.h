@@ -19,6 +19,7 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxK = 512;                    // kept blocks
 constexpr int kMaxGroup = 16;                 // query heads per KV head (MFMA rows)
 constexpr int kMaxSlices = 64;
+constexpr int kMaxDraft = 4;                  // draft tokens per request in multi-token decode
 
 // Host-side: byte counts of workspace regions are rounded up to 256.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -29,6 +30,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Context length of virtual request r = b*T + t when every request carries T draft tokens:
+// draft token t sees L_b - (T-1-t) tokens, itself included (T = 1: request r itself).
+__device__ __forceinline__ int draft_length(const int32_t* lens, int r, int T) {
+  if (T == 1) return lens[r];
+  const int b = r / T;
+  return max(0, lens[b] - (T - 1 - (r - b * T)));
+}
 
 // Sum over the 16 lanes of each DPP row; every lane of the row gets the row total.
 __device__ __forceinline__ int row16_sum(int x) {

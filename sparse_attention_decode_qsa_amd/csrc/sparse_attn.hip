@@ -154,23 +154,24 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
   }
 }
 
-// Grid (C * Hkv, P, B). Writes the partial of share c of (b, p, KV head g) for the query
-// heads of g: sub_out [B, P, C, Hq, 128] (normalised over the share), sub_lse [B, P, C, Hq]
+// Grid (C * Hkv, P, B). With T draft tokens per request, b is the virtual request
+// b_req*T + t (page-table row b_req, length L - (T-1-t)). Writes the partial of share c of
+// (b, p, KV head g) for the query heads of g: sub_out [B, P, C, Hq, 128] (normalised over the share), sub_lse [B, P, C, Hq]
 // (natural log; -inf for an empty share, whose output is 0).
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int Hq, int Hkv,
-    int max_pages, int k, int P, int C, float scale_log2, float* __restrict__ sub_out,
+    int max_pages, int k, int P, int C, int T, float scale_log2, float* __restrict__ sub_out,
     float* __restrict__ sub_lse) {
   const int g = blockIdx.x / C, c = blockIdx.x - g * C, p = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
   const int i16 = lane & 15, q4 = lane >> 4;
   const int group = Hq / Hkv;
-  const int L = lens[b];
+  const int L = draft_length(lens, b, T);
   const int K = sel_count[b];
   const int32_t* sb = sel + (size_t)b * k;
-  const int32_t* ptab = page_table + (size_t)b * max_pages;
+  const int32_t* ptab = page_table + (size_t)(b / T) * max_pages;
   const size_t share = ((size_t)b * P + p) * C + c;
 
   __shared__ int s_cnt[kAttnWaves][2];
@@ -309,7 +310,7 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                               const int32_t* lens, const int32_t* sel, const int32_t* sel_count, int B,
                               int Hq, int Hkv, int max_pages, int k, int P, float scale,
                               float* part_out, float* part_lse, float* out, float* out_lse,
-                              void* workspace, hipStream_t stream) {
+                              void* workspace, int T, hipStream_t stream) {
   const int C = attn_split(B, Hkv, P);
   float* sub_out = static_cast<float*>(workspace);
   float* sub_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn_sub_out_bytes(B, Hq, Hkv, P));
@@ -317,7 +318,7 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
   hipLaunchKernelGGL(sparse_attn_kernel, dim3(C * Hkv, P, B), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), page_table, lens, sel, sel_count, Hq, Hkv,
-                     max_pages, k, P, C, scale_log2, sub_out, sub_lse);
+                     max_pages, k, P, C, T, scale_log2, sub_out, sub_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_slice_merge(sub_out, sub_lse, B, P, C, Hq, part_out, part_lse, out, out_lse, stream);

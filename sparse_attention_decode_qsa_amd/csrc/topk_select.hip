@@ -184,12 +184,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
                                                                   const int32_t* __restrict__ page_max,
                                                                   int max_blocks, int max_pages, int k,
                                                                   int32_t* __restrict__ sel,
-                                                                  int32_t* __restrict__ sel_count) {
+                                                                  int32_t* __restrict__ sel_count, int T) {
   extern __shared__ uint64_t s_words[];  // [2][1024*R]: kept and tie masks per chunk
   __shared__ SelShared sh;
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = lane_id();
-  const int n = (lens[b] + kTokensPerBlock - 1) / kTokensPerBlock;
+  const int n = (draft_length(lens, b, T) + kTokensPerBlock - 1) / kTokensPerBlock;
   int32_t* out = sel + (size_t)b * k;
 
   if (n <= k) {  // every block is kept
@@ -522,19 +522,19 @@ size_t topk_workspace_bytes(int B, int max_blocks) {
 
 hipError_t launch_topk_select(const int32_t* scores, const int32_t* lens, const int32_t* page_max, int B,
                               int max_blocks, int max_pages, int k, int32_t* sel, int32_t* sel_count,
-                              hipStream_t stream) {
+                              int T, hipStream_t stream) {
   const int chunks = (max_blocks + kChunk - 1) / kChunk;
   const int R = chunks <= kSelThreads ? 1 : chunks <= 2 * kSelThreads ? 2 : 4;
   const size_t lds = 2 * (size_t)kSelThreads * R * sizeof(uint64_t);
   if (R == 1)
     hipLaunchKernelGGL(topk_select_kernel<1>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
-                       page_max, max_blocks, max_pages, k, sel, sel_count);
+                       page_max, max_blocks, max_pages, k, sel, sel_count, T);
   else if (R == 2)
     hipLaunchKernelGGL(topk_select_kernel<2>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
-                       page_max, max_blocks, max_pages, k, sel, sel_count);
+                       page_max, max_blocks, max_pages, k, sel, sel_count, T);
   else
     hipLaunchKernelGGL(topk_select_kernel<4>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
-                       page_max, max_blocks, max_pages, k, sel, sel_count);
+                       page_max, max_blocks, max_pages, k, sel, sel_count, T);
   return hipGetLastError();
 }
 

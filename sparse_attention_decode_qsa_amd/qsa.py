@@ -43,6 +43,10 @@ SIGNATURES = {
                         _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "qsa_workspace_clear": (_I, [_P, _Z, _P]),
     "qsa_check_pages": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
+    "qsa_decode_multi_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "qsa_index_score_multi": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "qsa_decode_multi": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                              _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "qsa_pool_build": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "qsa_cache_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "qsa_index_score_pooled": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
@@ -328,6 +332,72 @@ def check_pages(page_table, context_lens, num_pages, verdict=None):
     _check(lib().qsa_check_pages(_ptr(page_table), _ptr(context_lens), B, max_pages, PAGE_SIZE, int(num_pages),
                                  _ptr(verdict), _stream()))
     return verdict
+
+
+def index_score_multi(q_idx, idx_cache, page_table, context_lens, max_blocks=None, out=None, page_max=None):
+    """Scores of T draft tokens per request from one read of the keys: q_idx [B, T, 4, 64];
+    returns [B*T, max_blocks] int32 (row b*T + t)."""
+    _need(q_idx, torch.int8, "q_idx", 4)
+    _need(idx_cache, torch.int8, "idx_cache", 4)
+    _need(page_table, torch.int32, "page_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, T = q_idx.shape[:2]
+    max_pages = page_table.shape[1]
+    max_blocks = max_pages * PAGE_SIZE // 4 if max_blocks is None else max_blocks
+    if out is None:
+        out = torch.empty((B * T, max_blocks), dtype=torch.int32, device=q_idx.device)
+    _need(out, torch.int32, "out", 2)
+    if page_max is not None:
+        _need(page_max, torch.int32, "page_max", 2)
+    _check(lib().qsa_index_score_multi(_ptr(q_idx), _ptr(idx_cache), _ptr(page_table), _ptr(context_lens), B, T,
+                                       q_idx.shape[2], q_idx.shape[3], idx_cache.shape[1], max_pages, out.shape[1],
+                                       _ptr(out), _ptr(page_max), _stream()))
+    return out
+
+
+class MultiDecodePlan:
+    """Multi-token decode: T draft tokens per request, one qsa_decode_multi call per run().
+
+    q [B, T, Hq, 128] bf16, q_idx [B, T, 4, 64] int8; the results hold one row per
+    (request, draft token) in the order b*T + t (e.g. out [B*T, Hq, 128])."""
+
+    def __init__(self, q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P, k=MAX_K,
+                 softmax_scale=None, max_blocks=None):
+        _need(q, torch.bfloat16, "q", 4)
+        _need(q_idx, torch.int8, "q_idx", 4)
+        for t, dt, n in ((idx_cache, torch.int8, "idx_cache"), (k_cache, torch.bfloat16, "k_cache"),
+                         (v_cache, torch.bfloat16, "v_cache"), (page_table, torch.int32, "page_table"),
+                         (context_lens, torch.int32, "context_lens")):
+            _need(t, dt, n)
+        self.inputs = (q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens)
+        B, T, Hq, D = q.shape
+        Hkv = k_cache.shape[2]
+        max_pages = page_table.shape[1]
+        self.T = T
+        self.max_blocks = max_pages * PAGE_SIZE // 4 if max_blocks is None else max_blocks
+        dev = q.device
+        BT = B * T
+        self.scores = torch.empty((BT, self.max_blocks), dtype=torch.int32, device=dev)
+        self.sel = torch.empty((BT, k), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((BT,), dtype=torch.int32, device=dev)
+        self.partial_out = torch.empty((BT, P, Hq, D), dtype=torch.float32, device=dev)
+        self.partial_lse = torch.empty((BT, P, Hq), dtype=torch.float32, device=dev)
+        self.out = torch.empty((BT, Hq, D), dtype=torch.float32, device=dev)
+        self.out_lse = torch.empty((BT, Hq), dtype=torch.float32, device=dev)
+        self.workspace = Workspace(lib().qsa_decode_multi_workspace_size(B, T, Hq, Hkv, self.max_blocks, k, P), dev)
+        scale = D ** -0.5 if softmax_scale is None else softmax_scale
+        self._fn = lib().qsa_decode_multi
+        self._args = [
+            _ptr(q), _ptr(q_idx), _ptr(idx_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+            _ptr(context_lens), B, T, Hq, Hkv, D, q_idx.shape[2], q_idx.shape[3], k_cache.shape[1],
+            max_pages, self.max_blocks, k, P, ctypes.c_float(scale), _ptr(self.scores), _ptr(self.sel),
+            _ptr(self.sel_count), _ptr(self.partial_out), _ptr(self.partial_lse), _ptr(self.out),
+            _ptr(self.out_lse), self.workspace.ptr(), self.workspace.nbytes]
+
+    def run(self, stream=None):
+        s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
+        _check(self._fn(*self._args, s))
+        return self.out, self.out_lse
 
 
 class AppendPlan:

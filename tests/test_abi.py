@@ -219,3 +219,32 @@ def test_side_cache_host_checks():
     assert d(*bad) == NULL
     bad = list(dargs); bad[8] = 33
     assert d(*bad) == SHAPE
+
+
+def test_decode_multi_host_checks():
+    L = qsa.lib()
+    assert L.qsa_decode_multi_workspace_size(4, 3, 32, 4, 65536, 512, 4) == L.qsa_decode_workspace_size(
+        12, 32, 4, 65536, 512, 4)
+    assert L.qsa_decode_multi_workspace_size(4, 0, 32, 4, 65536, 512, 4) == 0
+    d = L.qsa_decode_multi
+    args = [FAKE] * 7 + [2, 2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 26, None]
+    bad = list(args); bad[8] = 0
+    assert d(*bad) == SHAPE                        # T = 0
+    bad = list(args); bad[8] = 5
+    assert d(*bad) == UNSUP                        # more than 4 draft tokens
+    bad = list(args); bad[7], bad[8] = 20000, 4
+    assert d(*bad) == UNSUP                        # B*T > 65535
+    bad = list(args); bad[1] = None
+    assert d(*bad) == NULL
+    bad = list(args); bad[28] = 100
+    assert d(*bad) == WS
+
+
+def test_index_score_multi_host_checks():
+    L = qsa.lib()
+    f = L.qsa_index_score_multi
+    assert f(None, None, None, None, 0, 2, 4, 64, 64, 16, 256, None, None, None) == OK
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 0, 4, 64, 64, 16, 256, FAKE, None, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 5, 4, 64, 64, 16, 256, FAKE, None, None) == UNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 4, 64, 64, 16, 255, FAKE, None, None) == SHAPE
+    assert f(FAKE, None, FAKE, FAKE, 2, 2, 4, 64, 64, 16, 256, FAKE, None, None) == NULL

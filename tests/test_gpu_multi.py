@@ -1,0 +1,110 @@
+"""Multi-token (draft) decode on the GPU (qsa_decode_multi through the C ABI) against the
+CPU oracle's decode_multi: for every (request, draft token) the block scores and kept ids
+match bit for bit and the outputs are within tolerance; T = 1 gives qsa_decode's bits, and
+the last draft token qsa_decode's selection (its outputs to float rounding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_qsa_amd import qsa
+from sparse_attention_decode_qsa_amd.inputs import WORKLOADS, Workload, bf16_bits, draft_queries, make_inputs
+from tests.helpers import oracle_arrays
+from tests.test_gpu_parity import check_request, say
+
+pytestmark = pytest.mark.gpu
+
+LENS = (3, 4, 5, 64, 65, 66, 67, 130, 2049, 9000, 40001)
+
+
+def _run(x, q, qi, P):
+    plan = qsa.MultiDecodePlan(q, qi, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, P)
+    plan.run()
+    torch.cuda.synchronize()
+    return plan, dict(scores=plan.scores.cpu().numpy(), sel=plan.sel.cpu().numpy(), cnt=plan.sel_count.cpu().numpy(),
+                      po=plan.partial_out.cpu().numpy(), pl=plan.partial_lse.cpu().numpy(),
+                      out=plan.out.cpu().numpy(), lse=plan.out_lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_multi_matches_oracle(T):
+    x = make_inputs(Workload("draft", len(LENS), ("list",) + LENS, 32, 4, 3), 51, "cuda")
+    q, qi = draft_queries(x, T, 51)
+    say(f"[multi T={T}] lens={LENS}")
+    _, g = _run(x, q, qi, 3)
+    a = oracle_arrays(x)
+    refs = oracle.decode_multi(bf16_bits(q), qi.cpu().numpy(), a["idx_cache"], a["k_cache"], a["v_cache"],
+                               a["page_table"], a["lengths"], T, 3, x.scale)
+    for b, L in enumerate(LENS):
+        for t in range(T):
+            r = b * T + t
+            check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"T{T} b{b} t{t}")
+
+
+def test_multi_scan_alone_matches_chain():
+    x = make_inputs(Workload("draft_s", len(LENS), ("list",) + LENS, 32, 4, 3), 54, "cuda")
+    q, qi = draft_queries(x, 3, 54)
+    plan, _ = _run(x, q, qi, 3)
+    s = qsa.index_score_multi(qi, x.idx_cache, x.page_table, x.context_lens)
+    torch.cuda.synchronize()
+    for b, L in enumerate(LENS):
+        for t in range(3):
+            n = (oracle.draft_length(L, 3, t) + 3) // 4
+            assert torch.equal(s[b * 3 + t, :n], plan.scores[b * 3 + t, :n]), (b, t)
+
+
+def test_one_draft_token_equals_decode():
+    x = make_inputs(Workload("draft1", len(LENS), ("list",) + LENS, 32, 4, 3), 52, "cuda")
+    q, qi = draft_queries(x, 1, 52)
+    plan, _ = _run(x, q, qi, 3)
+    single = qsa.DecodePlan(q[:, 0].contiguous(), qi[:, 0].contiguous(), x.idx_cache, x.k_cache, x.v_cache,
+                            x.page_table, x.context_lens, 3)
+    single.run()
+    torch.cuda.synchronize()
+    for name in ("sel", "sel_count", "partial_out", "partial_lse", "out", "out_lse"):
+        assert torch.equal(getattr(plan, name).view(torch.int32), getattr(single, name).view(torch.int32)), name
+
+
+def test_last_draft_token_equals_full_length_decode():
+    T = 4
+    x = make_inputs(Workload("draft4", len(LENS), ("list",) + LENS, 32, 4, 3), 53, "cuda")
+    q, qi = draft_queries(x, T, 53)
+    plan, _ = _run(x, q, qi, 3)
+    single = qsa.DecodePlan(q[:, T - 1].contiguous(), qi[:, T - 1].contiguous(), x.idx_cache, x.k_cache,
+                            x.v_cache, x.page_table, x.context_lens, 3)
+    single.run()
+    torch.cuda.synchronize()
+    last = torch.arange(len(LENS), device="cuda") * T + T - 1
+    for name in ("sel", "sel_count"):
+        assert torch.equal(getattr(plan, name)[last], getattr(single, name)), name
+    # the attention's share count depends on the number of (request, token) pairs, so the
+    # float sums are grouped differently: equal to float rounding, not bit for bit
+    for name in ("out", "out_lse"):
+        u, v = getattr(plan, name)[last], getattr(single, name)
+        fin = torch.isfinite(v)
+        assert torch.equal(torch.isfinite(u), fin), name
+        assert torch.allclose(u[fin], v[fin], atol=2e-6, rtol=1e-5), name
+    for b, L in enumerate(LENS):
+        n = (L + 3) // 4
+        assert torch.equal(plan.scores[b * T + T - 1, :n], single.scores[b, :n]), b
+
+
+def test_full_w4_four_draft_tokens():
+    T = 4
+    x = make_inputs(WORKLOADS["w4"], 0, "cuda")
+    q, qi = draft_queries(x, T, 0)
+    plan, g = _run(x, q, qi, 4)
+    for b, L in enumerate(x.lengths):
+        for t in range(T):
+            r = b * T + t
+            K = min(512, (oracle.draft_length(L, T, t) + 3) // 4)
+            assert g["cnt"][r] == K and np.all(np.diff(g["sel"][r, :K]) > 0)
+            assert np.all(np.isfinite(g["out"][r]))
+    # two sampled (request, draft token) pairs against the oracle, each as a single decode
+    a = oracle_arrays(x)
+    for b, t in ((3, 0), (0, 2)):
+        Lt = oracle.draft_length(x.lengths[b], T, t)
+        r = b * T + t
+        ref = oracle.decode_request(bf16_bits(q[b, t]), qi[b, t].cpu().numpy(), a["idx_cache"], a["k_cache"],
+                                    a["v_cache"], a["page_table"][b], Lt, 4, x.scale)
+        check_request(g, r, ref, Lt, what=f"w4 T4 b{b} t{t}")
