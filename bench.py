@@ -101,9 +101,12 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay each call from a HIP graph captured once per input set")
     ap.add_argument("--pooled", action="store_true",
-                    help="the side-cache variant: each call writes the step's token into the caches "
-                         "(qsa_cache_append, side cache included) and runs qsa_decode_pooled, whose scan "
-                         "reads the pooled int16 keys instead of the int8 keys")
+                    help="the side-cache variant: each call writes the step's token into the caches (side "
+                         "cache included) and decodes with a scan that reads the pooled int16 keys instead "
+                         "of the int8 keys (qsa_decode_step_pooled)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="with --pooled: make the step's cache writes with qsa_cache_append before "
+                         "qsa_decode_pooled instead of inside the scan (qsa_decode_step_pooled)")
     ap.add_argument("--draft", type=int, default=1, metavar="T",
                     help="multi-token decode: T draft tokens per request (qsa_decode_multi); a call then "
                          "decodes B*T tokens")
@@ -142,11 +145,16 @@ def main():
             pt = x.page_table.cpu()
             pages = torch.tensor([int(pt[b, (L - 1) // 64]) for b, L in enumerate(lengths)], device=dev)
             rows = torch.tensor([(L - 1) % 64 for L in lengths], device=dev)
-            appends.append(qsa.AppendPlan(x.k_cache[pages, rows].contiguous(), x.v_cache[pages, rows].contiguous(),
-                                          x.idx_cache[pages, rows].contiguous(), x.k_cache, x.v_cache, x.idx_cache,
-                                          x.page_table, x.context_lens, pooled=side))
+            k_new, v_new = x.k_cache[pages, rows].contiguous(), x.v_cache[pages, rows].contiguous()
+            i_new = x.idx_cache[pages, rows].contiguous()
+            if args.separate_append:
+                appends.append(qsa.AppendPlan(k_new, v_new, i_new, x.k_cache, x.v_cache, x.idx_cache,
+                                              x.page_table, x.context_lens, pooled=side))
             pooled.append(side)
-        if args.draft > 1:
+        if args.pooled and not args.separate_append:
+            plans.append(qsa.StepPlan(k_new, v_new, i_new, x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache,
+                                      x.page_table, x.context_lens, side, w.slices))
+        elif args.draft > 1:
             if args.pooled:
                 raise SystemExit("--draft and --pooled do not combine")
             dq, dqi = draft_queries(x, args.draft, args.seed + 1000 * r)
@@ -162,7 +170,7 @@ def main():
     stream = torch.cuda.current_stream()
     # ---- whole path
     def step(i):
-        if args.pooled:
+        if appends:
             appends[i % sets].run()
         plans[i % sets].run()
 
@@ -300,7 +308,8 @@ def main():
             "parallelism": f"1 GPU, P={w.slices} slices merged by LSE",
             "rotated_input_sets": sets,
             "launch": ("hip graph replay" if args.graph else "stream launches") +
-                      (" (qsa_cache_append + qsa_decode_pooled per call)" if args.pooled else
+                      ((" (qsa_cache_append + qsa_decode_pooled per call)" if args.separate_append else
+                        " (qsa_decode_step_pooled: cache writes in the scan, per call)") if args.pooled else
                        f" (qsa_decode_multi, T={D}, per call)" if D > 1 else " (qsa_decode per call)"),
             "indexer_keys": "pooled int16 side cache" if args.pooled else "int8 per token, pooled in the scan",
             "draft_tokens_per_request": D,

@@ -304,6 +304,23 @@ qsa_status_t qsa_decode_pooled(const void* q, const int8_t* q_idx, const int16_t
                                float* partial_out, float* partial_lse, float* out, float* out_lse,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step on the side cache: qsa_cache_append (with pooled_cache) followed by
+ * qsa_decode_pooled, in one call and with the same results. The cache writes are made by the
+ * scan (the wave that reads the page holding the new token), which saves a launch. Arguments
+ * as in those two calls; k_cache, v_cache, idx_cache and pooled_cache are written. */
+qsa_status_t qsa_decode_step_pooled(const void* k_new, const void* v_new, const int8_t* idx_new,
+                                    const int32_t* write, void* k_cache, void* v_cache,
+                                    int8_t* idx_cache, int16_t* pooled_cache,
+                                    const void* q, const int8_t* q_idx,
+                                    const int32_t* page_table, const int32_t* context_lens,
+                                    int B, int Hq, int Hkv, int head_dim, int n_idx_heads,
+                                    int idx_dim, int page_size, int max_pages_per_seq,
+                                    int max_blocks, int k, int P, float softmax_scale,
+                                    int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
+                                    float* partial_out, float* partial_lse, float* out,
+                                    float* out_lse, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /*
  * qsa_check_pages - check, on the device, the preconditions the compute calls do not check.
  *

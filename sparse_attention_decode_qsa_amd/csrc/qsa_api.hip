@@ -20,7 +20,8 @@ hipError_t launch_pool_build(const int8_t*, const int32_t*, const int32_t*, int,
 hipError_t launch_cache_append(const void*, const void*, const int8_t*, const int32_t*, void*, void*, int8_t*,
                                int16_t*, const int32_t*, const int32_t*, int, int, int, hipStream_t);
 hipError_t launch_index_score_pooled(const int8_t*, const int16_t*, const int32_t*, const int32_t*, int, int, int,
-                                     int32_t*, int32_t*, hipStream_t);
+                                     int32_t*, int32_t*, const void*, const void*, const int8_t*, const int32_t*,
+                                     void*, void*, int8_t*, int, hipStream_t);
 
 namespace {
 
@@ -194,6 +195,17 @@ size_t qsa_decode_workspace_size(int B, int Hq, int Hkv, int max_blocks, int k, 
 
 namespace {
 
+// The decode step's cache writes, made by the pooled scan (qsa_decode_step_pooled).
+struct StepIn {
+  const void* k_new;
+  const void* v_new;
+  const int8_t* idx_new;
+  const int32_t* write;
+  void* k_cache;
+  void* v_cache;
+  int8_t* idx_cache;
+};
+
 // The chain of qsa_decode / qsa_decode_pooled: the scan reads idx_cache (int8 keys) or, when
 // pooled is given, the side cache of pooled keys; the rest is shared.
 qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const int16_t* pooled,
@@ -202,7 +214,7 @@ qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_
                           int idx_dim, int page_size, int max_pages_per_seq, int max_blocks, int k, int P,
                           float softmax_scale, int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
                           float* partial_out, float* partial_lse, float* out, float* out_lse, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, const StepIn* step = nullptr) {
   const int8_t* keys = pooled ? reinterpret_cast<const int8_t*>(pooled) : idx_cache;
   if (T < 1 || (pooled && T != 1)) return QSA_ERR_SHAPE;
   if (T > kMaxDraft) return QSA_ERR_UNSUPPORTED;
@@ -224,7 +236,11 @@ qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_
   char* ws_attn = static_cast<char*>(workspace) + pmb + tb;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = pooled ? launch_index_score_pooled(q_idx, pooled, page_table, context_lens, B, max_pages_per_seq,
-                                                    max_blocks, block_scores, page_max, s)
+                                                    max_blocks, block_scores, page_max,
+                                                    step ? step->k_new : nullptr, step ? step->v_new : nullptr,
+                                                    step ? step->idx_new : nullptr, step ? step->write : nullptr,
+                                                    step ? step->k_cache : nullptr, step ? step->v_cache : nullptr,
+                                                    step ? step->idx_cache : nullptr, Hkv, s)
                         : launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
                                              max_blocks, block_scores, page_max, T, s);
   if (e == hipSuccess)
@@ -298,6 +314,26 @@ qsa_status_t qsa_decode_multi(const void* q, const int8_t* q_idx, const int8_t* 
                       workspace_bytes, stream);
 }
 
+qsa_status_t qsa_decode_step_pooled(const void* k_new, const void* v_new, const int8_t* idx_new, const int32_t* write,
+                                    void* k_cache, void* v_cache, int8_t* idx_cache, int16_t* pooled_cache,
+                                    const void* q, const int8_t* q_idx, const int32_t* page_table,
+                                    const int32_t* context_lens, int B, int Hq, int Hkv, int head_dim,
+                                    int n_idx_heads, int idx_dim, int page_size, int max_pages_per_seq,
+                                    int max_blocks, int k, int P, float softmax_scale, int32_t* block_scores,
+                                    int32_t* sel_blocks, int32_t* sel_count, float* partial_out, float* partial_lse,
+                                    float* out, float* out_lse, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (B > 0 && (!k_new || !v_new || !idx_new || !idx_cache || !pooled_cache)) return QSA_ERR_NULL;
+  if (B > 0 && (misaligned(k_new) || misaligned(v_new) || misaligned(idx_new) || misaligned(pooled_cache)))
+    return QSA_ERR_SHAPE;
+  if (Hkv > 64) return QSA_ERR_UNSUPPORTED;
+  const StepIn step{k_new, v_new, idx_new, write, k_cache, v_cache, idx_cache};
+  return decode_chain(q, q_idx, nullptr, pooled_cache, k_cache, v_cache, page_table, context_lens, B, 1, Hq, Hkv,
+                      head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
+                      block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, workspace,
+                      workspace_bytes, stream, &step);
+}
+
 qsa_status_t qsa_pool_build(const int8_t* idx_cache, const int32_t* page_table, const int32_t* context_lens, int B,
                             int n_idx_heads, int idx_dim, int page_size, int max_pages_per_seq,
                             int16_t* pooled_cache, void* stream) {
@@ -337,7 +373,8 @@ qsa_status_t qsa_index_score_pooled(const int8_t* q_idx, const int16_t* pooled_c
                                 n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, block_scores);
   if (st != QSA_OK || B == 0) return st;
   return hip_status(launch_index_score_pooled(q_idx, pooled_cache, page_table, context_lens, B, max_pages_per_seq,
-                                              max_blocks, block_scores, page_max, (hipStream_t)stream));
+                                              max_blocks, block_scores, page_max, nullptr, nullptr, nullptr, nullptr,
+                                              nullptr, nullptr, nullptr, 0, (hipStream_t)stream));
 }
 
 qsa_status_t qsa_check_pages(const int32_t* page_table, const int32_t* context_lens, int B,

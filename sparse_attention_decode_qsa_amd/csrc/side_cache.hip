@@ -121,11 +121,27 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 // counted in the page maximum.
 typedef short short2v __attribute__((ext_vector_type(2)));
 
+// The decode step's cache writes, done by the scan (k_new == nullptr: none). The wave that
+// scans the page holding the new token t = L_b - 1 writes its K/V/indexer rows and recomputes
+// the side-cache entry of block t/4 from the block's earlier indexer rows plus the new key,
+// and scores that block from the recomputed entry. Nothing else in the launch reads what it
+// writes, so the results equal those of cache_append_kernel followed by the scan.
+struct StepWrite {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int8_t* idx_new;
+  const int32_t* write;   // nullable: every request writes
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int8_t* idx_cache;
+  int Hkv;
+};
+
 template <int WAVES, int PPW>
 __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
-    const int8_t* __restrict__ q_idx, const int16_t* __restrict__ pooled, const int32_t* __restrict__ page_table,
+    const int8_t* __restrict__ q_idx, int16_t* pooled, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ lens, int max_pages, int max_blocks, int32_t* __restrict__ scores,
-    int32_t* __restrict__ page_max) {
+    int32_t* __restrict__ page_max, StepWrite step) {
   const int b = blockIdx.y, lane = lane_id(), wave = threadIdx.x >> 6;
   const int L = lens[b];
   const int npages = (L + kPageSize - 1) / kPageSize;
@@ -144,18 +160,56 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
   }
   // every load of the wave's pages is issued before any arithmetic
   i32x4 v[PPW][8];
+  int pages[PPW];
 #pragma unroll
   for (int k = 0; k < PPW; ++k) {
     if (p0 + k >= npages) break;
     const int page = page_table[(size_t)b * max_pages + p0 + k];
+    pages[k] = page;
     const int8_t* base = reinterpret_cast<const int8_t*>(pooled) + (size_t)page * kPooledPageBytes + 16 * lane;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[k][i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + 1024 * i));
   }
+  const bool writes = step.k_new != nullptr && L > 0 && (step.write == nullptr || step.write[b] != 0);
 #pragma unroll
   for (int k = 0; k < PPW; ++k) {
     const int p = p0 + k;
     if (p >= npages) break;
+    if (writes && p == npages - 1) {   // this page holds the new token (the same for the whole wave)
+      const int page = pages[k];
+      const int row = (L - 1) % kPageSize;
+      const size_t kv_row = ((size_t)page * kPageSize + row) * step.Hkv * kHeadDim;
+      const int nvec = step.Hkv * kHeadDim / 8;
+      const i32x4* ks = reinterpret_cast<const i32x4*>(step.k_new + (size_t)b * step.Hkv * kHeadDim);
+      const i32x4* vs = reinterpret_cast<const i32x4*>(step.v_new + (size_t)b * step.Hkv * kHeadDim);
+      for (int x = lane; x < nvec; x += 64) {
+        reinterpret_cast<i32x4*>(step.k_cache + kv_row)[x] = ks[x];
+        reinterpret_cast<i32x4*>(step.v_cache + kv_row)[x] = vs[x];
+      }
+      const int8_t* in = step.idx_new + (size_t)b * kIdxTokenBytes;
+      int8_t* page_keys = step.idx_cache + (size_t)page * kIdxPageBytes;
+      if (lane < 16)
+        reinterpret_cast<i32x4*>(page_keys + row * kIdxTokenBytes)[lane] = reinterpret_cast<const i32x4*>(in)[lane];
+      // new entry of slot row/4: the half holding that slot recomputes its 8 keys per lane
+      const int slot = row / kTokensPerBlock;
+      if (hf == (slot & 1)) {
+        int sum[8];
+        const int2 nw = *reinterpret_cast<const int2*>(in + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] = sbyte(e < 4 ? nw.x : nw.y, e & 3);
+        for (int u = slot * kTokensPerBlock; u < row; ++u) {
+          const int2 ow = *reinterpret_cast<const int2*>(page_keys + u * kIdxTokenBytes + 8 * c);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[e] += sbyte(e < 4 ? ow.x : ow.y, e & 3);
+        }
+        const i32x4 packed = {(sum[0] & 0xFFFF) | (sum[1] << 16), (sum[2] & 0xFFFF) | (sum[3] << 16),
+                              (sum[4] & 0xFFFF) | (sum[5] << 16), (sum[6] & 0xFFFF) | (sum[7] << 16)};
+        *reinterpret_cast<i32x4*>(reinterpret_cast<int8_t*>(pooled) + (size_t)page * kPooledPageBytes +
+                                  slot * kPooledBlockBytes + 16 * c) = packed;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[k][i] = i == slot / 2 ? packed : v[k][i];
+      }
+    }
     int tot[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -205,13 +259,19 @@ hipError_t launch_cache_append(const void* k_new, const void* v_new, const int8_
   return hipGetLastError();
 }
 
+// k_new == nullptr: the scan alone; otherwise it also makes the decode step's cache writes.
 hipError_t launch_index_score_pooled(const int8_t* q_idx, const int16_t* pooled, const int32_t* page_table,
                                      const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
-                                     int32_t* page_max, hipStream_t stream) {
+                                     int32_t* page_max, const void* k_new, const void* v_new, const int8_t* idx_new,
+                                     const int32_t* write, void* k_cache, void* v_cache, int8_t* idx_cache, int Hkv,
+                                     hipStream_t stream) {
   constexpr int kPagesPerWave = 1;
   const unsigned gx = (unsigned)((max_pages + kSideWaves * kPagesPerWave - 1) / (kSideWaves * kPagesPerWave));
+  const StepWrite step{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), idx_new, write,
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), idx_cache, Hkv};
   hipLaunchKernelGGL((index_score_pooled_kernel<kSideWaves, kPagesPerWave>), dim3(gx, B), dim3(kSideWaves * 64), 0,
-                     stream, q_idx, pooled, page_table, lens, max_pages, max_blocks, scores, page_max);
+                     stream, q_idx, const_cast<int16_t*>(pooled), page_table, lens, max_pages, max_blocks, scores,
+                     page_max, step);
   return hipGetLastError();
 }
 

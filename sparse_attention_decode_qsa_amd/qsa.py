@@ -47,6 +47,8 @@ SIGNATURES = {
     "qsa_index_score_multi": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "qsa_decode_multi": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                               _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "qsa_decode_step_pooled": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                    _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "qsa_pool_build": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "qsa_cache_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "qsa_index_score_pooled": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
@@ -393,6 +395,51 @@ class MultiDecodePlan:
             max_pages, self.max_blocks, k, P, ctypes.c_float(scale), _ptr(self.scores), _ptr(self.sel),
             _ptr(self.sel_count), _ptr(self.partial_out), _ptr(self.partial_lse), _ptr(self.out),
             _ptr(self.out_lse), self.workspace.ptr(), self.workspace.nbytes]
+
+    def run(self, stream=None):
+        s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
+        _check(self._fn(*self._args, s))
+        return self.out, self.out_lse
+
+
+class StepPlan:
+    """One decode step on the side cache per run(): the new token's cache writes and the decode
+    (qsa_decode_step_pooled; the same results as AppendPlan.run() then DecodePlan(pooled).run())."""
+
+    def __init__(self, k_new, v_new, idx_new, q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens,
+                 pooled, P, k=MAX_K, softmax_scale=None, write=None):
+        for t, dt, n in ((k_new, torch.bfloat16, "k_new"), (v_new, torch.bfloat16, "v_new"),
+                         (idx_new, torch.int8, "idx_new"), (q, torch.bfloat16, "q"), (q_idx, torch.int8, "q_idx"),
+                         (idx_cache, torch.int8, "idx_cache"), (k_cache, torch.bfloat16, "k_cache"),
+                         (v_cache, torch.bfloat16, "v_cache"), (page_table, torch.int32, "page_table"),
+                         (context_lens, torch.int32, "context_lens")):
+            _need(t, dt, n)
+        _need(pooled, torch.int16, "pooled", 4)
+        if write is not None:
+            _need(write, torch.int32, "write", 1)
+        self.inputs = (k_new, v_new, idx_new, q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens,
+                       pooled, write)
+        B, Hq, D = q.shape
+        Hkv = k_cache.shape[2]
+        max_pages = page_table.shape[1]
+        self.max_blocks = max_pages * PAGE_SIZE // 4
+        dev = q.device
+        self.scores = torch.empty((B, self.max_blocks), dtype=torch.int32, device=dev)
+        self.sel = torch.empty((B, k), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.partial_out = torch.empty((B, P, Hq, D), dtype=torch.float32, device=dev)
+        self.partial_lse = torch.empty((B, P, Hq), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        self.out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.workspace = Workspace(decode_workspace_size(B, Hq, Hkv, self.max_blocks, k, P), dev)
+        scale = D ** -0.5 if softmax_scale is None else softmax_scale
+        self._fn = lib().qsa_decode_step_pooled
+        self._args = [
+            _ptr(k_new), _ptr(v_new), _ptr(idx_new), _ptr(write), _ptr(k_cache), _ptr(v_cache), _ptr(idx_cache),
+            _ptr(pooled), _ptr(q), _ptr(q_idx), _ptr(page_table), _ptr(context_lens), B, Hq, Hkv, D,
+            q_idx.shape[1], q_idx.shape[2], k_cache.shape[1], max_pages, self.max_blocks, k, P, ctypes.c_float(scale),
+            _ptr(self.scores), _ptr(self.sel), _ptr(self.sel_count), _ptr(self.partial_out), _ptr(self.partial_lse),
+            _ptr(self.out), _ptr(self.out_lse), self.workspace.ptr(), self.workspace.nbytes]
 
     def run(self, stream=None):
         s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()

@@ -248,3 +248,20 @@ def test_index_score_multi_host_checks():
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 5, 4, 64, 64, 16, 256, FAKE, None, None) == UNSUP
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 4, 64, 64, 16, 255, FAKE, None, None) == SHAPE
     assert f(FAKE, None, FAKE, FAKE, 2, 2, 4, 64, 64, 16, 256, FAKE, None, None) == NULL
+
+
+def test_decode_step_pooled_host_checks():
+    L = qsa.lib()
+    f = L.qsa_decode_step_pooled
+    args = [FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 32, 4, 128, 4, 64, 64, 16,
+            256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 26, None]
+    bad = list(args); bad[0] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[7] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[7] = FAKE.value + 4
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[13] = 33
+    assert f(*bad) == SHAPE                        # Hq % Hkv
+    bad = list(args); bad[32] = 100
+    assert f(*bad) == WS

@@ -167,3 +167,30 @@ def test_full_w4_pooled_chain():
     for b, L in enumerate(x.lengths):
         nblk = (L + 3) // 4
         assert torch.equal(plain.scores[b, :nblk], fast.scores[b, :nblk])
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_fused_step_equals_append_then_decode(masked):
+    """qsa_decode_step_pooled (cache writes made by the scan) against qsa_cache_append followed
+    by qsa_decode_pooled: every result and every cache, main and side, bit for bit."""
+    lens = (1, 4, 5, 64, 65, 130, 2049, 9000, 70001)
+    x = make_inputs(W(lens, P=4), 36, "cuda")
+    write = (torch.tensor([b % 2 for b in range(len(lens))], dtype=torch.int32, device="cuda") if masked else None)
+    k, v, idx, side, k_new, v_new, i_new = _stripped(x)
+    k2, v2, idx2, side2 = k.clone(), v.clone(), idx.clone(), side.clone()
+    # A: the two calls
+    qsa.cache_append(k_new, v_new, i_new, k, v, idx, x.page_table, x.context_lens, pooled=side, write=write)
+    a = qsa.DecodePlan(x.q, x.q_idx, idx, k, v, x.page_table, x.context_lens, 4, pooled=side)
+    a.run()
+    # B: the fused step
+    bplan = qsa.StepPlan(k_new, v_new, i_new, x.q, x.q_idx, idx2, k2, v2, x.page_table, x.context_lens, side2, 4,
+                         write=write)
+    bplan.run()
+    torch.cuda.synchronize()
+    for name, u, w in (("k", k, k2), ("v", v, v2), ("idx", idx, idx2), ("side", side, side2)):
+        assert torch.equal(u.view(torch.int8), w.view(torch.int8)), name
+    for name in ("sel", "sel_count", "partial_out", "partial_lse", "out", "out_lse"):
+        assert torch.equal(getattr(a, name).view(torch.int32), getattr(bplan, name).view(torch.int32)), name
+    for b, L in enumerate(lens):
+        n = (L + 3) // 4
+        assert torch.equal(a.scores[b, :n], bplan.scores[b, :n]), b
