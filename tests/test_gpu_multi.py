@@ -108,3 +108,23 @@ def test_full_w4_four_draft_tokens():
         ref = oracle.decode_request(bf16_bits(q[b, t]), qi[b, t].cpu().numpy(), a["idx_cache"], a["k_cache"],
                                     a["v_cache"], a["page_table"][b], Lt, 4, x.scale)
         check_request(g, r, ref, Lt, what=f"w4 T4 b{b} t{t}")
+
+
+def test_maximum_context_four_draft_tokens():
+    """T = 4 at the largest context (one request of 1,048,576 tokens): every draft token's
+    selection equals a single-token decode's at its length (through qsa_decode)."""
+    T = 4
+    x = make_inputs(Workload("max4", 1, ("list", 1048576), 32, 4, 4, max_context=1048576), 16, "cuda")
+    q, qi = draft_queries(x, T, 16)
+    plan, g = _run(x, q, qi, 4)
+    for t in range(T):
+        Lt = oracle.draft_length(x.lengths[0], T, t)
+        lens_t = torch.tensor([Lt], dtype=torch.int32, device="cuda")
+        single = qsa.DecodePlan(q[:, t].contiguous(), qi[:, t].contiguous(), x.idx_cache, x.k_cache, x.v_cache,
+                                x.page_table, lens_t, 4)
+        single.run()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.sel[t], single.sel[0]) and int(plan.sel_count[t]) == int(single.sel_count[0])
+        n = (Lt + 3) // 4
+        assert torch.equal(plan.scores[t, :n], single.scores[0, :n])
+        assert torch.allclose(plan.out[t], single.out[0], atol=2e-6, rtol=1e-5)

@@ -193,6 +193,16 @@ def test_w5_shape_whole_batch():
     check_properties(x, g)
 
 
+def test_maximum_context_one_request():
+    """The largest context the ABI takes: one request of 1,048,576 tokens (262,144 blocks, the
+    selection's widest layout of four 64-block chunks per thread, with page maxima), checked
+    whole against the oracle."""
+    x = make_inputs(W("max", (1048576,), P=4, max_context=1048576), 15, "cuda")
+    assert x.max_blocks == 262144
+    g, _ = check_whole(x, what="max")
+    check_properties(x, g)
+
+
 def test_check_pages_verdicts():
     """The precondition check reports bad lengths and the first out-of-range page id."""
     x = make_inputs(W("chk", (5000, 9000, 130, 70, 0)), 13, "cuda")
