@@ -342,7 +342,8 @@ qsa_status_t qsa_check_pages(const int32_t* page_table, const int32_t* context_l
                              int max_pages_per_seq, int page_size, int num_pages, int32_t* verdict,
                              void* stream);
 
-/* Fill a workspace with zero bytes on `stream` (for its first use). */
+/* Fill a workspace with zero bytes on `stream`. No entry point needs it (a workspace needs no
+ * initialisation); it is there for callers that want known memory contents. */
 qsa_status_t qsa_workspace_clear(void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -33,7 +33,6 @@ qsa_status_t hip_status(hipError_t e) {
   return QSA_ERR_HIP;
 }
 
-
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 qsa_status_t check_index(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
@@ -117,7 +116,7 @@ const char* qsa_status_string(int s) {
 
 int qsa_last_hip_error(void) { return g_last_hip_error; }
 
-int qsa_version(void) { return 100; }
+int qsa_version(void) { return 200; }   // 0.2.0: side cache, multi-token decode, page check
 
 qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
                              const int32_t* context_lens, int B, int n_idx_heads, int idx_dim,
@@ -206,8 +205,10 @@ struct StepIn {
   int8_t* idx_cache;
 };
 
-// The chain of qsa_decode / qsa_decode_pooled: the scan reads idx_cache (int8 keys) or, when
-// pooled is given, the side cache of pooled keys; the rest is shared.
+// The chain of qsa_decode, qsa_decode_pooled, qsa_decode_step_pooled and qsa_decode_multi: the
+// scan reads idx_cache (int8 keys, T draft queries per request) or, when pooled is given, the
+// side cache of pooled keys (and makes the step's cache writes when step is given); the
+// selection, attention and merge run on the B*T virtual requests.
 qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const int16_t* pooled,
                           const void* k_cache, const void* v_cache, const int32_t* page_table,
                           const int32_t* context_lens, int B, int T, int Hq, int Hkv, int head_dim, int n_idx_heads,

@@ -11,13 +11,22 @@
 // u = uint32(score) ^ 0x80000000. Thread t owns the R chunks c = t + 1024*r of 64
 // consecutive blocks [64c, 64c + 64), so a per-thread 64-bit mask over a chunk is one
 // word of a bitmap in block order.
-//   1. load    the keys (in registers when R = 1, else re-read from memory) and the
-//              range [lo, hi] = [min u, max u] over the request.
-//   2. sample  keys 0, 16, 32, 48 of every chunk are histogrammed over [lo, hi]; the
-//              lower edge of the bin holding their top 2*k*(samples/n) + 8 is a threshold
-//              tau that about 2k keys reach.
-//   3. list    if between k and 4096 keys reach tau, those candidates go to an LDS list
-//              (key, block); otherwise the narrowing below runs over every key.
+// A short candidate list comes first, in one of two ways:
+//   A. page maxima (written by the scan; used when there are at least k pages): the page
+//      maxima are histogrammed over their [min, max] in 2048 bins and tau = the lower edge of
+//      the bin holding the k-th largest. At least k pages reach tau, each with a block >= tau,
+//      so the k-th key is >= tau and only pages reaching tau can hold kept blocks. Those pages
+//      (about k) are compacted, their scores read by 4 lanes per page with every load of a
+//      batch in flight, and the keys >= tau go to an LDS list (key, block) of at most 4096.
+//   B. otherwise, or if that list would overflow:
+//      1. load    the keys (in registers when R = 1, else re-read from memory) and the
+//                 range [lo, hi] = [min u, max u] over the request.
+//      2. sample  keys 0, 16, 32, 48 of every chunk are histogrammed over [lo, hi]; the
+//                 lower edge of the bin holding their top 2*k*(samples/n) + 8 is a
+//                 threshold tau that about 2k keys reach.
+//      3. list    if between k and 4096 keys reach tau, those candidates go to the list;
+//                 otherwise the narrowing below runs over every key.
+// Then:
 //   4. narrow  repeat: histogram the keys inside [lo, hi] into 2048 bins of width
 //              2^shift (shift = bitlen(hi - lo) - 11, at least 0); the bin holding the
 //              need-th largest key becomes [lo, hi]; need drops by the keys above it.
@@ -26,8 +35,11 @@
 //              block order). At most 3 passes for 32-bit keys.
 //   5. output  kept and tie masks per chunk; block prefix sums of their popcounts give
 //              the tie ranks and the ascending output positions.
-// Histogram loops over all keys are branch-free: a key that is not counted goes to the
-// lane's own dummy bin. Requests with at most k blocks keep all of them.
+// The bucket search runs on one wave (DPP prefix sums) while the other waves clear the
+// second histogram buffer. Histogram loops over all keys are branch-free: a key that is
+// not counted goes to the lane's own dummy bin. Requests with at most k blocks keep all of
+// them. With T draft tokens per request (multi-token decode) workgroup r is the virtual
+// request r = b*T + t, of length L_b - (T-1-t).
 #include "qsa_device.h"
 
 namespace qsa {
