@@ -108,8 +108,8 @@ def main():
                     help="with --pooled: make the step's cache writes with qsa_cache_append before "
                          "qsa_decode_pooled instead of inside the scan (qsa_decode_step_pooled)")
     ap.add_argument("--draft", type=int, default=1, metavar="T",
-                    help="multi-token decode: T draft tokens per request (qsa_decode_multi); a call then "
-                         "decodes B*T tokens")
+                    help="multi-token decode: T new tokens per request (qsa_decode_multi; drafts for T <= 4, "
+                         "a prefill chunk beyond); a call then decodes B*T tokens")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 copies of MIB MiB each with qsa_calib_copy (the scan's "
                          "kind of loads and stores), so that hardware byte counters can be scaled "
@@ -278,6 +278,10 @@ def main():
         algo += sum(2 * w.hkv * 256 + 256 + 512 + 256 * ((L - 1) % 4) for L in lengths if L)
         k1_bytes += pooled_keys - IDX_TOKEN_BYTES * sum(lengths)
     gbs = algo / (ms_step * 1e-3) / 1e9
+    # With more than 4 new tokens per request the scan is an int8 matrix product on the matrix
+    # cores: 2*256 operations per (query, visible token); it also writes every query's block
+    # scores. Its roofline is the larger of the two times at peak.
+    scan_ops = 2 * 256 * sum(vlens) if D > 4 else 0
     k1_gbs = k1_bytes / (ms_k1 * 1e-3) / 1e9
 
     # HBM bytes per launch of the scan from the committed counter runs, while the scan's
@@ -321,7 +325,20 @@ def main():
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "read_ceiling_GBps": round(read_gbs, 1),
         "algorithmic_bytes_per_call": algo,
-        "roofline": {
+        "roofline": ({
+            "kernel": f"index_score_mq_kernel (T={D} queries per request: int8 MFMA 16x16x64 scan)",
+            "bound": "mfma" if scan_ops / 5.0e15 > k1_bytes / (HBM_PEAK_GBS * 1e9) else "hbm",
+            "achieved": round(scan_ops / (ms_k1 * 1e-3) / 1e12, 1),
+            "peak": 5000.0,
+            "unit": "TOP/s (int8 dense)",
+            "frac": round(scan_ops / (ms_k1 * 1e-3) / 5.0e15, 4),
+            "hbm_achieved_GBps": round(k1_bytes / (ms_k1 * 1e-3) / 1e9, 1),
+            "hbm_frac": round(k1_bytes / (ms_k1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(ms_k1 * 1000, 3),
+            "ops_per_launch": scan_ops,
+            "bytes_per_launch": k1_bytes,
+        } if D > 4 else {
             "kernel": ("index_score_pooled_kernel (side-cache scan + scores)" if args.pooled
                        else f"index_score_kernel<T={D}> (indexer scan + pooling + scores of {D} draft tokens)"
                        if D > 1 else "index_score_kernel (indexer scan + pooling + scores)"),
@@ -334,7 +351,7 @@ def main():
             "frac_of_read_ceiling": round(k1_gbs / read_gbs, 4),
             "avg_launch_us": round(ms_k1 * 1000, 3),
             "bytes_per_launch": k1_bytes,
-        },
+        }),
     }
     if args.copy_calibration:
         from sparse_attention_decode_qsa_amd import calib

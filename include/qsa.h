@@ -208,8 +208,10 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * qsa_decode_multi - multi-token decode: T draft tokens per request (speculative decoding with
- * a multi-token-prediction head), 1 <= T <= 4, B*T <= 65535.
+ * qsa_decode_multi - multi-token decode: T new tokens per request, 1 <= T <= 4096, B*T <= 65535
+ * (draft tokens of speculative decoding with a multi-token-prediction head, T <= 4, or a
+ * prefill chunk). For T <= 4 the scan uses int8 dot products per query; for larger T it runs
+ * as an int8 matrix product of the T queries with every page's keys on the matrix cores.
  *
  * The T new tokens are the last T positions of each request's cache (context_lens counts them
  * all). Draft token t, at position L_b - T + t, is decoded exactly as qsa_decode decodes a
@@ -229,7 +231,8 @@ size_t qsa_decode_multi_workspace_size(int B, int T, int Hq, int Hkv, int max_bl
  * per-page maxima [B*T, max_pages_per_seq]) of all T draft tokens of every request, from one
  * read of the indexer keys. q_idx [B, T, n_idx_heads, idx_dim]; block_scores [B*T, max_blocks];
  * row b*T + t holds draft token t's scores for blocks < ceil((L_b - T + 1 + t) / 4). Checks as
- * qsa_index_score, plus 1 <= T <= 4 and B*T <= 65535. */
+ * qsa_index_score, plus 1 <= T <= 4096, B*T <= 65535, max_blocks % 4 == 0 and block_scores
+ * 16-byte aligned. */
 qsa_status_t qsa_index_score_multi(const int8_t* q_idx, const int8_t* idx_cache,
                                    const int32_t* page_table, const int32_t* context_lens, int B,
                                    int T, int n_idx_heads, int idx_dim, int page_size,

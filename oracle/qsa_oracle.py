@@ -57,8 +57,8 @@ Readings where the pages leave a step open (each is repeated in the design notes
                   A request whose write flag is 0 writes nothing (section "What the pull
                   request actually changes", bullets: synthetic batches must not write the
                   side caches); neither does a request of length 0.
-  R13 draft       multi-token decode (speculative drafts of T <= 4 tokens): the T new tokens
-                  are the last T positions of the cache (L counts them all); draft token t
+  R13 draft       multi-token decode (T new tokens: speculative drafts, or a prefill chunk):
+                  the T new tokens are the last T positions of the cache (L counts them all); token t
                   sits at position L-T+t and is decoded exactly as a single token at length
                   L-T+1+t - its own indexer query and selection, attention over its own kept
                   tokens, slices of that length - so it sees itself and the tokens before it.

@@ -116,6 +116,87 @@ __device__ __forceinline__ void slice_merge_regs(const float* __restrict__ so, c
   }
 }
 
+// P * C <= 8 (every slice in one share, as with many virtual requests): the same operations,
+// four dims per thread (16-byte loads and stores), four heads per workgroup of 128 threads.
+template <int C>
+__global__ __launch_bounds__(128) void slice_merge_v4_kernel(const float* __restrict__ so,
+                                                             const float* __restrict__ sl, int P, int Hq,
+                                                             float* __restrict__ part_out,
+                                                             float* __restrict__ part_lse,
+                                                             float* __restrict__ out,
+                                                             float* __restrict__ out_lse) {
+  constexpr int NV = 8;
+  constexpr int PM = NV / C;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 5), b = blockIdx.y, d0 = 4 * (threadIdx.x & 31);
+  if (h >= Hq) return;
+  const int n = P * C;
+  const float* col = so + ((size_t)b * n * Hq + h) * kHeadDim + d0;
+  const float* lcol = sl + (size_t)b * n * Hq + h;
+  const size_t stride = (size_t)Hq * kHeadDim;
+  float lv[NV];
+  f32x4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    lv[i] = i < n ? lcol[(size_t)i * Hq] : -INFINITY;
+    v[i] = i < n ? *reinterpret_cast<const f32x4*>(col + i * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float mp[PM], lp[PM];
+#pragma unroll
+  for (int p = 0; p < PM; ++p) {
+    float Mp = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < C; ++c) Mp = fmaxf(Mp, lv[p * C + c]);
+    float ws = 0.f;
+    if (Mp != -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (lv[p * C + c] != -INFINITY) ws += __expf(lv[p * C + c] - Mp);
+    }
+    mp[p] = Mp;
+    lp[p] = ws > 0.f ? Mp + __logf(ws) : -INFINITY;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < PM; ++p) M = fmaxf(M, lp[p]);
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < PM; ++p) {
+    if (p >= P) break;
+    float ws = 0.f;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if (mp[p] != -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const float l = lv[p * C + c];
+        if (l == -INFINITY) continue;
+        const float w = __expf(l - mp[p]);
+        ws += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] += w * v[p * C + c][e];
+      }
+    }
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = ws > 0.f ? a[e] / ws : 0.f;
+    *reinterpret_cast<f32x4*>(part_out + (((size_t)b * P + p) * Hq + h) * kHeadDim + d0) = o;
+    if (d0 == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp[p];
+    if (M != -INFINITY && lp[p] != -INFINITY) {
+      const float w = __expf(lp[p] - M);
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += w * o[e];
+    }
+  }
+  if (out) {
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = wsum > 0.f ? acc[e] / wsum : 0.f;
+    *reinterpret_cast<f32x4*>(out + ((size_t)b * Hq + h) * kHeadDim + d0) = r;
+    if (out_lse && d0 == 0) out_lse[(size_t)b * Hq + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+  }
+}
+
 // Any P * C: the share lse values go through LDS, and slice p+1's share values are loaded
 // while slice p is combined.
 __device__ __forceinline__ void slice_merge_lds(const float* __restrict__ so, const float* __restrict__ sl,
@@ -214,8 +295,22 @@ hipError_t launch_lse_merge(const float* po, const float* pl, int B, int P, int 
 hipError_t launch_slice_merge(const float* so, const float* sl, int B, int P, int C, int Hq, float* part_out,
                               float* part_lse, float* out, float* out_lse, hipStream_t stream) {
   if ((C != 1 && C != 2 && C != 4 && C != 8) || P > kMaxSlices) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(slice_merge_kernel, dim3(Hq, B), dim3(kHeadDim), 0, stream, so, sl, P, C, Hq, part_out,
-                     part_lse, out, out_lse);
+  if (P * C <= 8) {
+    const dim3 grid((Hq + 3) / 4, B);
+    switch (C) {
+      case 1: hipLaunchKernelGGL(slice_merge_v4_kernel<1>, grid, dim3(128), 0, stream, so, sl, P, Hq, part_out,
+                                 part_lse, out, out_lse); break;
+      case 2: hipLaunchKernelGGL(slice_merge_v4_kernel<2>, grid, dim3(128), 0, stream, so, sl, P, Hq, part_out,
+                                 part_lse, out, out_lse); break;
+      case 4: hipLaunchKernelGGL(slice_merge_v4_kernel<4>, grid, dim3(128), 0, stream, so, sl, P, Hq, part_out,
+                                 part_lse, out, out_lse); break;
+      default: hipLaunchKernelGGL(slice_merge_v4_kernel<8>, grid, dim3(128), 0, stream, so, sl, P, Hq, part_out,
+                                  part_lse, out, out_lse); break;
+    }
+  } else {
+    hipLaunchKernelGGL(slice_merge_kernel, dim3(Hq, B), dim3(kHeadDim), 0, stream, so, sl, P, C, Hq, part_out,
+                       part_lse, out, out_lse);
+  }
   return hipGetLastError();
 }
 

@@ -71,7 +71,7 @@ qsa_status_t check_attn(const void* q, const void* kc, const void* vc, const int
   if (B > 65535 || Hkv > 65535) return QSA_ERR_UNSUPPORTED;
   if (B == 0) return QSA_OK;
   if (!q || !kc || !vc || !page_table || !lens || !sel || !cnt || !po || !pl) return QSA_ERR_NULL;
-  if (misaligned(q) || misaligned(kc) || misaligned(vc)) return QSA_ERR_SHAPE;
+  if (misaligned(q) || misaligned(kc) || misaligned(vc) || misaligned(po)) return QSA_ERR_SHAPE;
   return QSA_OK;
 }
 
@@ -82,6 +82,7 @@ qsa_status_t check_merge(const float* po, const float* pl, int B, int P, int Hq,
   if (B > 65535 || Hq > 65535) return QSA_ERR_UNSUPPORTED;
   if (B == 0) return QSA_OK;
   if (!po || !pl || !out) return QSA_ERR_NULL;
+  if (misaligned(out)) return QSA_ERR_SHAPE;
   return QSA_OK;
 }
 
@@ -218,7 +219,7 @@ qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_
                           size_t workspace_bytes, void* stream, const StepIn* step = nullptr) {
   const int8_t* keys = pooled ? reinterpret_cast<const int8_t*>(pooled) : idx_cache;
   if (T < 1 || (pooled && T != 1)) return QSA_ERR_SHAPE;
-  if (T > kMaxDraft) return QSA_ERR_UNSUPPORTED;
+  if (T > kMaxQueries) return QSA_ERR_UNSUPPORTED;
   const int BT = B * T;   // virtual requests (request, draft token)
   qsa_status_t st = check_index(q_idx, keys, page_table, context_lens, B, n_idx_heads, idx_dim, page_size,
                                 max_pages_per_seq, max_blocks, block_scores);
@@ -288,16 +289,17 @@ qsa_status_t qsa_index_score_multi(const int8_t* q_idx, const int8_t* idx_cache,
                                    int page_size, int max_pages_per_seq, int max_blocks, int32_t* block_scores,
                                    int32_t* page_max, void* stream) {
   if (T < 1) return QSA_ERR_SHAPE;
-  if (T > kMaxDraft || (long long)B * T > 65535) return QSA_ERR_UNSUPPORTED;
+  if (T > kMaxQueries || (long long)B * T > 65535) return QSA_ERR_UNSUPPORTED;
   qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim, page_size,
                                 max_pages_per_seq, max_blocks, block_scores);
   if (st != QSA_OK || B == 0) return st;
+  if (max_blocks % 4 != 0 || misaligned(block_scores)) return QSA_ERR_SHAPE;   // 16-byte score stores
   return hip_status(launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
                                        max_blocks, block_scores, page_max, T, (hipStream_t)stream));
 }
 
 size_t qsa_decode_multi_workspace_size(int B, int T, int Hq, int Hkv, int max_blocks, int k, int P) {
-  if (B <= 0 || T <= 0 || T > kMaxDraft) return 0;
+  if (B <= 0 || T <= 0 || T > kMaxQueries) return 0;
   return qsa_decode_workspace_size(B * T, Hq, Hkv, max_blocks, k, P);
 }
 

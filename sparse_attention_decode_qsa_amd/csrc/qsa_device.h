@@ -19,7 +19,7 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxK = 512;                    // kept blocks
 constexpr int kMaxGroup = 16;                 // query heads per KV head (MFMA rows)
 constexpr int kMaxSlices = 64;
-constexpr int kMaxDraft = 4;                  // draft tokens per request in multi-token decode
+constexpr int kMaxQueries = 4096;             // new tokens per request in multi-token decode
 
 // Host-side: byte counts of workspace regions are rounded up to 256.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

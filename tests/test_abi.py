@@ -230,8 +230,8 @@ def test_decode_multi_host_checks():
     args = [FAKE] * 7 + [2, 2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 26, None]
     bad = list(args); bad[8] = 0
     assert d(*bad) == SHAPE                        # T = 0
-    bad = list(args); bad[8] = 5
-    assert d(*bad) == UNSUP                        # more than 4 draft tokens
+    bad = list(args); bad[8] = 4097
+    assert d(*bad) == UNSUP                        # more than 4096 new tokens
     bad = list(args); bad[7], bad[8] = 20000, 4
     assert d(*bad) == UNSUP                        # B*T > 65535
     bad = list(args); bad[1] = None
@@ -245,7 +245,7 @@ def test_index_score_multi_host_checks():
     f = L.qsa_index_score_multi
     assert f(None, None, None, None, 0, 2, 4, 64, 64, 16, 256, None, None, None) == OK
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 0, 4, 64, 64, 16, 256, FAKE, None, None) == SHAPE
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 5, 4, 64, 64, 16, 256, FAKE, None, None) == UNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 4097, 4, 64, 64, 16, 256, FAKE, None, None) == UNSUP
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 4, 64, 64, 16, 255, FAKE, None, None) == SHAPE
     assert f(FAKE, None, FAKE, FAKE, 2, 2, 4, 64, 64, 16, 256, FAKE, None, None) == NULL
 

@@ -128,3 +128,42 @@ def test_maximum_context_four_draft_tokens():
         n = (Lt + 3) // 4
         assert torch.equal(plan.scores[t, :n], single.scores[0, :n])
         assert torch.allclose(plan.out[t], single.out[0], atol=2e-6, rtol=1e-5)
+
+
+@pytest.mark.parametrize("T,lens", [(5, LENS), (16, LENS), (37, (70, 130, 300, 2049, 5000)),
+                                    (64, (70, 130, 2049, 5000))])
+def test_many_queries_match_oracle(T, lens):
+    """T > 4 runs the scan as an int8 matrix product on the matrix cores; every (request,
+    token) pair against the oracle, including tokens that see fewer than T earlier ones."""
+    x = make_inputs(Workload("mq", len(lens), ("list",) + tuple(lens), 32, 4, 2), 55 + T, "cuda")
+    q, qi = draft_queries(x, T, 55 + T)
+    say(f"[many queries T={T}] lens={lens}")
+    _, g = _run(x, q, qi, 2)
+    a = oracle_arrays(x)
+    refs = oracle.decode_multi(bf16_bits(q), qi.cpu().numpy(), a["idx_cache"], a["k_cache"], a["v_cache"],
+                               a["page_table"], a["lengths"], T, 2, x.scale)
+    for b, L in enumerate(lens):
+        for t in range(T):
+            r = b * T + t
+            check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"T{T} b{b} t{t}")
+
+
+def test_prefill_chunk_1024_tokens():
+    """A prefill chunk: the last 1024 tokens of an 8192-token request; sampled tokens against
+    the oracle, every token's selection against the single-token decode at its length."""
+    T = 1024
+    x = make_inputs(Workload("chunk", 1, ("list", 8192), 32, 4, 4), 56, "cuda")
+    q, qi = draft_queries(x, T, 56)
+    plan, g = _run(x, q, qi, 4)
+    a = oracle_arrays(x)
+    for t in (0, 1, 511, 1022, 1023):
+        Lt = oracle.draft_length(8192, T, t)
+        ref = oracle.decode_request(bf16_bits(q[0, t]), qi[0, t].cpu().numpy(), a["idx_cache"], a["k_cache"],
+                                    a["v_cache"], a["page_table"][0], Lt, 4, x.scale)
+        check_request(g, t, ref, Lt, what=f"chunk t{t}")
+    # selection of every token equals the oracle's selection from the GPU's own scores
+    for t in range(0, T, 37):
+        Lt = oracle.draft_length(8192, T, t)
+        n = (Lt + 3) // 4
+        kept = oracle.select_blocks(g["scores"][t, :n])
+        assert np.array_equal(g["sel"][t, :len(kept)], kept), t
