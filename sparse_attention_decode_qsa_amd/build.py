@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
-SOURCES = ["index_score.hip", "topk_select.hip", "sparse_attn.hip", "lse_merge.hip", "check_pages.hip",
+SOURCES = ["index_score.hip", "index_score_mq.hip", "topk_select.hip", "sparse_attn.hip", "lse_merge.hip", "check_pages.hip",
            "side_cache.hip", "qsa_api.hip"]
 CALIB_LIB = os.path.join(PKG, "libqsa_calib.so")
 CALIB_SOURCES = ["calib_copy.hip"]

@@ -25,8 +25,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SCAN_SOURCES = ("csrc/index_score.hip", "csrc/qsa_device.h")
 SCAN_KERNEL = "index_score_kernel"
 CALIB_KERNEL = "calib_copy_kernel"
-CHAIN = ("cache_append_kernel", "index_score_kernel", "index_score_pooled_kernel", "topk_select_kernel",
-         "sparse_attn_kernel", "slice_merge_kernel", "lse_merge_kernel")
+CHAIN = ("cache_append_kernel", "index_score_kernel", "index_score_pooled_kernel", "index_score_mq_kernel",
+         "topk_select_kernel", "sparse_attn_kernel", "slice_merge_kernel", "slice_merge_v4_kernel",
+         "lse_merge_kernel")
 
 
 def scan_source_hash() -> str:
