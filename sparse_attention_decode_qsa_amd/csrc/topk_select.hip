@@ -60,25 +60,23 @@ struct SelShared {
   int cpages[kListCap];             // candidate page ids of the page-maximum path
   int scan[kSelWaves + 1];
   uint32_t red[2][kSelWaves];
-  int out[4];
+  uint32_t mm[2][2];                // (min, max) slots of the two block_minmax calls
+  int fb[2][4];                     // find_bucket results, one slot per histogram buffer
+  int ncp;                          // candidate pages of the page-maximum path
   int list_n;
 };
 
 
-// Block-wide min and max (every thread must call).
-__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, uint32_t* gmn,
+// Block-wide min and max into slot sh.mm[slot], which thread 0 set to (~0, 0) before an
+// earlier barrier (every thread must call; one barrier; the slot is not reused).
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, int slot, uint32_t* gmn,
                                              uint32_t* gmx) {
   mn = wave_min(mn);
   mx = wave_max(mx);
-  const int wave = threadIdx.x >> 6;
-  if (lane_id() == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
+  if (lane_id() == 0) { atomicMin(&sh.mm[slot][0], mn); atomicMax(&sh.mm[slot][1], mx); }
   __syncthreads();
-  uint32_t a = 0xFFFFFFFFu, b = 0u;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) { a = min(a, sh.red[0][w]); b = max(b, sh.red[1][w]); }
-  *gmn = a;
-  *gmx = b;
-  __syncthreads();
+  *gmn = sh.mm[slot][0];
+  *gmx = sh.mm[slot][1];
 }
 
 // Block-wide sum (every thread must call; ends with a barrier).
@@ -94,13 +92,15 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, SelShared& sh) {
   return s;
 }
 
-// Bin of the complete histogram holding the need-th largest key and the number of keys in
-// the bins above it (*beta = -1 when it holds fewer than `need`). Wave 0 searches (each
-// lane sums 32 bins, a reverse wave scan finds the lane, that lane walks its bins) while
-// the other threads clear the other histogram buffer; then the buffers swap. Every
-// thread must call it; it costs two barriers.
+// Bin of the complete histogram holding the need-th largest key, the number of keys in
+// the bins above it and in the bin itself (*beta = -1 when it holds fewer than `need`).
+// Wave 0 searches (each lane sums 32 bins, a reverse wave scan finds the lane, that lane
+// walks its bins) while the other threads clear the other histogram buffer; then the
+// buffers swap. The result goes through slot sh.fb[hsel]: the next call writes the other
+// slot, and the call after it comes after that call's barrier, when every thread has read
+// this one. Every thread must call it; it costs one barrier.
 __device__ __forceinline__ void find_bucket(SelShared& sh, int& hsel, uint32_t need, int* beta,
-                                            uint32_t* above) {
+                                            uint32_t* above, uint32_t* count = nullptr) {
   constexpr int per = kSelBins / 64;
   const int t = threadIdx.x, lane = lane_id();
   const uint32_t* h = sh.hbuf[hsel];
@@ -116,7 +116,7 @@ __device__ __forceinline__ void find_bucket(SelShared& sh, int& hsel, uint32_t n
     const uint32_t suf = (uint32_t)wave_inclusive_scan((int)c);
     const uint64_t hit = __ballot(suf - c < need && suf >= need);
     if (hit == 0) {
-      if (lane == 0) { sh.out[0] = -1; sh.out[1] = 0; sh.out[2] = 0; }
+      if (lane == 0) { sh.fb[hsel][0] = -1; sh.fb[hsel][1] = 0; sh.fb[hsel][2] = 0; }
     } else {
       const int L = __builtin_ctzll(hit);
       const int G = 63 - L;
@@ -125,15 +125,15 @@ __device__ __forceinline__ void find_bucket(SelShared& sh, int& hsel, uint32_t n
       const uint32_t v = lane < per ? h[G * per + (per - 1 - lane)] : 0u;
       const uint32_t sv = (uint32_t)wave_inclusive_scan((int)v);
       const bool mine = lane < per && runG + sv - v < need && runG + sv >= need;
-      if (mine) { sh.out[0] = G * per + (per - 1 - lane); sh.out[1] = (int)(runG + sv - v); sh.out[2] = (int)v; }
+      if (mine) { sh.fb[hsel][0] = G * per + (per - 1 - lane); sh.fb[hsel][1] = (int)(runG + sv - v); sh.fb[hsel][2] = (int)v; }
     }
   } else {
     for (int i = t - 64; i < kSelBins + 64; i += kSelThreads - 64) other[i] = 0;
   }
   __syncthreads();
-  *beta = sh.out[0];
-  *above = (uint32_t)sh.out[1];
-  __syncthreads();
+  *beta = sh.fb[hsel][0];
+  *above = (uint32_t)sh.fb[hsel][1];
+  if (count) *count = (uint32_t)sh.fb[hsel][2];
   hsel ^= 1;   // every thread flips its own copy: the cleared buffer is filled next
 }
 
@@ -147,8 +147,8 @@ __device__ __forceinline__ bool narrow_step(SelShared& sh, int& hsel, int shift,
                                             uint32_t* need) {
   int beta;
   uint32_t above;
-  find_bucket(sh, hsel, *need, &beta, &above);
-  const uint32_t count = (uint32_t)sh.out[2];
+  uint32_t count;
+  find_bucket(sh, hsel, *need, &beta, &above, &count);
   const uint32_t nlo = *lo + ((uint32_t)beta << shift);
   const uint32_t span = (1u << shift) - 1u;
   *hi = (*hi - nlo < span) ? *hi : nlo + span;
@@ -158,7 +158,7 @@ __device__ __forceinline__ bool narrow_step(SelShared& sh, int& hsel, int shift,
 }
 
 // Narrow [lo, hi] over the LDS candidate list (all candidates are >= lo), then write the
-// kept and tie masks of the candidates into the per-chunk words.
+// kept and tie masks of the candidates into the per-chunk words (zero on entry).
 template <int R>
 __device__ __forceinline__ void narrow_list_and_mark(SelShared& sh, int& hsel, uint32_t ncand, uint32_t lo, uint32_t hi,
                                                      uint32_t* need_io, bool* all_io, uint32_t* lo_out,
@@ -175,9 +175,7 @@ __device__ __forceinline__ void narrow_list_and_mark(SelShared& sh, int& hsel, u
     __syncthreads();
     if (narrow_step(sh, hsel, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
   }
-#pragma unroll
-  for (int r = 0; r < R; ++r) { kept_w[t + kSelThreads * r] = 0; tie_w[t + kSelThreads * r] = 0; }
-  __syncthreads();
+  // kept_w and tie_w were cleared at kernel start
   for (int i = t; i < (int)ncand; i += kSelThreads) {
     const uint32_t u = sh.list_u[i];
     const int j = sh.list_j[i];
@@ -239,6 +237,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     }
   }
   for (int i = t; i < kSelBins + 64; i += kSelThreads) sh.hbuf[0][i] = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) { kept_w[t + kSelThreads * r] = 0; tie_w[t + kSelThreads * r] = 0; }
+  if (t == 0) {
+    sh.mm[0][0] = sh.mm[1][0] = 0xFFFFFFFFu;
+    sh.mm[0][1] = sh.mm[1][1] = 0u;
+    sh.ncp = 0;
+    sh.list_n = 0;
+  }
   __syncthreads();
 
   bool have_list = false;
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       mx = max(mx, pv[i]);
     }
     uint32_t plo, phi;
-    block_minmax(mn, mx, sh, &plo, &phi);
+    block_minmax(mn, mx, sh, 0, &plo, &phi);
     hi = phi;                                    // the largest page maximum is the largest key
     uint32_t tau = plo;
     if (plo != phi) {
@@ -273,14 +279,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     uint32_t flags = 0;
 #pragma unroll
     for (int i = 0; i < PV; ++i) flags |= (uint32_t)((t + kSelThreads * i < np) & (pv[i] >= tau)) << i;
-    if (t == 0) { sh.list_n = 0; sh.out[3] = 0; }
-    __syncthreads();
     {
       // compact the candidate page ids: one LDS reservation per wave
       const int cnt = __builtin_popcount(flags);
       const int incl = wave_inclusive_scan(cnt);
       int base = 0;
-      if (lane == 63 && incl) base = atomicAdd(&sh.out[3], incl);
+      if (lane == 63 && incl) base = atomicAdd(&sh.ncp, incl);
       int slot = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
 #pragma unroll
       for (int i = 0; i < PV; ++i)
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         }
     }
     __syncthreads();
-    const int ncp = sh.out[3];
+    const int ncp = sh.ncp;
     if (ncp <= kListCap) {
       const int wave = t >> 6, sub = lane >> 2, q4 = lane & 3;
       constexpr int kPagesPerStep = 16 * kSelWaves;
@@ -349,12 +353,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       }
     }
     __syncthreads();
-    ncand = (uint32_t)sh.list_n;
+    ncand = (uint32_t)sh.list_n;   // list_n is written again only after later barriers
     if (ncp <= kListCap && ncand <= (uint32_t)kListCap) {
       have_list = true;
       lo = tau;
     }
-    __syncthreads();
   }
 
   // Sample path and full fallback over every key.
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       for (int r = 0; r < R; ++r)
         for (int e = 0; e < nv[r]; ++e) { const uint32_t u = key(r, e); mn = min(mn, u); mx = max(mx, u); }
     }
-    block_minmax(mn, mx, sh, &lo, &hi);
+    block_minmax(mn, mx, sh, 1, &lo, &hi);
 
     if (lo != hi) {
       // sample: keys 0, 16, 32, 48 of every chunk.
