@@ -81,26 +81,4 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) { return ~wave_max(~x); }
 
-// Exclusive scan over the threads of a block of NT threads (NT a multiple of 64, <= 1024).
-// `tmp` holds at least NT/64 + 1 ints of LDS. Returns the exclusive prefix and writes
-// the block total to *total. Must be reached by every thread of the block.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
-  constexpr int NW = NT / 64;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int inc = wave_inclusive_scan(x);
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < NW; ++w) { int v = tmp[w]; tmp[w] = run; run += v; }
-    tmp[NW] = run;
-  }
-  __syncthreads();
-  int r = tmp[wave] + inc - x;
-  *total = tmp[NW];
-  __syncthreads();
-  return r;
-}
-
 }  // namespace qsa

@@ -49,6 +49,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kChunk = 64;                       // blocks per chunk (one bitmap word)
 constexpr int kSelBins = 2048;
 constexpr int kListCap = 4096;
+constexpr int kWavePages = 256;                  // candidate pages one wave can hold
 constexpr int kMaxSelBlocks = 262144;            // contexts up to 1,048,576 tokens
 
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
@@ -57,15 +58,44 @@ struct SelShared {
   uint32_t hbuf[2][kSelBins + 64];  // double-buffered histogram (+ one dummy bin per lane)
   uint32_t list_u[kListCap];
   int list_j[kListCap];
-  int cpages[kListCap];             // candidate page ids of the page-maximum path
-  int scan[kSelWaves + 1];
+  int wpages[kSelWaves][kWavePages];     // per-wave candidate page ids of the page-maximum path
+  alignas(16) int scan[2 * kSelWaves];   // block_exclusive_scan halves
   uint32_t red[2][kSelWaves];
   uint32_t mm[2][2];                // (min, max) slots of the two block_minmax calls
   int fb[2][4];                     // find_bucket results, one slot per histogram buffer
-  int ncp;                          // candidate pages of the page-maximum path
   int list_n;
 };
 
+
+// Exclusive scan over the threads of a block of NT threads (NT a multiple of 256, <= 1024)
+// with one barrier. `tmp` holds 2 * NT/64 ints of 16-byte aligned LDS and `buf` (0 or 1,
+// the same in every thread, flipped by the call) picks the half this call uses: a call's
+// wave totals are read after its barrier, and the half is written again only by the call
+// after next, which comes after the next call's barrier. Returns the exclusive prefix and
+// writes the block total to *total. Must be reached by every thread of the block.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int& buf, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(x);
+  int* h = tmp + buf * NW;
+  if (lane == 63) h[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w4 = 0; w4 < NW / 4; ++w4) {
+    const i32x4 v = reinterpret_cast<const i32x4*>(h)[w4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int w = 4 * w4 + e;
+      before += w < wave ? v[e] : 0;
+      all += v[e];
+    }
+  }
+  buf ^= 1;
+  *total = all;
+  return before + inc - x;
+}
 
 // Block-wide min and max into slot sh.mm[slot], which thread 0 set to (~0, 0) before an
 // earlier barrier (every thread must call; one barrier; the slot is not reused).
@@ -242,7 +272,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   if (t == 0) {
     sh.mm[0][0] = sh.mm[1][0] = 0xFFFFFFFFu;
     sh.mm[0][1] = sh.mm[1][1] = 0u;
-    sh.ncp = 0;
     sh.list_n = 0;
   }
   __syncthreads();
@@ -261,6 +290,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     block_minmax(mn, mx, sh, 0, &plo, &phi);
     hi = phi;                                    // the largest page maximum is the largest key
     uint32_t tau = plo;
+    int ncp = np;                                // pages whose maximum reaches tau
     if (plo != phi) {
       const int shift = shift_for(plo, phi);
 #pragma unroll
@@ -268,48 +298,49 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         atomicAdd(&sh.hbuf[hsel][t + kSelThreads * i < np ? (pv[i] - plo) >> shift : dummy], 1u);
       __syncthreads();
       int beta;
-      uint32_t above;
-      find_bucket(sh, hsel, (uint32_t)k, &beta, &above);
+      uint32_t above, count;
+      find_bucket(sh, hsel, (uint32_t)k, &beta, &above, &count);
       tau = plo + ((uint32_t)beta << shift);
+      ncp = (int)(above + count);
     }
-    // B. candidate pages (pm >= tau), then their candidate blocks: each page is read by 4
-    // lanes with one 16-byte load each, a wave takes 16 pages per step, and all steps' loads
-    // (up to 1024 pages) are issued before any key is appended; a wave reserves list slots
-    // with one LDS atomic per key position. Order in the list does not matter.
-    uint32_t flags = 0;
-#pragma unroll
-    for (int i = 0; i < PV; ++i) flags |= (uint32_t)((t + kSelThreads * i < np) & (pv[i] >= tau)) << i;
-    {
-      // compact the candidate page ids: one LDS reservation per wave
-      const int cnt = __builtin_popcount(flags);
-      const int incl = wave_inclusive_scan(cnt);
-      int base = 0;
-      if (lane == 63 && incl) base = atomicAdd(&sh.ncp, incl);
-      int slot = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
-#pragma unroll
-      for (int i = 0; i < PV; ++i)
-        if ((flags >> i) & 1u) {
-          if (slot < kListCap) sh.cpages[slot] = t + kSelThreads * i;
-          ++slot;
-        }
-    }
-    __syncthreads();
-    const int ncp = sh.ncp;
+    // B. candidate blocks. Each wave compacts the pages of its lanes that reach tau into its
+    // own LDS list (ballots, no block barrier; more than kWavePages in one wave counts as an
+    // overflow), then reads them 4 lanes per page with one 16-byte load each, 16 pages per
+    // step and every step's load in flight before any key is used, and appends the keys
+    // >= tau to the block's LDS list with one reservation per wave and step. Order in the
+    // list does not matter. Each such page adds at least one key, so more than kListCap
+    // pages go straight to the fallback.
     if (ncp <= kListCap) {
       const int wave = t >> 6, sub = lane >> 2, q4 = lane & 3;
-      constexpr int kPagesPerStep = 16 * kSelWaves;
+      int* wp = sh.wpages[wave];
+      int nwp = 0;                               // wave-uniform
+#pragma unroll
+      for (int i = 0; i < PV; ++i) {
+        const bool f = (t + kSelThreads * i < np) & (pv[i] >= tau);
+        const uint64_t m = __ballot(f);
+        const int pos = nwp + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (f && pos < kWavePages) wp[pos] = t + kSelThreads * i;
+        nwp += __builtin_popcountll(m);
+      }
+      if (nwp > kWavePages) {
+        if (lane == 0) atomicAdd(&sh.list_n, kListCap + 1);   // overflow: the list is not used
+        nwp = 0;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       constexpr int kBatch = 4;
-      const int nsteps = (ncp + kPagesPerStep - 1) / kPagesPerStep;
-      for (int st0 = 0; st0 < nsteps; st0 += kBatch) {
+      for (int st0 = 0; st0 < nwp; st0 += 16 * kBatch) {
         int j0[kBatch];
         i32x4 v[kBatch];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-          const int ci = (st0 + q) * kPagesPerStep + wave * 16 + sub;
+          const int ci = st0 + 16 * q + sub;
           j0[q] = -1;
           v[q] = i32x4{0, 0, 0, 0};
-          if (st0 + q < nsteps && ci < ncp) {
-            const int j = kBlocksPerPage * sh.cpages[ci] + 4 * q4;
+          if (ci < nwp) {
+            const int j = kBlocksPerPage * wp[ci] + 4 * q4;
             if (j < n) { j0[q] = j; v[q] = *reinterpret_cast<const i32x4*>(s + j); }
           }
         }
@@ -491,7 +522,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   }
   __syncthreads();
 
-  // The first `need` ties in block order join the kept set; then ascending ids.
+  // The first `need` ties in block order join the kept set; then ascending ids. Each
+  // thread reads and updates only its own words here, so no barrier is needed between.
+  int sbuf = 0;   // block_exclusive_scan half
   if (!all_of_bucket) {
     int run = 0;
 #pragma unroll
@@ -499,7 +532,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       const int c = t + kSelThreads * r;
       const uint64_t m0 = tie_w[c];
       int tot;
-      int before = run + block_exclusive_scan<kSelThreads>(__builtin_popcountll(m0), sh.scan, &tot);
+      int before = run + block_exclusive_scan<kSelThreads>(__builtin_popcountll(m0), sh.scan, sbuf, &tot);
       uint64_t m = m0, take = 0;
       while (m && before < (int)need) {
         take |= m & (~m + 1);
@@ -516,7 +549,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     const int c = t + kSelThreads * r;
     uint64_t m = kept_w[c];
     int tot;
-    int pos = run + block_exclusive_scan<kSelThreads>(__builtin_popcountll(m), sh.scan, &tot);
+    int pos = run + block_exclusive_scan<kSelThreads>(__builtin_popcountll(m), sh.scan, sbuf, &tot);
     while (m) {
       const int j = kChunk * c + __builtin_ctzll(m);
       m &= m - 1;
