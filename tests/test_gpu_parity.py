@@ -404,6 +404,60 @@ def test_topk_select_crafted_scores(max_blocks, k, with_page_max):
         assert np.all(sel[b, len(ref):] == -1)
 
 
+def _page_maxima(rows, lens, max_blocks):
+    """Per-page maxima over the valid blocks, as the scan writes them."""
+    pmax = np.full((len(rows), max_blocks // 16), -2**31, np.int64)
+    for b, (row, L) in enumerate(zip(rows, lens)):
+        n = (L + 3) // 4
+        for p in range((n + 15) // 16):
+            pmax[b, p] = row[16 * p:min(16 * p + 16, n)].max()
+    return pmax
+
+
+@pytest.mark.parametrize("max_blocks", [65536, 131072, 262144])
+def test_topk_select_page_path_limits(max_blocks):
+    """The page-maximum path at its limits, against the oracle: (a) the candidate pages held
+    by one wave's lanes (pages p with p mod 1024 < 64: with more than 256 of them that wave's
+    page list overflows and the selection must fall back), (b) about k candidate pages whose
+    every block is a candidate (more than 4096 keys: the candidate list overflows), (c) the
+    k-th page maximum tied across 2000 pages (ties taken in block order)."""
+    rng = np.random.default_rng(max_blocks)
+    n = max_blocks
+    npg = n // 16
+    pages = np.arange(npg)
+    rows = []
+    # (a) high scores only in the pages owned by wave 0 (page p -> thread p mod 1024)
+    row = rng.integers(-1000, 1000, n).astype(np.int64)
+    hot = pages[(pages % 1024) < 64]
+    for p in hot:
+        row[16 * p:16 * p + 16] = rng.integers(10**6, 2 * 10**6, 16)
+    rows.append(row)
+    # (b) 600 pages, spread at random, whose 16 blocks all sit within 2 of the page's maximum
+    row = rng.integers(-1000, 1000, n).astype(np.int64)
+    for p in rng.choice(npg, 600, replace=False):
+        row[16 * p:16 * p + 16] = int(rng.integers(10**6, 2 * 10**6)) - rng.integers(0, 3, 16)
+    rows.append(row)
+    # (c) page maxima tied at one value on 2000 pages, lower elsewhere
+    row = rng.integers(-1000, 1000, n).astype(np.int64)
+    for p in rng.choice(npg, min(2000, npg), replace=False):
+        row[16 * p + rng.integers(0, 16)] = 777777
+    rows.append(row)
+    lens = [4 * n, 4 * n - 1, 4 * n - 6]
+    say(f"[topk limits] max_blocks={max_blocks} hot pages={len(hot)}")
+    scores = torch.tensor(np.stack(rows).astype(np.int32), device="cuda")
+    cl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    pm = torch.tensor(_page_maxima(rows, lens, max_blocks).astype(np.int32), device="cuda")
+    for page_max in (pm, None):
+        sel, cnt = qsa.topk_select(scores, cl, 512, page_max=page_max)
+        torch.cuda.synchronize()
+        sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+        for b, (row, L) in enumerate(zip(rows, lens)):
+            nb = (L + 3) // 4
+            ref = oracle.select_blocks(row[:nb], 512)
+            assert cnt[b] == len(ref), (b, page_max is None)
+            assert np.array_equal(sel[b, :len(ref)], ref), (b, page_max is None)
+
+
 @pytest.mark.parametrize("name,lens", [("pm_u127", (70000, 2049, 33000, 65537)),
                                        ("pm_u2", (70000, 40000, 8192, 8193))])
 def test_page_max_and_both_selection_paths(name, lens):
