@@ -17,10 +17,10 @@
 // partial of its share; the slice partial is the log-sum-exp merge of its C shares
 // (slice_merge_kernel), the same formula that merges the slices.
 //
-// Inside a workgroup: every thread reads two kept slots, counts (by wave ballots) the slots
-// before and inside the slice and, for a slot inside, loads its physical page at once, so
-// the only dependent global loads before the K/V rows are the ids and the page-table
-// entries. The share's ids and pages go to LDS; tiles are dealt round-robin to the waves;
+// Inside a workgroup: every thread reads two kept slots (loaded together with sel_count and
+// the length), counts (by wave ballots) the slots before and inside the slice and, for a
+// slot inside, loads its physical page at once, so the only dependent global loads before
+// the K/V rows are the ids and the page-table entries. The share's ids and pages go to LDS; tiles are dealt round-robin to the waves;
 // a wave issues the loads of up to kTilesInFlight tiles before it computes on the first,
 // and keeps an online softmax over its tiles. The 4 wave partials are merged in one LDS
 // round, each thread finishing 8 output dims of one query head.
@@ -168,9 +168,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
   const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
   const int i16 = lane & 15, q4 = lane >> 4;
   const int group = Hq / Hkv;
+  const int32_t* sb = sel + (size_t)b * k;
+  // Kept slots t and t + 256 are loaded first, whether or not the slot is below K (every
+  // slot < k is in bounds), so the loads wait neither for sel_count nor for the length.
+  int jraw[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int slot = t + kAttnThreads * r;
+    jraw[r] = slot < k ? sb[slot] : 0;
+  }
   const int L = draft_length(lens, b, T);
   const int K = sel_count[b];
-  const int32_t* sb = sel + (size_t)b * k;
   const int32_t* ptab = page_table + (size_t)(b / T) * max_pages;
   const size_t share = ((size_t)b * P + p) * C + c;
 
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
   for (int r = 0; r < 2; ++r) {
     const int slot = t + kAttnThreads * r;
     const bool valid = slot < K;
-    const int j = valid ? sb[slot] : 0;
+    const int j = valid ? jraw[r] : 0;
     const int pg = j / kBlocksPerPage;
     inr[r] = valid && pg >= pg0 && pg < pg1;
     jr[r] = j;
