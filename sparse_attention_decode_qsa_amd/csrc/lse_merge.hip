@@ -25,14 +25,21 @@ __global__ __launch_bounds__(kHeadDim) void lse_merge_kernel(const float* __rest
                                                              float* __restrict__ out_lse) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const float* lse = pl + (size_t)b * P * Hq + h;
+  // The first 64 slice lse values come in by one vector load per wave (lane p holds slice p)
+  // and are read out as wave-uniform values; slices past 64 are read directly.
+  const int lane = threadIdx.x & 63;
+  const int lse_lane = __float_as_int(lane < P ? lse[(size_t)lane * Hq] : -INFINITY);
+  auto lse_of = [&](int p) {
+    return p < 64 ? __int_as_float(__builtin_amdgcn_readlane(lse_lane, p)) : lse[(size_t)p * Hq];
+  };
   float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, lse[(size_t)p * Hq]);
+  for (int p = 0; p < P; ++p) M = fmaxf(M, lse_of(p));
   float wsum = 0.f, acc = 0.f;
   if (M != -INFINITY) {
 #pragma unroll 8
     for (int p = 0; p < P; ++p) {
       const float v = po[(((size_t)b * P + p) * Hq + h) * kHeadDim + d];   // loaded in batches
-      const float l = lse[(size_t)p * Hq];
+      const float l = lse_of(p);
       if (l == -INFINITY) continue;
       const float w = __expf(l - M);
       wsum += w;
@@ -50,8 +57,8 @@ __global__ __launch_bounds__(kHeadDim) void lse_merge_kernel(const float* __rest
 // then the slices are merged with the operations of lse_merge_kernel, in the same order.
 constexpr int kFastShares = 32;
 
-// P * C <= kFastShares: each thread loads every share lse (same address in all threads)
-// and every share value of its dim at entry, and combines them in registers.
+// P * C <= kFastShares: each thread loads every share value of its dim at entry (the share
+// lse values arrive by one vector load per wave), and combines them in registers.
 template <int C>
 __device__ __forceinline__ void slice_merge_regs(const float* __restrict__ so, const float* __restrict__ sl,
                                                  int P, int Hq, int h, int b, int d, float* __restrict__ part_out,
@@ -62,12 +69,17 @@ __device__ __forceinline__ void slice_merge_regs(const float* __restrict__ so, c
   const float* col = so + ((size_t)b * n * Hq + h) * kHeadDim + d;   // share i at col[i * Hq * 128]
   const float* lcol = sl + (size_t)b * n * Hq + h;                   // share i at lcol[i * Hq]
   const size_t stride = (size_t)Hq * kHeadDim;
+  // One vector load brings the n <= 32 share lse values into lanes 0..n-1 (then read out as
+  // wave-uniform values); the share values are loaded without branches (a share past n reads
+  // share 0 and is never used: its lse is -inf).
+  const int lane = threadIdx.x & 63;
+  const float lse_lane = lane < n ? lcol[(size_t)lane * Hq] : -INFINITY;
   float lv[kFastShares], v[kFastShares];
 #pragma unroll
-  for (int i = 0; i < kFastShares; ++i) {
-    lv[i] = i < n ? lcol[(size_t)i * Hq] : -INFINITY;
-    v[i] = i < n ? col[i * stride] : 0.f;
-  }
+  for (int i = 0; i < kFastShares; ++i) v[i] = col[(i < n ? i : 0) * stride];
+#pragma unroll
+  for (int i = 0; i < kFastShares; ++i)
+    lv[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse_lane), i));
   float mp[PM], lp[PM];
 #pragma unroll
   for (int p = 0; p < PM; ++p) {
@@ -133,12 +145,21 @@ __global__ __launch_bounds__(128) void slice_merge_v4_kernel(const float* __rest
   const float* col = so + ((size_t)b * n * Hq + h) * kHeadDim + d0;
   const float* lcol = sl + (size_t)b * n * Hq + h;
   const size_t stride = (size_t)Hq * kHeadDim;
+  // The n <= NV share lse values: a wave holds two heads (lanes 0-31 and 32-63), and lane
+  // 32*half + i loads share i of its half's head, so one vector load brings both heads' values;
+  // each half reads its own lanes (two uniform reads, one select). The share values are loaded
+  // without branches (a share past n reads share 0 and is never used).
+  const int sub = threadIdx.x & 31;
+  const bool upper = (threadIdx.x & 32) != 0;
+  const int lse_lane = __float_as_int(sub < n ? lcol[(size_t)sub * Hq] : -INFINITY);
   float lv[NV];
   f32x4 v[NV];
 #pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const f32x4*>(col + (i < n ? i : 0) * stride);
+#pragma unroll
   for (int i = 0; i < NV; ++i) {
-    lv[i] = i < n ? lcol[(size_t)i * Hq] : -INFINITY;
-    v[i] = i < n ? *reinterpret_cast<const f32x4*>(col + i * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int lo = __builtin_amdgcn_readlane(lse_lane, i), hi = __builtin_amdgcn_readlane(lse_lane, 32 + i);
+    lv[i] = __int_as_float(upper ? hi : lo);
   }
   float mp[PM], lp[PM];
 #pragma unroll

@@ -404,6 +404,32 @@ def test_topk_select_crafted_scores(max_blocks, k, with_page_max):
         assert np.all(sel[b, len(ref):] == -1)
 
 
+@pytest.mark.parametrize("P", [1, 3, 64, 100])
+def test_lse_merge_alone(P):
+    """qsa_lse_merge on crafted partials against the oracle's merge: lse spread over a wide
+    range, about a quarter of the partials empty (-inf), and heads whose every partial is
+    empty; P = 100 passes the 64 slices whose lse arrive by one vector load per wave."""
+    rng = np.random.default_rng(P)
+    B, Hq = 3, 32
+    po = rng.normal(0, 1, (B, P, Hq, 128))
+    pl = rng.normal(5, 20, (B, P, Hq))
+    pl[rng.random((B, P, Hq)) < 0.25] = -np.inf
+    pl[1, :, 7] = -np.inf                               # a head with no partial at all
+    po32, pl32 = po.astype(np.float32), pl.astype(np.float32)
+    say(f"[lse_merge] B={B} P={P} Hq={Hq}")
+    out, lse = qsa.lse_merge(torch.tensor(po32, device="cuda"), torch.tensor(pl32, device="cuda"))
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        ro, rl = oracle.lse_merge(po32[b].astype(np.float64), pl32[b].astype(np.float64))
+        ok, ma, mr = tolerance_report(out[b], ro, ATOL, RTOL)
+        assert ok, (b, ma, mr)
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(lse[b]), fin)
+        assert np.allclose(lse[b][fin], rl[fin], atol=ATOL, rtol=RTOL)
+        assert np.all(out[b][~fin] == 0)
+
+
 def _page_maxima(rows, lens, max_blocks):
     """Per-page maxima over the valid blocks, as the scan writes them."""
     pmax = np.full((len(rows), max_blocks // 16), -2**31, np.int64)
