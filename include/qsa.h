@@ -33,7 +33,7 @@
  *              lengths       context_lens [B] int32, 0 <= L_b <= max_pages_per_seq*page_size
  *              Token t of request b lives in page page_table[b][t / page_size], row
  *              t % page_size, in all three caches (one page table for the indexer keys
- *              and K/V: the article's "one cache group" bullet).
+ *              and K/V, as the article's bullet on the single cache group has it).
  *   Compiled   page_size 64, n_idx_heads 4, idx_dim 64, head_dim 128, Hq/Hkv <= 16,
  *              k <= 512. Other values return QSA_ERR_UNSUPPORTED.
  *   Errors     arguments visible on the host are checked before anything is enqueued;
