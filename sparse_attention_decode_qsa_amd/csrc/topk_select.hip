@@ -344,10 +344,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
             if (j < n) { j0[q] = j; v[q] = *reinterpret_cast<const i32x4*>(s + j); }
           }
         }
-        // Lane candidates (0..4 per load) -> wave prefix from the 3 bits of each count,
-        // then one list reservation per wave for the whole batch.
+        // Lane candidates (0..16 per batch) -> one wave prefix sum, then one list
+        // reservation per wave for the whole batch; each lane writes its run of slots.
         uint32_t cm[kBatch];
-        int pre[kBatch], tot[kBatch], all = 0;
+        int c = 0;
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
           uint32_t m4 = 0;
@@ -355,32 +355,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
           for (int e = 0; e < 4; ++e)
             m4 |= (uint32_t)(j0[q] >= 0 && j0[q] + e < n && score_key(v[q][e]) >= tau) << e;
           cm[q] = m4;
-          const int cnt = __builtin_popcount(m4);
-          int pf = 0, tt = 0;
-#pragma unroll
-          for (int bit = 0; bit < 3; ++bit) {
-            const uint64_t bm = __ballot((cnt >> bit) & 1);
-            pf += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << bit;
-            tt += __builtin_popcountll(bm) << bit;
-          }
-          pre[q] = pf;
-          tot[q] = tt;
-          all += tt;
+          c += __builtin_popcount(m4);
         }
+        const int incl = wave_inclusive_scan(c);
         int base = 0;
-        if (lane == 0 && all) base = atomicAdd(&sh.list_n, all);
-        base = __shfl(base, 0, 64);
+        if (lane == 63 && incl) base = atomicAdd(&sh.list_n, incl);
+        int slot = __builtin_amdgcn_readlane(base, 63) + incl - c;
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          int slot = base + pre[q];
+        for (int q = 0; q < kBatch; ++q)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if ((cm[q] >> e) & 1u) {
               if (slot < kListCap) { sh.list_u[slot] = score_key(v[q][e]); sh.list_j[slot] = j0[q] + e; }
               ++slot;
             }
-          base += tot[q];
-        }
       }
     }
     __syncthreads();
