@@ -16,9 +16,11 @@
 //      maxima are histogrammed over their [min, max] in 2048 bins and tau = the lower edge of
 //      the bin holding the k-th largest. At least k pages reach tau, each with a block >= tau,
 //      so the k-th key is >= tau and only pages reaching tau can hold kept blocks. Those pages
-//      (about k) are compacted, their scores read by 4 lanes per page with every load of a
-//      batch in flight, and the keys >= tau go to an LDS list (key, block) of at most 4096.
-//   B. otherwise, or if that list would overflow:
+//      (about k; the bucket search counts them) are compacted by each wave for its own lanes
+//      (ballots, no block barrier), their scores read by 4 lanes per page with every load of
+//      a batch in flight, and the keys >= tau go to an LDS list (key, block) of at most 4096,
+//      each wave reserving its slots with one atomic after a wave prefix sum.
+//   B. otherwise, or if that list (or one wave's page list) would overflow:
 //      1. load    the keys (in registers when R = 1, else re-read from memory) and the
 //                 range [lo, hi] = [min u, max u] over the request.
 //      2. sample  keys 0, 16, 32, 48 of every chunk are histogrammed over [lo, hi]; the
@@ -36,7 +38,8 @@
 //   5. output  kept and tie masks per chunk; block prefix sums of their popcounts give
 //              the tie ranks and the ascending output positions.
 // The bucket search runs on one wave (DPP prefix sums) while the other waves clear the
-// second histogram buffer. Histogram loops over all keys are branch-free: a key that is
+// second histogram buffer; it and the block prefix sums cost one barrier each, reading
+// their results from double-buffered LDS slots. Histogram loops over all keys are branch-free: a key that is
 // not counted goes to the lane's own dummy bin. Requests with at most k blocks keep all of
 // them. With T draft tokens per request (multi-token decode) workgroup r is the virtual
 // request r = b*T + t, of length L_b - (T-1-t).
