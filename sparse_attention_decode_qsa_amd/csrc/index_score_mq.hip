@@ -18,20 +18,26 @@ namespace qsa {
 // r = 4*g4 + v holds token 16*g4 + 4*tt + v, so the lane's rows are block 4*g4 + tt, the
 // block score is the sum of its four values, and over the four tiles the lane holds the four
 // consecutive blocks 4*g4 .. 4*g4+3 (one 16-byte store per lane; a query's 16 blocks of the
-// page are 64 contiguous bytes). Grid (page groups, B), 16 waves per workgroup, one page per
-// wave: the wave keeps its page's 64 keys in registers in the A layout (16 loads of 16 bytes;
+// page are 64 contiguous bytes). Grid (page groups, B), 8 waves per workgroup (two
+// workgroups share a CU, so one's loads overlap the other's compute), one page per wave: the wave keeps its page's 64 keys in registers in the A layout (16 loads of 16 bytes;
 // lane i16 of tile tt: token 16*(i16/4) + 4*tt + i16%4, bytes 64*s + 16*g4 .. +15) and runs
 // every 16-query tile of the request against them, so the keys are read once. The queries go
-// through LDS in chunks of kQueryChunk, loaded once per workgroup. Causal masking (query m
-// sees tokens < L_b - T + 1 + m) is applied only on pages that reach into the new tokens.
-constexpr int kMqWaves = 16;
-constexpr int kQueryChunk = 128;   // queries staged in LDS at a time (32 KiB)
+// through LDS in chunks of kQueryChunk, loaded once per workgroup (the first chunk's loads
+// are issued before the keys', and the page id comes by a scalar load, so neither waits on
+// the other). Causal masking (query m sees tokens < L_b - T + 1 + m) is applied only on
+// pages that reach into the new tokens.
+constexpr int kMqWaves = 8;
+constexpr int kQueryChunk = 64;    // queries staged in LDS at a time (17 KiB with padding)
+constexpr int kQStride = kIdxTokenBytes / 16 + 1;   // 16-byte vectors per staged query
 
 __global__ __launch_bounds__(kMqWaves * 64) void index_score_mq_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ idx_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages,
     int max_blocks, int T, int32_t* __restrict__ scores, int32_t* __restrict__ page_max) {
-  __shared__ i32x4 s_q[kQueryChunk * kIdxTokenBytes / 16];
+  // Query m of the chunk at s_q[m * kQStride ..]: 16 vectors plus one of padding, so the 16
+  // queries a wave reads at once start in different banks.
+  __shared__ i32x4 s_q[kQueryChunk * kQStride];
+  static_assert((kQueryChunk * kIdxTokenBytes / 16) % (kMqWaves * 64) == 0, "whole vectors per thread");
   const int b = blockIdx.y;
   const int L = lens[b];
   const int npages = (L + kPageSize - 1) / kPageSize;
@@ -41,9 +47,26 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_mq_kernel(
   const int p = blockIdx.x * kMqWaves + wave;
   const bool active = p < npages;                 // idle waves still join the barriers
   const int valid = L - p * kPageSize;
+  // The page id is wave-uniform: a scalar load (its own counter, so the keys wait for it
+  // and not for the query loads), without a branch (an idle wave reads the last page's
+  // entry; npages >= 1 here).
+  const int page = page_table[(size_t)b * max_pages + __builtin_amdgcn_readfirstlane(min(p, npages - 1))];
+  // The first query chunk is loaded before the keys, so its latency overlaps theirs; it is
+  // written to LDS once it arrives (the key loads stay in flight).
+  constexpr int kQVecs = kQueryChunk * kIdxTokenBytes / 16;   // 16-byte vectors per chunk
+  constexpr int kQPer = kQVecs / (kMqWaves * 64);
+  const int8_t* qrow0 = q_idx + (size_t)b * T * kIdxTokenBytes;
+  const int nq0 = min(kQueryChunk, T);
+  i32x4 q0[kQPer];
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int x = threadIdx.x + kMqWaves * 64 * j;
+    const int lim = nq0 * kIdxTokenBytes / 16;      // loaded without a branch (clamped index)
+    const i32x4 v = reinterpret_cast<const i32x4*>(qrow0)[min(x, lim - 1)];
+    q0[j] = x < lim ? v : i32x4{0, 0, 0, 0};
+  }
   i32x4 key[4][4];
   if (active) {
-    const int page = page_table[(size_t)b * max_pages + p];
     const int8_t* base = idx_cache + (size_t)page * kIdxPageBytes + 16 * g4;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -57,20 +80,28 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_mq_kernel(
   }
   const int L0 = L - T + 1;                        // query 0 sees tokens < L0
   const bool causal = active && p * kPageSize + kPageSize > L0;
-  const int8_t* qrow0 = q_idx + (size_t)b * T * kIdxTokenBytes;
   for (int m0 = 0; m0 < T; m0 += kQueryChunk) {
     const int nq = min(kQueryChunk, T - m0);
-    __syncthreads();                               // the previous chunk is no longer read
-    for (int x = threadIdx.x; x < kQueryChunk * kIdxTokenBytes / 16; x += kMqWaves * 64)
-      s_q[x] = x < nq * kIdxTokenBytes / 16 ? reinterpret_cast<const i32x4*>(qrow0 + (size_t)m0 * kIdxTokenBytes)[x]
-                                            : i32x4{0, 0, 0, 0};
+    if (m0 == 0) {
+#pragma unroll
+      for (int j = 0; j < kQPer; ++j) {
+        const int x = threadIdx.x + kMqWaves * 64 * j;
+        s_q[(x >> 4) * kQStride + (x & 15)] = q0[j];
+      }
+    } else {
+      __syncthreads();                             // the previous chunk is no longer read
+      for (int x = threadIdx.x; x < kQVecs; x += kMqWaves * 64)
+        s_q[(x >> 4) * kQStride + (x & 15)] =
+            x < nq * kIdxTokenBytes / 16 ? reinterpret_cast<const i32x4*>(qrow0 + (size_t)m0 * kIdxTokenBytes)[x]
+                                         : i32x4{0, 0, 0, 0};
+    }
     __syncthreads();
     if (!active) continue;
     for (int qt = 0; qt < nq; qt += 16) {
       const int m = m0 + qt + i16;                 // this lane's query
       i32x4 qv[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qv[s] = s_q[(qt + i16) * (kIdxTokenBytes / 16) + 4 * s + g4];
+      for (int s = 0; s < 4; ++s) qv[s] = s_q[(qt + i16) * kQStride + 4 * s + g4];
       const int Lm = L0 + m;
       const int nblk = m < T && Lm > 0 ? (Lm + kTokensPerBlock - 1) / kTokensPerBlock : 0;
       int pmax = (int)0x80000000;
