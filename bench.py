@@ -103,9 +103,19 @@ def cpu_baseline(x, budget_s=12.0):
                           x.workload.slices, x.scale)
             t_total += time.perf_counter() - t0
             calls += 1
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": calls / t_total, "unit": "calls/s", "cores": 1, "kind": "oracle",
             "sample": f"{calls} full calls on the benchmarked batch (all {x.batch} requests, input set 0), "
-                      f"numpy float64/int64 on one host thread, {t_total:.1f} s"}
+                      f"numpy float64/int64 on one host thread of {model} ({os.cpu_count()} logical CPUs "
+                      f"visible), {t_total:.1f} s"}
 
 
 def main():
