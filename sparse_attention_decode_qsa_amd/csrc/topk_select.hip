@@ -18,15 +18,16 @@
 //      so the k-th key is >= tau and only pages reaching tau can hold kept blocks. Those pages
 //      (about k; the bucket search counts them) are compacted by each wave for its own lanes
 //      (ballots, no block barrier), their scores read by 4 lanes per page with every load of
-//      a batch in flight, and the keys >= tau go to an LDS list (key, block) of at most 4096,
-//      each wave reserving its slots with one atomic after a wave prefix sum.
+//      a batch in flight, and the keys >= tau go to an LDS list (key, block) of at most 8192
+//      entries (4096 past 256K tokens), each wave reserving its slots with one atomic after a
+//      wave prefix sum.
 //   B. otherwise, or if that list (or one wave's page list) would overflow:
 //      1. load    the keys (in registers when R = 1, else re-read from memory) and the
 //                 range [lo, hi] = [min u, max u] over the request.
 //      2. sample  keys 0, 16, 32, 48 of every chunk are histogrammed over [lo, hi]; the
 //                 lower edge of the bin holding their top 2*k*(samples/n) + 8 is a
 //                 threshold tau that about 2k keys reach.
-//      3. list    if between k and 4096 keys reach tau, those candidates go to the list;
+//      3. list    if between k and the list capacity keys reach tau, they go to the list;
 //                 otherwise the narrowing below runs over every key.
 // Then:
 //   4. narrow  repeat: histogram the keys inside [lo, hi] into 2048 bins of width
@@ -51,13 +52,17 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kChunk = 64;                       // blocks per chunk (one bitmap word)
 constexpr int kSelBins = 2048;
-constexpr int kListCap = 4096;
+// Candidate list capacity: 8192 when each thread owns one chunk (contexts up to 256K
+// tokens), else 4096 (the mask words of longer contexts take the LDS).
+constexpr int list_cap(int R) { return R == 1 ? 8192 : 4096; }
 constexpr int kWavePages = 256;                  // candidate pages one wave can hold
 constexpr int kMaxSelBlocks = 262144;            // contexts up to 1,048,576 tokens
 
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
 
+template <int R>
 struct SelShared {
+  static constexpr int kListCap = list_cap(R);
   uint32_t hbuf[2][kSelBins + 64];  // double-buffered histogram (+ one dummy bin per lane)
   uint32_t list_u[kListCap];
   int list_j[kListCap];
@@ -102,7 +107,8 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int& buf, i
 
 // Block-wide min and max into slot sh.mm[slot], which thread 0 set to (~0, 0) before an
 // earlier barrier (every thread must call; one barrier; the slot is not reused).
-__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, int slot, uint32_t* gmn,
+template <typename SH>
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SH& sh, int slot, uint32_t* gmn,
                                              uint32_t* gmx) {
   mn = wave_min(mn);
   mx = wave_max(mx);
@@ -113,7 +119,8 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared
 }
 
 // Block-wide sum (every thread must call; ends with a barrier).
-__device__ __forceinline__ uint32_t block_sum(uint32_t x, SelShared& sh) {
+template <typename SH>
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, SH& sh) {
   x = wave_sum(x);
   const int wave = threadIdx.x >> 6;
   if (lane_id() == 0) sh.red[0][wave] = x;
@@ -132,7 +139,8 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, SelShared& sh) {
 // buffers swap. The result goes through slot sh.fb[hsel]: the next call writes the other
 // slot, and the call after it comes after that call's barrier, when every thread has read
 // this one. Every thread must call it; it costs one barrier.
-__device__ __forceinline__ void find_bucket(SelShared& sh, int& hsel, uint32_t need, int* beta,
+template <typename SH>
+__device__ __forceinline__ void find_bucket(SH& sh, int& hsel, uint32_t need, int* beta,
                                             uint32_t* above, uint32_t* count = nullptr) {
   constexpr int per = kSelBins / 64;
   const int t = threadIdx.x, lane = lane_id();
@@ -176,7 +184,8 @@ __device__ __forceinline__ int shift_for(uint32_t lo, uint32_t hi) {
 
 // One narrowing step on a complete histogram of the keys in [lo, hi]. Returns true when
 // the bucket's keys are exactly the ones still needed.
-__device__ __forceinline__ bool narrow_step(SelShared& sh, int& hsel, int shift, uint32_t* lo, uint32_t* hi,
+template <typename SH>
+__device__ __forceinline__ bool narrow_step(SH& sh, int& hsel, int shift, uint32_t* lo, uint32_t* hi,
                                             uint32_t* need) {
   int beta;
   uint32_t above;
@@ -193,7 +202,7 @@ __device__ __forceinline__ bool narrow_step(SelShared& sh, int& hsel, int shift,
 // Narrow [lo, hi] over the LDS candidate list (all candidates are >= lo), then write the
 // kept and tie masks of the candidates into the per-chunk words (zero on entry).
 template <int R>
-__device__ __forceinline__ void narrow_list_and_mark(SelShared& sh, int& hsel, uint32_t ncand, uint32_t lo, uint32_t hi,
+__device__ __forceinline__ void narrow_list_and_mark(SelShared<R>& sh, int& hsel, uint32_t ncand, uint32_t lo, uint32_t hi,
                                                      uint32_t* need_io, bool* all_io, uint32_t* lo_out,
                                                      uint64_t* kept_w, uint64_t* tie_w) {
   const int t = threadIdx.x;
@@ -229,7 +238,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
                                                                   int32_t* __restrict__ sel,
                                                                   int32_t* __restrict__ sel_count, int T) {
   extern __shared__ uint64_t s_words[];  // [2][1024*R]: kept and tie masks per chunk
-  __shared__ SelShared sh;
+  __shared__ SelShared<R> sh;
+  constexpr int kListCap = SelShared<R>::kListCap;
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = lane_id();
   const int n = (draft_length(lens, b, T) + kTokensPerBlock - 1) / kTokensPerBlock;
