@@ -56,6 +56,7 @@ constexpr int kSelBins = 2048;
 // tokens), else 4096 (the mask words of longer contexts take the LDS).
 constexpr int list_cap(int R) { return R == 1 ? 8192 : 4096; }
 constexpr int kWavePages = 256;                  // candidate pages one wave can hold
+constexpr int kStridedOut = 8192;                // requests up to this many blocks write ids per block
 constexpr int kMaxSelBlocks = 262144;            // contexts up to 1,048,576 tokens
 
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
@@ -68,6 +69,7 @@ struct SelShared {
   int list_j[kListCap];
   int wpages[kSelWaves][kWavePages];     // per-wave candidate page ids of the page-maximum path
   alignas(16) int scan[2 * kSelWaves];   // block_exclusive_scan halves
+  int wpre[kSelThreads];                 // output position of each mask word (short requests)
   uint32_t red[2][kSelWaves];
   uint32_t mm[2][2];                // (min, max) slots of the two block_minmax calls
   int fb[2][4];                     // find_bucket results, one slot per histogram buffer
@@ -392,11 +394,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     }
   }
 
-  // Sample path and full fallback over every key.
+  // Sample path and full fallback over every key. With R = 1 the keys sit in registers,
+  // strided: thread t holds blocks t + 1024*e (e = 0..63), so the loads are coalesced, every
+  // thread has a share of a short request, and block t + 1024*e falls in mask word
+  // wave + 16*e at bit lane (one ballot per slot gives a whole word). With R > 1 thread t
+  // owns the chunks c = t + 1024*r of 64 consecutive blocks and reads its keys again.
   uint32_t reg[R == 1 ? kChunk : 1];
-  int nv[R];
+  int nv[R];   // valid slots e: R = 1: t + 1024*e < n; R > 1: 64*c + e < n
 #pragma unroll
-  for (int r = 0; r < R; ++r) nv[r] = min(kChunk, max(0, n - kChunk * (t + kSelThreads * r)));
+  for (int r = 0; r < R; ++r)
+    nv[r] = R == 1 ? (n > t ? min(kChunk, (n - t + kSelThreads - 1) / kSelThreads) : 0)
+                   : min(kChunk, max(0, n - kChunk * (t + kSelThreads * r)));
   auto key = [&](int r, int e) -> uint32_t {
     if constexpr (R == 1) {
       (void)r;
@@ -405,19 +413,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       return score_key(s[min(kChunk * (t + kSelThreads * r) + e, n - 1)]);
     }
   };
+  auto blk = [&](int r, int e) -> int {
+    return R == 1 ? t + kSelThreads * e : kChunk * (t + kSelThreads * r) + e;
+  };
   if (!have_list) {
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
     if constexpr (R == 1) {
-      // 16 loads of 16 bytes. A vector that starts at or past block n reads the row's last
-      // vector instead (in bounds since max_blocks % 4 == 0); its keys are masked by nv.
-      const int last_vec = (n - 1) & ~3;
+      // up to 64 coalesced loads of 4 bytes (a wave reads 256 contiguous bytes per slot);
+      // slots at or past n are not loaded.
 #pragma unroll
-      for (int m = 0; m < kChunk / 4; ++m) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(s + min(kChunk * t + 4 * m, last_vec));
-        reg[4 * m + 0] = score_key(v.x);
-        reg[4 * m + 1] = score_key(v.y);
-        reg[4 * m + 2] = score_key(v.z);
-        reg[4 * m + 3] = score_key(v.w);
+      for (int e = 0; e < kChunk; ++e) {
+        const int j = t + kSelThreads * e;
+        reg[e] = j < n ? score_key(s[j]) : 0u;
       }
 #pragma unroll
       for (int e = 0; e < kChunk; ++e) {
@@ -433,17 +440,29 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     block_minmax(mn, mx, sh, 1, &lo, &hi);
 
     if (lo != hi) {
-      // sample: keys 0, 16, 32, 48 of every chunk.
+      // sample one key in 16: with R = 1 the slots e with e % 16 == (t / 16) % 16 (four per
+      // thread, spread over the context), with R > 1 keys 0, 16, 32, 48 of every chunk.
       int shift = shift_for(lo, hi);
       uint32_t mine = 0;
+      if constexpr (R == 1) {
+        const int c16 = (t >> 4) & 15;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+        for (int e = 0; e < kChunk; ++e)
+          if ((e & 15) == c16) {
+            const bool ok = e < nv[0];
+            mine += ok;
+            atomicAdd(&sh.hbuf[hsel][ok ? (reg[e] - lo) >> shift : dummy], 1u);
+          }
+      } else {
 #pragma unroll
-        for (int e = 0; e < kChunk; e += 16) {
-          const bool ok = e < nv[r];
-          mine += ok;
-          atomicAdd(&sh.hbuf[hsel][ok ? (key(r, e) - lo) >> shift : dummy], 1u);
-        }
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < kChunk; e += 16) {
+            const bool ok = e < nv[r];
+            mine += ok;
+            atomicAdd(&sh.hbuf[hsel][ok ? (key(r, e) - lo) >> shift : dummy], 1u);
+          }
+      }
       const uint32_t nsamp = block_sum(mine, sh);
       const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
       uint32_t tau = lo;
@@ -466,17 +485,34 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       }
       ncand = block_sum(mine, sh);
       if (ncand >= (uint32_t)k && ncand <= (uint32_t)kListCap) {
+        // A thread's candidates take consecutive slots: one wave prefix sum of the counts and
+        // one reservation per wave. With R = 1 the keys come from registers (unrolled, so the
+        // register array is never indexed at run time); otherwise they are read again.
         if (t == 0) sh.list_n = 0;
         __syncthreads();
+        const int incl = wave_inclusive_scan((int)mine);
+        int base = 0;
+        if (lane == 63 && incl) base = atomicAdd(&sh.list_n, incl);
+        int slot = __builtin_amdgcn_readlane(base, 63) + incl - (int)mine;
+        if constexpr (R == 1) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          uint64_t m = cand[r];
-          while (m) {
-            const int j = kChunk * (t + kSelThreads * r) + __builtin_ctzll(m);
-            m &= m - 1;
-            const int slot = atomicAdd(&sh.list_n, 1);
-            sh.list_u[slot] = score_key(s[j]);
-            sh.list_j[slot] = j;
+          for (int e = 0; e < kChunk; ++e)
+            if ((cand[0] >> e) & 1u) {
+              sh.list_u[slot] = reg[e];
+              sh.list_j[slot] = blk(0, e);
+              ++slot;
+            }
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            uint64_t m = cand[r];
+            while (m) {
+              const int j = kChunk * (t + kSelThreads * r) + __builtin_ctzll(m);
+              m &= m - 1;
+              sh.list_u[slot] = score_key(s[j]);
+              sh.list_j[slot] = j;
+              ++slot;
+            }
           }
         }
         __syncthreads();
@@ -500,18 +536,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       }
     }
     if (!have_list) {  // masks from every key
+      if constexpr (R == 1) {
+        // slot e of wave w covers word w + 16e, bit = lane: one ballot each, one owner
+        const int wave = t >> 6;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        uint64_t mk = 0, mt = 0;
-#pragma unroll kU
         for (int e = 0; e < kChunk; ++e) {
-          const uint32_t u = key(r, e);
-          const bool ok = e < nv[r];
-          mk |= (uint64_t)(ok & (all_of_bucket ? u >= lo : u > hi)) << e;
-          mt |= (uint64_t)(ok & !all_of_bucket & (u == lo)) << e;
+          const uint32_t u = reg[e];
+          const bool ok = e < nv[0];
+          const uint64_t bk = __ballot(ok & (all_of_bucket ? u >= lo : u > hi));
+          const uint64_t bt = __ballot(ok & !all_of_bucket & (u == lo));
+          if (lane == 0) { kept_w[wave + kSelWaves * e] = bk; tie_w[wave + kSelWaves * e] = bt; }
         }
-        kept_w[t + kSelThreads * r] = mk;
-        tie_w[t + kSelThreads * r] = mt;
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          uint64_t mk = 0, mt = 0;
+#pragma unroll kU
+          for (int e = 0; e < kChunk; ++e) {
+            const uint32_t u = key(r, e);
+            const bool ok = e < nv[r];
+            mk |= (uint64_t)(ok & (all_of_bucket ? u >= lo : u > hi)) << e;
+            mt |= (uint64_t)(ok & !all_of_bucket & (u == lo)) << e;
+          }
+          kept_w[t + kSelThreads * r] = mk;
+          tie_w[t + kSelThreads * r] = mt;
+        }
       }
       masks_done = true;
     }
@@ -545,6 +594,28 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     }
   }
   int run = 0;
+  if (R == 1 && n <= kStridedOut) {
+    // Short request: the kept blocks sit in a few words, so instead of each word's owner
+    // writing its ids one by one, thread t writes the ids of its blocks t + 1024*e, at the
+    // word's prefix plus the kept bits below it in the word.
+    const uint64_t m = kept_w[t];
+    int tot;
+    sh.wpre[t] = block_exclusive_scan<kSelThreads>(__builtin_popcountll(m), sh.scan, sbuf, &tot);
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kStridedOut / kSelThreads; ++e) {
+      const int j = t + kSelThreads * e;
+      if (j < n) {
+        const uint64_t w = kept_w[j >> 6];
+        const uint64_t below = w & ((1ull << (j & 63)) - 1ull);
+        if ((w >> (j & 63)) & 1ull) {
+          const int pos = sh.wpre[j >> 6] + __builtin_popcountll(below);
+          if (pos < k) out[pos] = j;
+        }
+      }
+    }
+    run = tot;
+  } else {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int c = t + kSelThreads * r;
@@ -558,6 +629,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       ++pos;
     }
     run += tot;
+  }
   }
   for (int i = run + t; i < k; i += kSelThreads) out[i] = -1;
   if (t == 0) sel_count[b] = min(run, k);
