@@ -107,6 +107,19 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int& buf, i
   return before + inc - x;
 }
 
+// f(e) for the register slots e = 0 .. nvmax-1, unrolled in groups of 8 (so every index
+// is a constant and the register array stays in registers) with a wave-uniform exit after
+// the last group that holds a valid slot: a short request runs one or two groups, not 64.
+template <typename F>
+__device__ __forceinline__ void for_slots(int nvmax, F&& f) {
+#pragma unroll
+  for (int g = 0; g < kChunk / 8; ++g) {
+    if (8 * g >= nvmax) break;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f(8 * g + i);
+  }
+}
+
 // Block-wide min and max into slot sh.mm[slot], which thread 0 set to (~0, 0) before an
 // earlier barrier (every thread must call; one barrier; the slot is not reused).
 template <typename SH>
@@ -418,20 +431,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   };
   if (!have_list) {
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    // R = 1: the wave's largest slot count (lane 0 has it); every loop over the register
+    // slots stops there, so slots past it are never read.
+    const int nvmax = R == 1 ? __builtin_amdgcn_readfirstlane(nv[0]) : 0;
     if constexpr (R == 1) {
       // up to 64 coalesced loads of 4 bytes (a wave reads 256 contiguous bytes per slot);
       // slots at or past n are not loaded.
-#pragma unroll
-      for (int e = 0; e < kChunk; ++e) {
+      for_slots(nvmax, [&](int e) {
         const int j = t + kSelThreads * e;
         reg[e] = j < n ? score_key(s[j]) : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < kChunk; ++e) {
+      });
+      for_slots(nvmax, [&](int e) {
         const bool ok = e < nv[0];
         mn = min(mn, ok ? reg[e] : 0xFFFFFFFFu);
         mx = max(mx, ok ? reg[e] : 0u);
-      }
+      });
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -446,13 +460,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       uint32_t mine = 0;
       if constexpr (R == 1) {
         const int c16 = (t >> 4) & 15;
-#pragma unroll
-        for (int e = 0; e < kChunk; ++e)
+        for_slots(nvmax, [&](int e) {
           if ((e & 15) == c16) {
             const bool ok = e < nv[0];
             mine += ok;
             atomicAdd(&sh.hbuf[hsel][ok ? (reg[e] - lo) >> shift : dummy], 1u);
           }
+        });
       } else {
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -478,8 +492,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         uint64_t m = 0;
+        if constexpr (R == 1) {
+          for_slots(nvmax, [&](int e) { m |= (uint64_t)((e < nv[0]) & (reg[e] >= tau)) << e; });
+        } else {
 #pragma unroll kU
-        for (int e = 0; e < kChunk; ++e) m |= (uint64_t)((e < nv[r]) & (key(r, e) >= tau)) << e;
+          for (int e = 0; e < kChunk; ++e) m |= (uint64_t)((e < nv[r]) & (key(r, e) >= tau)) << e;
+        }
         cand[r] = m;
         mine += __builtin_popcountll(m);
       }
@@ -495,13 +513,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         if (lane == 63 && incl) base = atomicAdd(&sh.list_n, incl);
         int slot = __builtin_amdgcn_readlane(base, 63) + incl - (int)mine;
         if constexpr (R == 1) {
-#pragma unroll
-          for (int e = 0; e < kChunk; ++e)
+          for_slots(nvmax, [&](int e) {
             if ((cand[0] >> e) & 1u) {
               sh.list_u[slot] = reg[e];
               sh.list_j[slot] = blk(0, e);
               ++slot;
             }
+          });
         } else {
 #pragma unroll
           for (int r = 0; r < R; ++r) {
@@ -523,13 +541,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         while (lo != hi) {
           shift = shift_for(lo, hi);
           const uint32_t clo = lo, span_all = hi - lo;
+          if constexpr (R == 1) {
+            for_slots(nvmax, [&](int e) {
+              const uint32_t d = reg[e] - clo;
+              atomicAdd(&sh.hbuf[hsel][((e < nv[0]) & (d <= span_all)) ? d >> shift : dummy], 1u);
+            });
+          } else {
 #pragma unroll
-          for (int r = 0; r < R; ++r)
+            for (int r = 0; r < R; ++r)
 #pragma unroll kU
-            for (int e = 0; e < kChunk; ++e) {
-              const uint32_t d = key(r, e) - clo;
-              atomicAdd(&sh.hbuf[hsel][((e < nv[r]) & (d <= span_all)) ? d >> shift : dummy], 1u);
-            }
+              for (int e = 0; e < kChunk; ++e) {
+                const uint32_t d = key(r, e) - clo;
+                atomicAdd(&sh.hbuf[hsel][((e < nv[r]) & (d <= span_all)) ? d >> shift : dummy], 1u);
+              }
+          }
           __syncthreads();
           if (narrow_step(sh, hsel, shift, &lo, &hi, &need)) { all_of_bucket = true; break; }
         }
@@ -538,15 +563,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
     if (!have_list) {  // masks from every key
       if constexpr (R == 1) {
         // slot e of wave w covers word w + 16e, bit = lane: one ballot each, one owner
+        // (words of slots past the wave's last valid one stay as cleared at kernel start)
         const int wave = t >> 6;
-#pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
+        for_slots(nvmax, [&](int e) {
           const uint32_t u = reg[e];
           const bool ok = e < nv[0];
           const uint64_t bk = __ballot(ok & (all_of_bucket ? u >= lo : u > hi));
           const uint64_t bt = __ballot(ok & !all_of_bucket & (u == lo));
           if (lane == 0) { kept_w[wave + kSelWaves * e] = bk; tie_w[wave + kSelWaves * e] = bt; }
-        }
+        });
       } else {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
