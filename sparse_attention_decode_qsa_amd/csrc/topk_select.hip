@@ -70,8 +70,8 @@ struct SelShared {
   int wpages[kSelWaves][kWavePages];     // per-wave candidate page ids of the page-maximum path
   alignas(16) int scan[2 * kSelWaves];   // block_exclusive_scan halves
   int wpre[kSelThreads];                 // output position of each mask word (short requests)
-  uint32_t red[2][kSelWaves];
   uint32_t mm[2][2];                // (min, max) slots of the two block_minmax calls
+  uint32_t sums[2];                 // slots of the two block_sum calls
   int fb[2][4];                     // find_bucket results, one slot per histogram buffer
   int list_n;
 };
@@ -133,18 +133,14 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SH& sh, i
   *gmx = sh.mm[slot][1];
 }
 
-// Block-wide sum (every thread must call; ends with a barrier).
+// Block-wide sum into slot sh.sums[slot], which thread 0 set to 0 before an earlier barrier
+// (every thread must call; one barrier; the slot is not reused).
 template <typename SH>
-__device__ __forceinline__ uint32_t block_sum(uint32_t x, SH& sh) {
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, SH& sh, int slot) {
   x = wave_sum(x);
-  const int wave = threadIdx.x >> 6;
-  if (lane_id() == 0) sh.red[0][wave] = x;
+  if (lane_id() == 0 && x) atomicAdd(&sh.sums[slot], x);
   __syncthreads();
-  uint32_t s = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) s += sh.red[0][w];
-  __syncthreads();
-  return s;
+  return sh.sums[slot];
 }
 
 // Bin of the complete histogram holding the need-th largest key, the number of keys in
@@ -300,6 +296,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   if (t == 0) {
     sh.mm[0][0] = sh.mm[1][0] = 0xFFFFFFFFu;
     sh.mm[0][1] = sh.mm[1][1] = 0u;
+    sh.sums[0] = sh.sums[1] = 0u;
     sh.list_n = 0;
   }
   __syncthreads();
@@ -477,7 +474,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
             atomicAdd(&sh.hbuf[hsel][ok ? (key(r, e) - lo) >> shift : dummy], 1u);
           }
       }
-      const uint32_t nsamp = block_sum(mine, sh);
+      const uint32_t nsamp = block_sum(mine, sh, 0);
       const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
       uint32_t tau = lo;
       {
@@ -501,7 +498,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         cand[r] = m;
         mine += __builtin_popcountll(m);
       }
-      ncand = block_sum(mine, sh);
+      ncand = block_sum(mine, sh, 1);
       if (ncand >= (uint32_t)k && ncand <= (uint32_t)kListCap) {
         // A thread's candidates take consecutive slots: one wave prefix sum of the counts and
         // one reservation per wave. With R = 1 the keys come from registers (unrolled, so the
