@@ -153,7 +153,7 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
  *   partial_lse  out [B, P, Hq] float32, natural log
  *   workspace    qsa_attn_workspace_size(B, Hq, Hkv, k, P) bytes (see Workspace). Each
  *                slice's kept tokens are split into C shares attended in parallel, C the
- *                largest power of two <= min(8, ceil(512 / (B*Hkv*P))) (at least 1); the
+ *                largest power of two <= min(32, ceil(512 / (B*Hkv*P))) (at least 1); the
  *                workspace holds the share partials, B*P*C*Hq*head_dim + B*P*C*Hq floats
  *                (each part rounded up to 256 bytes), which are merged into the slice
  *                partials by log-sum-exp.

@@ -17,7 +17,7 @@
 
 namespace qsa {
 
-constexpr int kMaxShares = 8;   // shares per slice (at most the attention kernel's split)
+constexpr int kMaxShares = 32;  // shares per slice (at most the attention kernel's split)
 
 __global__ __launch_bounds__(kHeadDim) void lse_merge_kernel(const float* __restrict__ po,
                                                              const float* __restrict__ pl, int P,
@@ -220,8 +220,9 @@ __global__ __launch_bounds__(128) void slice_merge_v4_kernel(const float* __rest
 
 // Any P * C: the share lse values go through LDS, and slice p+1's share values are loaded
 // while slice p is combined.
+template <int C>
 __device__ __forceinline__ void slice_merge_lds(const float* __restrict__ so, const float* __restrict__ sl,
-                                                int P, int C, int Hq, int h, int b, int d,
+                                                int P, int Hq, int h, int b, int d,
                                                 float* __restrict__ part_out, float* __restrict__ part_lse,
                                                 float* __restrict__ out, float* __restrict__ out_lse) {
   const int n = P * C;
@@ -247,21 +248,20 @@ __device__ __forceinline__ void slice_merge_lds(const float* __restrict__ so, co
   __syncthreads();
   float M = -INFINITY;
   for (int p = 0; p < P; ++p) M = fmaxf(M, s_slice_lse[p]);
-  float cur[kMaxShares], nxt[kMaxShares];
+  float cur[C], nxt[C];
 #pragma unroll
-  for (int c = 0; c < kMaxShares; ++c) cur[c] = c < C ? col[c * stride] : 0.f;
+  for (int c = 0; c < C; ++c) cur[c] = col[c * stride];
   float wsum = 0.f, acc = 0.f;
   for (int p = 0; p < P; ++p) {
     if (p + 1 < P) {
 #pragma unroll
-      for (int c = 0; c < kMaxShares; ++c) nxt[c] = c < C ? col[((size_t)(p + 1) * C + c) * stride] : 0.f;
+      for (int c = 0; c < C; ++c) nxt[c] = col[((size_t)(p + 1) * C + c) * stride];
     }
     const float Mp = s_slice_max[p];
     float ws = 0.f, a = 0.f;
     if (Mp != -INFINITY) {
 #pragma unroll
-      for (int c = 0; c < kMaxShares; ++c) {
-        if (c >= C) break;
+      for (int c = 0; c < C; ++c) {
         const float l = s_share_lse[p * C + c];
         if (l == -INFINITY) continue;
         const float w = __expf(l - Mp);
@@ -279,7 +279,7 @@ __device__ __forceinline__ void slice_merge_lds(const float* __restrict__ so, co
       acc += w * o;
     }
 #pragma unroll
-    for (int c = 0; c < kMaxShares; ++c) cur[c] = nxt[c];
+    for (int c = 0; c < C; ++c) cur[c] = nxt[c];
   }
   if (out) {
     out[((size_t)b * Hq + h) * kHeadDim + d] = wsum > 0.f ? acc / wsum : 0.f;
@@ -287,7 +287,7 @@ __device__ __forceinline__ void slice_merge_lds(const float* __restrict__ so, co
   }
 }
 
-// C is 1, 2, 4 or 8.
+// C is 1, 2, 4, 8, 16 or 32.
 __global__ __launch_bounds__(kHeadDim) void slice_merge_kernel(const float* __restrict__ so,
                                                                const float* __restrict__ sl, int P, int C,
                                                                int Hq, float* __restrict__ part_out,
@@ -295,15 +295,19 @@ __global__ __launch_bounds__(kHeadDim) void slice_merge_kernel(const float* __re
                                                                float* __restrict__ out,
                                                                float* __restrict__ out_lse) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  if (P * C <= kFastShares) {
-    switch (C) {
-      case 1: slice_merge_regs<1>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
-      case 2: slice_merge_regs<2>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
-      case 4: slice_merge_regs<4>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
-      default: slice_merge_regs<8>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); return;
-    }
+#define QSA_MERGE_C(CC)                                                                         \
+  if (P * C <= kFastShares) slice_merge_regs<CC>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse); \
+  else slice_merge_lds<CC>(so, sl, P, Hq, h, b, d, part_out, part_lse, out, out_lse);                      \
+  return
+  switch (C) {
+    case 1: QSA_MERGE_C(1);
+    case 2: QSA_MERGE_C(2);
+    case 4: QSA_MERGE_C(4);
+    case 8: QSA_MERGE_C(8);
+    case 16: QSA_MERGE_C(16);
+    default: QSA_MERGE_C(32);
   }
-  slice_merge_lds(so, sl, P, C, Hq, h, b, d, part_out, part_lse, out, out_lse);
+#undef QSA_MERGE_C
 }
 
 hipError_t launch_lse_merge(const float* po, const float* pl, int B, int P, int Hq, float* out,
@@ -315,7 +319,7 @@ hipError_t launch_lse_merge(const float* po, const float* pl, int B, int P, int 
 
 hipError_t launch_slice_merge(const float* so, const float* sl, int B, int P, int C, int Hq, float* part_out,
                               float* part_lse, float* out, float* out_lse, hipStream_t stream) {
-  if ((C != 1 && C != 2 && C != 4 && C != 8) || P > kMaxSlices) return hipErrorInvalidValue;
+  if ((C != 1 && C != 2 && C != 4 && C != 8 && C != 16 && C != 32) || P > kMaxSlices) return hipErrorInvalidValue;
   if (P * C <= 8) {
     const dim3 grid((Hq + 3) / 4, B);
     switch (C) {

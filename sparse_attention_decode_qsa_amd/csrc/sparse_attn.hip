@@ -50,7 +50,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kTilesInFlight = 4;        // tiles whose loads a wave issues before computing
 constexpr int kAttnTargetGroups = 512;   // two workgroups per CU
-constexpr int kMaxSplit = 8;             // shares per slice
+constexpr int kMaxSplit = 32;            // shares per slice (tiny batches: one request, few heads)
 static_assert(kMaxK <= 2 * kAttnThreads, "two kept slots per thread");
 
 // Shares per slice for a launch of B requests, Hkv KV heads and P slices: the largest power

@@ -101,7 +101,8 @@ def test_attention_checks():
     assert _attn(L, ws=None, nbytes=0) == WS       # the share partials need a workspace
     assert _attn(L, nbytes=attn_ws(2, 32, 4, 4) - 1) == WS
     # share partials of C shares per slice
-    assert [attn_split(B, 4, 4) for B in (1, 2, 3, 5, 8, 16, 32, 128)] == [8, 8, 8, 4, 4, 2, 1, 1]
+    assert [attn_split(B, 4, 4) for B in (1, 2, 3, 5, 8, 16, 32, 128)] == [32, 16, 8, 4, 4, 2, 1, 1]
+    assert attn_split(1, 2, 1) == 32 and attn_split(4, 4, 4) == 8     # one small request; w4
     assert L.qsa_attn_workspace_size(2, 32, 4, 512, 4) == attn_ws(2, 32, 4, 4)
     assert L.qsa_attn_workspace_size(128, 32, 4, 512, 4) == attn_ws(128, 32, 4, 4)   # C = 1
     assert L.qsa_attn_workspace_size(0, 32, 4, 512, 4) == 0
@@ -112,8 +113,8 @@ def align256(n):
 
 
 def attn_split(B, Hkv, P):
-    """Shares per slice: largest power of two <= min(8, ceil(512 / (B*Hkv*P))), at least 1."""
-    want = min(8, -(-512 // (B * Hkv * P)))
+    """Shares per slice: largest power of two <= min(32, ceil(512 / (B*Hkv*P))), at least 1."""
+    want = min(32, -(-512 // (B * Hkv * P)))
     c = 1
     while 2 * c <= want:
         c *= 2

@@ -150,12 +150,14 @@ def test_slice_counts(P):
     check_whole(make_inputs(W("P", (50000, 9000, 129)), 9, "cuda"), P=P, what=f"P{P}")
 
 
-@pytest.mark.parametrize("B,hkv,P,C", [(64, 4, 2, 1), (32, 4, 2, 2), (13, 4, 2, 4), (3, 4, 3, 8), (1, 4, 8, 8)])
+@pytest.mark.parametrize("B,hkv,P,C", [(64, 4, 2, 1), (32, 4, 2, 2), (13, 4, 2, 4), (3, 4, 3, 8), (1, 4, 8, 16),
+                                       (1, 2, 1, 32), (1, 4, 2, 32)])
 def test_share_counts(B, hkv, P, C):
-    """Batch shapes whose attention launch splits every slice into C = 1, 2, 4, 8 shares (the
-    last one, P*C = 64, merges the shares through LDS instead of registers)."""
-    want = min(8, -(-512 // (B * hkv * P)))
-    assert max(c for c in (1, 2, 4, 8) if c <= want) == C
+    """Batch shapes whose attention launch splits every slice into C = 1 .. 32 shares (with
+    P*C > 32, as for C = 16 at P = 8 and C = 32 at P = 2, the shares merge through LDS
+    instead of registers)."""
+    want = min(32, -(-512 // (B * hkv * P)))
+    assert max(c for c in (1, 2, 4, 8, 16, 32) if c <= want) == C
     rng = random.Random(B)
     lens = tuple(rng.choice([0, 5, 2048, 2049, 2600, 4100, 9000, 20000]) for _ in range(B))
     check_whole(make_inputs(W("shares", lens, 32, hkv, P), 11, "cuda"), P=P, what=f"C{C}")
