@@ -455,7 +455,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
       // thread, spread over the context), with R > 1 keys 0, 16, 32, 48 of every chunk.
       int shift = shift_for(lo, hi);
       uint32_t mine = 0;
-      if constexpr (R == 1) {
+      // With n <= 2k + 128 the sample's threshold would keep every key (its target count,
+      // 2k*nsamp/n + 8, reaches nsamp), so the sample is skipped and tau = lo.
+      const bool sample = n > 2 * k + 128;
+      if (!sample) {
+        // nothing: every key is a candidate
+      } else if constexpr (R == 1) {
         const int c16 = (t >> 4) & 15;
         for_slots(nvmax, [&](int e) {
           if ((e & 15) == c16) {
@@ -474,10 +479,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
             atomicAdd(&sh.hbuf[hsel][ok ? (key(r, e) - lo) >> shift : dummy], 1u);
           }
       }
-      const uint32_t nsamp = block_sum(mine, sh, 0);
-      const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
       uint32_t tau = lo;
-      {
+      if (sample) {   // the same for the whole workgroup
+        const uint32_t nsamp = block_sum(mine, sh, 0);
+        const uint32_t need_s = (uint32_t)(((unsigned long long)2 * k * nsamp + n - 1) / n) + 8;
         int bs;
         uint32_t ab;
         find_bucket(sh, hsel, need_s, &bs, &ab);   // always: it also clears the next buffer
@@ -498,7 +503,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
         cand[r] = m;
         mine += __builtin_popcountll(m);
       }
-      ncand = block_sum(mine, sh, 1);
+      ncand = sample ? block_sum(mine, sh, 1) : (uint32_t)n;   // without a sample every key is one
       if (ncand >= (uint32_t)k && ncand <= (uint32_t)kListCap) {
         // A thread's candidates take consecutive slots: one wave prefix sum of the counts and
         // one reservation per wave. With R = 1 the keys come from registers (unrolled, so the
