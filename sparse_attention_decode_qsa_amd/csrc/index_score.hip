@@ -36,15 +36,20 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_kernel(
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages,
     int max_blocks, int32_t* __restrict__ scores, int32_t* __restrict__ page_max) {
   const int b = blockIdx.y;
-  const int L = lens[b];
-  const int npages = (L + kPageSize - 1) / kPageSize;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int p = blockIdx.x * WAVES + wave;
-  if (p >= npages) return;
   const int r4 = lane >> 4, c = lane & 15;
-
-  const int page = page_table[(size_t)b * max_pages + p];
+  // The length and this wave's page-table entry (a scalar load at a clamped index, in bounds
+  // whatever the length) are loaded together, so the keys wait for one round trip, not for
+  // the length and then the page. The empty asm takes the page as an input ahead of the
+  // exit test; without it the compiler moves the page load (and the loads of the kernel
+  // arguments it needs) past the test, a chain of dependent round trips.
+  const int L = lens[b];
+  const int page = page_table[(size_t)b * max_pages + __builtin_amdgcn_readfirstlane(min(p, max_pages - 1))];
+  asm volatile("" ::"s"(page));
+  const int npages = (L + kPageSize - 1) / kPageSize;
+  if (p >= npages) return;
   i32x4 qv[T];
 #pragma unroll
   for (int t = 0; t < T; ++t)
