@@ -39,18 +39,19 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_mq_kernel(
   __shared__ i32x4 s_q[kQueryChunk * kQStride];
   static_assert((kQueryChunk * kIdxTokenBytes / 16) % (kMqWaves * 64) == 0, "whole vectors per thread");
   const int b = blockIdx.y;
-  const int L = lens[b];
-  const int npages = (L + kPageSize - 1) / kPageSize;
-  if (blockIdx.x * kMqWaves >= npages) return;   // the same for the whole workgroup
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g4 = lane >> 4;
   const int p = blockIdx.x * kMqWaves + wave;
+  // The page id is wave-uniform: a scalar load (its own counter, so the keys wait for it
+  // and not for the query loads) at a clamped index, in bounds whatever the length, issued
+  // together with the length's load (the empty asm keeps it ahead of the exit test).
+  const int page = page_table[(size_t)b * max_pages + __builtin_amdgcn_readfirstlane(min(p, max_pages - 1))];
+  const int L = lens[b];
+  asm volatile("" ::"s"(page), "s"(L));
+  const int npages = (L + kPageSize - 1) / kPageSize;
+  if (blockIdx.x * kMqWaves >= npages) return;   // the same for the whole workgroup
   const bool active = p < npages;                 // idle waves still join the barriers
   const int valid = L - p * kPageSize;
-  // The page id is wave-uniform: a scalar load (its own counter, so the keys wait for it
-  // and not for the query loads), without a branch (an idle wave reads the last page's
-  // entry; npages >= 1 here).
-  const int page = page_table[(size_t)b * max_pages + __builtin_amdgcn_readfirstlane(min(p, npages - 1))];
   // The first query chunk is loaded before the keys, so its latency overlaps theirs; it is
   // written to LDS once it arrives (the key loads stay in flight).
   constexpr int kQVecs = kQueryChunk * kIdxTokenBytes / 16;   // 16-byte vectors per chunk

@@ -143,9 +143,17 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
     const int32_t* __restrict__ lens, int max_pages, int max_blocks, int32_t* __restrict__ scores,
     int32_t* __restrict__ page_max, StepWrite step) {
   const int b = blockIdx.y, lane = lane_id(), wave = threadIdx.x >> 6;
-  const int L = lens[b];
-  const int npages = (L + kPageSize - 1) / kPageSize;
   const int p0 = (blockIdx.x * WAVES + wave) * PPW;   // the wave's PPW consecutive pages
+  // The length and the wave's page-table entries (scalar loads at clamped indices, in bounds
+  // whatever the length) are loaded together, and the empty asm keeps the entries ahead of
+  // the exit test, so the keys wait for one round trip instead of two.
+  const int L = lens[b];
+  int pages[PPW];
+#pragma unroll
+  for (int k = 0; k < PPW; ++k)
+    pages[k] = page_table[(size_t)b * max_pages + __builtin_amdgcn_readfirstlane(min(p0 + k, max_pages - 1))];
+  asm volatile("" ::"s"(pages[0]));
+  const int npages = (L + kPageSize - 1) / kPageSize;
   if (p0 >= npages) return;
   const int hf = lane >> 5, c = lane & 31;
   const int nblk = (L + kTokensPerBlock - 1) / kTokensPerBlock;
@@ -160,13 +168,10 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
   }
   // every load of the wave's pages is issued before any arithmetic
   i32x4 v[PPW][8];
-  int pages[PPW];
 #pragma unroll
   for (int k = 0; k < PPW; ++k) {
     if (p0 + k >= npages) break;
-    const int page = page_table[(size_t)b * max_pages + p0 + k];
-    pages[k] = page;
-    const int8_t* base = reinterpret_cast<const int8_t*>(pooled) + (size_t)page * kPooledPageBytes + 16 * lane;
+    const int8_t* base = reinterpret_cast<const int8_t*>(pooled) + (size_t)pages[k] * kPooledPageBytes + 16 * lane;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[k][i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + 1024 * i));
   }
