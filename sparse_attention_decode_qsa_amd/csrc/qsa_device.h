@@ -32,9 +32,10 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Context length of virtual request r = b*T + t when every request carries T draft tokens:
-// draft token t sees L_b - (T-1-t) tokens, itself included (T = 1: request r itself).
+// draft token t sees L_b - (T-1-t) tokens, itself included (T = 1: request r itself, whose
+// length 0 <= L_r is returned as it is). No branch, so loads issued next to it are not held
+// behind it.
 __device__ __forceinline__ int draft_length(const int32_t* lens, int r, int T) {
-  if (T == 1) return lens[r];
   const int b = r / T;
   return max(0, lens[b] - (T - 1 - (r - b * T)));
 }

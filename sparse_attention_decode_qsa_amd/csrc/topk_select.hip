@@ -253,7 +253,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   constexpr int kListCap = SelShared<R>::kListCap;
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = lane_id();
-  const int n = (draft_length(lens, b, T) + kTokensPerBlock - 1) / kTokensPerBlock;
+  // The page maxima are loaded at clamped indices (in bounds whatever the length) together
+  // with the length, so they do not wait for it; entries past the request's pages are masked
+  // where they are used. The loads take no branch (without page maxima they read lens[0],
+  // unused), and the empty asm statements keep them ahead of the early exit.
+  constexpr int PV = 4 * R;                      // page maxima per thread (np <= 4096*R)
+  const int32_t* pm = page_max != nullptr ? page_max + (size_t)b * max_pages : lens;
+  const int pm_last = page_max != nullptr ? max_pages - 1 : 0;
+  const int len = draft_length(lens, b, T);
+  int32_t pm_raw[PV];
+#pragma unroll
+  for (int i = 0; i < PV; ++i) pm_raw[i] = pm[min(t + kSelThreads * i, pm_last)];
+  asm volatile("" ::"s"(len));
+#pragma unroll
+  for (int i = 0; i < PV; ++i) asm volatile("" ::"v"(pm_raw[i]));
+  uint32_t pv[PV];
+#pragma unroll
+  for (int i = 0; i < PV; ++i) pv[i] = score_key(pm_raw[i]);
+  const int n = (len + kTokensPerBlock - 1) / kTokensPerBlock;
   int32_t* out = sel + (size_t)b * k;
 
   if (n <= k) {  // every block is kept
@@ -280,15 +297,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   // histogram is cleared, so the two overlap.
   const int np = (n + kBlocksPerPage - 1) / kBlocksPerPage;
   const bool use_pm = page_max != nullptr && np >= k;
-  constexpr int PV = 4 * R;                      // page maxima per thread (np <= 4096*R)
-  uint32_t pv[PV];
   if (use_pm) {
-    const int32_t* pm = page_max + (size_t)b * max_pages;
 #pragma unroll
-    for (int i = 0; i < PV; ++i) {
-      const int pidx = t + kSelThreads * i;
-      pv[i] = pidx < np ? score_key(pm[pidx]) : 0u;
-    }
+    for (int i = 0; i < PV; ++i) pv[i] = t + kSelThreads * i < np ? pv[i] : 0u;
   }
   for (int i = t; i < kSelBins + 64; i += kSelThreads) sh.hbuf[0][i] = 0;
 #pragma unroll
