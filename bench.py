@@ -55,6 +55,22 @@ def index_bytes(lengths):
     return sum(IDX_TOKEN_BYTES * L + 256 + 4 * ((L + 63) // 64) + 4 * ((L + 3) // 4) for L in lengths)
 
 
+def default_sets(lengths, hkv, draft=1, k=512, max_sets=64, max_bytes=96 << 30):
+    """Rotated input sets for a timed window that no cache can shorten.
+
+    The scan's nontemporal loads do not displace what sits in the 256 MB MALL, so a set's
+    kept K/V rows (16.8 MB per call at the 256K batch) would still be there when the rotation
+    comes back to it after a few sets; in a model with many layers nothing of one layer's K/V
+    survives until its next step. So one rotation must both stream >= 1 GiB of indexer keys and
+    gather >= 512 MiB of distinct K/V rows. Capped at max_sets and at max_bytes of inputs.
+    """
+    idx = IDX_TOKEN_BYTES * sum(lengths)
+    kept = draft * sum(min(4 * k, L) for L in lengths) * hkv * 512
+    per_set = idx + sum(lengths) * hkv * 512           # indexer keys + K and V caches
+    n = max(math.ceil((1 << 30) / max(idx, 1)), math.ceil((512 << 20) / max(kept, 1)))
+    return max(1, min(n, max_sets, max(1, max_bytes // max(per_set, 1))))
+
+
 def kept_tokens_exact(sel, lengths):
     """|T_b| from the kept block ids (tail block counted with its valid tokens only)."""
     import numpy as np
@@ -125,7 +141,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="w4")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed 1 GiB)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotated input sets (0: enough that one rotation streams >= 1 GiB of indexer keys "
+                         "and gathers >= 512 MiB of distinct K/V rows, so the 256 MB MALL serves no repeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each call from a HIP graph captured once per input set")
@@ -158,7 +176,7 @@ def main():
     lengths = draw_lengths(w, args.seed)
     wl = w.with_(lengths=("list",) + tuple(lengths))   # every rotated set keeps seed-0 lengths
     idx_bytes_per_set = IDX_TOKEN_BYTES * sum(lengths)
-    sets = args.sets or max(1, min(16, math.ceil((1 << 30) / max(idx_bytes_per_set, 1))))
+    sets = args.sets or default_sets(lengths, w.hkv, args.draft)
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
