@@ -161,9 +161,35 @@ def test_prefill_chunk_1024_tokens():
         ref = oracle.decode_request(bf16_bits(q[0, t]), qi[0, t].cpu().numpy(), a["idx_cache"], a["k_cache"],
                                     a["v_cache"], a["page_table"][0], Lt, 4, x.scale)
         check_request(g, t, ref, Lt, what=f"chunk t{t}")
-    # selection of every token equals the oracle's selection from the GPU's own scores
-    for t in range(0, T, 37):
-        Lt = oracle.draft_length(8192, T, t)
+    # every 37th token: scores and selection against the oracle's, computed from the inputs
+    _check_scores_and_selection(g, qi, a, 0, 8192, T, range(0, T, 37))
+
+
+def _check_scores_and_selection(g, qi, a, b, L, T, tokens):
+    qi_np = qi.cpu().numpy()
+    for t in tokens:
+        Lt = oracle.draft_length(L, T, t)
         n = (Lt + 3) // 4
-        kept = oracle.select_blocks(g["scores"][t, :n])
-        assert np.array_equal(g["sel"][t, :len(kept)], kept), t
+        ref = oracle.index_scores(qi_np[b, t], a["idx_cache"], a["page_table"][b], Lt)
+        assert np.array_equal(g["scores"][b * T + t, :n], ref), f"scores of token {t}"
+        kept = oracle.select_blocks(ref)
+        assert np.array_equal(g["sel"][b * T + t, :len(kept)], kept), f"selection of token {t}"
+        assert g["cnt"][b * T + t] == len(kept)
+
+
+def test_prefill_chunk_max_tokens():
+    """The largest chunk the entry points take, 4096 new tokens: the last 4096 tokens of a
+    4200-token request (new token t sees 105 + t tokens, so tokens up to 1943 keep every
+    block and the later ones select). Sampled tokens, the dense boundary among them, against
+    the oracle in full; every 31st token's scores and selection."""
+    T, L = 4096, 4200
+    x = make_inputs(Workload("chunk_max", 1, ("list", L), 32, 4, 4), 57, "cuda")
+    q, qi = draft_queries(x, T, 57)
+    plan, g = _run(x, q, qi, 4)
+    a = oracle_arrays(x)
+    for t in (0, 1, 1942, 1943, 1944, 2047, 4094, 4095):   # 1943 sees 2,048 tokens, 1944 one more
+        Lt = oracle.draft_length(L, T, t)
+        ref = oracle.decode_request(bf16_bits(q[0, t]), qi[0, t].cpu().numpy(), a["idx_cache"], a["k_cache"],
+                                    a["v_cache"], a["page_table"][0], Lt, 4, x.scale)
+        check_request(g, t, ref, Lt, what=f"chunk_max t{t}")
+    _check_scores_and_selection(g, qi, a, 0, L, T, range(0, T, 31))
