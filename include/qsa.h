@@ -8,9 +8,10 @@
  *     best blocks (about 2,048 positions) are kept; the final softmax and the value
  *     aggregation run on the uncompressed K and V.
  *   - same section, first paragraph and bullets, and section "Questions worth answering
- *     directly" (DCP versus TP): each decode-context-parallel rank reads only its slice of
- *     the context and the partial attention results are combined afterwards. Here the P
- *     slices of one request are read on one GPU and merged by log-sum-exp.
+ *     directly" (DCP versus TP): under DCP every rank scans one contiguous piece of a
+ *     request's context, and the per-piece attention partials are joined in a second
+ *     step. Here the P pieces (slices) of one request are read on one GPU and joined by
+ *     log-sum-exp.
  *
  * One decode step of one QSA layer is the chain
  *     qsa_index_score -> qsa_topk_select -> qsa_sparse_attn_decode -> qsa_lse_merge
@@ -136,8 +137,8 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
  *
  * Article, same paragraph: the final softmax and the value aggregation use the
  * uncompressed K and V at the kept positions; section "What the pull request actually
- * changes", first paragraph and bullets: each rank reads only its own slice of the
- * context. Request b's pages are cut into P contiguous runs of S_b = ceil(ceil(L_b/64)/P)
+ * changes", first paragraph and bullets: under DCP a rank attends over its own contiguous
+ * piece of the context. Request b's pages are cut into P contiguous runs of S_b = ceil(ceil(L_b/64)/P)
  * pages; slice p covers tokens [64*p*S_b, min(64*(p+1)*S_b, L_b)). For each slice p and
  * query head h (KV head g = h / (Hq/Hkv)), over the kept tokens t of slice p:
  *     s_t = softmax_scale * dot(q[b][h], K[t][g])
@@ -171,8 +172,8 @@ qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const vo
  * qsa_lse_merge - combine the P slice partials of every (request, head).
  *
  * Article, section "What the pull request actually changes", bullets, and section
- * "Questions worth answering directly" (DCP versus TP): the partial attention results of
- * the slices are combined after the split read. With M = max over p of the finite
+ * "Questions worth answering directly" (DCP versus TP): the per-slice partials are joined
+ * once every slice has been read. With M = max over p of the finite
  * partial_lse, w_p = exp(partial_lse - M):
  *     out = sum_p w_p partial_out[p] / sum_p w_p,   out_lse = M + ln(sum_p w_p)
  * Slices with lse = -inf carry no weight; if every slice is -inf, out = 0, out_lse = -inf.

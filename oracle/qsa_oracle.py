@@ -15,12 +15,12 @@ draft PR for Qwen3.8-Flash-Next" (orcarouter.ai blog):
           indexer compresses the keys into micro-blocks of 4 tokens, scores those blocks,
           keeps the 512 best (about 2,048 token positions), and the final softmax and the
           value aggregation still use the full, uncompressed K and V.
-  [SPLIT] same section, first paragraph and first bullets: under decode context
-          parallelism each rank reads only its own slice of the context (of the main KV
-          cache) and the attention results are combined after that split read.
+  [SPLIT] same section, first paragraph and first bullets: with decode context
+          parallelism the main KV cache is sharded by context position, a rank attends
+          over its own contiguous piece, and a second step joins the pieces.
   [MERGE] section "Questions worth answering directly", answer on how DCP differs from
-          tensor parallelism: each rank holds and reads a slice of the context, and the
-          partial attention results are merged afterwards.
+          tensor parallelism: the shards are pieces of the sequence rather than of the
+          heads, so the per-piece attention partials have to be joined at the end.
   [GROUP] section "What the pull request actually changes", bullets: the selector and the
           main KV cache sit in one cache group (here: one page table and one length per
           request serve both the indexer keys and K/V).

@@ -2,8 +2,8 @@
 //
 // Article "Qwen 4 QSA gets decode context parallelism: inside vLLM's draft PR for
 // Qwen3.8-Flash-Next", section "What the pull request actually changes" (bullets) and
-// section "Questions worth answering directly" (how DCP differs from TP): the partial
-// attention results of the slices are combined after the split read. With M the largest
+// section "Questions worth answering directly" (how DCP differs from TP): the per-slice
+// partials are joined once every slice has been read. With M the largest
 // finite slice lse and w_p = exp(lse_p - M):
 //     out = sum_p w_p o_p / sum_p w_p,   lse = M + ln(sum_p w_p)
 // Slices with lse = -inf carry no weight; with none finite, out = 0 and lse = -inf.

@@ -24,12 +24,25 @@ def oracle_decode(oracle, x, P=None, k=512):
                          a["page_table"], a["lengths"], P, x.scale, k)
 
 
-def tolerance_report(got, ref, atol=2e-3, rtol=1e-2):
-    """Element-wise |g - r| <= atol + rtol*|r|; returns (ok, max_abs, max_rel_over_big)."""
+# The parity bar for floating-point results against the float64 oracle: a maximum absolute
+# error of 2e-3 and, separately, a maximum relative error of 1e-2. The relative error is taken
+# over elements with |oracle| >= REL_FLOOR: below that an fp32 result's relative error is set
+# by absolute rounding (~1e-7 here) and says nothing about the method.
+ATOL, RTOL, REL_FLOOR = 2e-3, 1e-2, 1e-3
+
+
+def tolerance_report(got, ref, atol=ATOL, rtol=RTOL, floor=REL_FLOOR):
+    """Two separate bounds: max |g - r| <= atol over every element, and max |g - r| / |r| <= rtol
+    over the elements with |r| >= floor; every result must be finite.
+
+    Returns (ok, max_abs, max_rel)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if got.size == 0:
+        return True, 0.0, 0.0
     err = np.abs(got - ref)
-    ok = bool(np.all(err <= atol + rtol * np.abs(ref)) and np.all(np.isfinite(got)))
-    big = np.abs(ref) >= atol / rtol
+    big = np.abs(ref) >= floor
+    max_abs = float(err.max())
     max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
-    return ok, float(err.max()) if err.size else 0.0, max_rel
+    ok = bool(np.all(np.isfinite(got)) and max_abs <= atol and max_rel <= rtol)
+    return ok, max_abs, max_rel

@@ -1,9 +1,10 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Block scores, kept block ids and counts must match bit for bit. Attention partials and
-merged outputs must satisfy |gpu - oracle| <= 2e-3 + 1e-2*|oracle| element-wise (the
-oracle is float64). Small batches are checked whole; the full-size workloads are checked
-on sampled requests plus properties that hold for every request.
+merged outputs must stay within two separate bounds of the float64 oracle: a maximum
+absolute error of 2e-3 and a maximum relative error of 1e-2 (over |oracle| >= 1e-3).
+Small batches and the full-size workloads are checked request by request against the
+oracle.
 """
 import math
 import random
@@ -17,10 +18,9 @@ import oracle
 from sparse_attention_decode_qsa_amd import qsa
 from sparse_attention_decode_qsa_amd.inputs import (PAGE_SIZE, WORKLOADS, Workload, make_inputs,
                                                     request_subset)
-from tests.helpers import oracle_decode, tolerance_report
+from tests.helpers import ATOL, RTOL, oracle_decode, tolerance_report
 
 pytestmark = pytest.mark.gpu
-ATOL, RTOL = 2e-3, 1e-2
 
 
 def say(msg):
@@ -56,7 +56,7 @@ def check_request(g, b, r, L, k=512, what=""):
         fin = np.isfinite(ref)
         assert np.array_equal(np.isfinite(got), fin), f"{what} {name}: -inf pattern differs (b={b})"
         ok, ma, mr = tolerance_report(got[fin], ref[fin], ATOL, RTOL)
-        assert ok, f"{what} {name} outside tolerance (b={b}, max abs {ma:.3g})"
+        assert ok, f"{what} {name} outside tolerance (b={b}, max abs {ma:.3g}, max rel {mr:.3g})"
     return tolerance_report(g["out"][b], r["out"], ATOL, RTOL)
 
 
@@ -428,7 +428,8 @@ def test_lse_merge_alone(P):
         assert ok, (b, ma, mr)
         fin = np.isfinite(rl)
         assert np.array_equal(np.isfinite(lse[b]), fin)
-        assert np.allclose(lse[b][fin], rl[fin], atol=ATOL, rtol=RTOL)
+        ok, ma, mr = tolerance_report(lse[b][fin], rl[fin], ATOL, RTOL)
+        assert ok, (b, ma, mr)
         assert np.all(out[b][~fin] == 0)
 
 

@@ -187,16 +187,52 @@ def _sdpa(q, k_rows, v_rows, scale):
     return o.numpy(), lse.numpy()
 
 
+def _torch_bf16(bits):
+    """bf16 bit patterns decoded by torch's own bfloat16 -> float64 conversion (not the oracle's)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_decoding_every_bit_pattern():
+    """bf16_to_f64 on raw bits equals torch's bfloat16 -> float64 conversion for all 65,536
+    patterns: +-0 (sign kept), subnormals, normals, +-inf, and NaN for every NaN pattern."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        got = oracle.bf16_to_f64(bits)
+    ref = _torch_bf16(bits)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127                      # exponent all ones, mantissa != 0, both signs
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decoding_hand_values():
+    """Values fixed by the bf16 format (1 sign, 8 exponent bits with bias 127, 7 fraction bits)."""
+    table = {0x0000: 0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0xC040: -3.0, 0x3FC0: 1.5,
+             0x3F01: 0.50390625, 0x4049: 3.140625, 0x0080: 2.0**-126, 0x0001: 2.0**-133,
+             0x007F: 127 * 2.0**-133, 0x7F7F: (2 - 2.0**-7) * 2.0**127, 0x7F80: math.inf, 0xFF80: -math.inf}
+    bits = np.array(list(table), dtype=np.uint16)
+    got = oracle.bf16_to_f64(bits)
+    assert got.tolist() == list(table.values())
+    assert np.signbit(oracle.bf16_to_f64(np.array([0x8000], dtype=np.uint16)))[0]
+    assert np.isnan(oracle.bf16_to_f64(np.array([0x7FC0, 0xFF81], dtype=np.uint16))).all()
+
+
 @pytest.mark.parametrize("L", [1, 5, 100, 2047, 2048])
 def test_short_context_equals_dense_attention(L):
     w = Workload("t", 1, ("list", L), 32, 4, 4)
     x = make_inputs(w, seed=L)
     r = oracle_decode(oracle, x)[0]
     assert len(r["kept"]) == (L + 3) // 4          # every block kept
-    a = oracle_arrays(x)
-    kr = oracle.bf16_to_f64(oracle.request_rows(a["k_cache"], a["page_table"][0], L))
-    vr = oracle.bf16_to_f64(oracle.request_rows(a["v_cache"], a["page_table"][0], L))
-    o, lse = _sdpa(oracle.bf16_to_f64(a["q"][0]), kr, vr, x.scale)
+    # The reference reads the request's K/V rows straight from the torch tensors (logical
+    # order through the page table) and decodes bf16 with torch, so it shares neither the
+    # oracle's row gathering nor its bf16 decoding.
+    pt = x.page_table[0].tolist()
+    rows = [(pt[t // 64], t % 64) for t in range(L)]
+    kr = torch.stack([x.k_cache[p, t] for p, t in rows]).to(torch.float64).numpy()
+    vr = torch.stack([x.v_cache[p, t] for p, t in rows]).to(torch.float64).numpy()
+    o, lse = _sdpa(x.q[0].to(torch.float64).numpy(), kr, vr, x.scale)
     np.testing.assert_allclose(r["out"], o, rtol=0, atol=1e-12)
     np.testing.assert_allclose(r["lse"], lse, rtol=0, atol=1e-12)
 

@@ -108,6 +108,20 @@ def _append_new_row_only(k_cache, v_cache, idx_cache, side, page_table, lengths,
     return k2, v2, i2, s2
 
 
+def _bf16_as_fp16(x):                    # reads the bits as IEEE half precision
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return a.view(np.float16).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _bf16_shift8(x):                     # places the 16 bits 8 positions too low in the float32
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 8).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
 def _draft_one_short(length, T, t):              # draft token t misses itself
     return max(0, int(length) - (T - t))
 
@@ -136,6 +150,12 @@ MUTATIONS = [
     ("side_cache", _side_slot_shift, lambda: side_pins.test_side_cache_brute_force((5, 70))),
     ("append_token", _append_whole_block, lambda: side_pins.test_append_reproduces_full_caches((6, 130))),
     ("append_token", _append_new_row_only, lambda: side_pins.test_append_reproduces_full_caches((7, 64))),
+    ("bf16_to_f64", _bf16_as_fp16, pins.test_bf16_decoding_every_bit_pattern),
+    ("bf16_to_f64", _bf16_shift8, pins.test_bf16_decoding_every_bit_pattern),
+    ("bf16_to_f64", _bf16_as_fp16, pins.test_bf16_decoding_hand_values),
+    ("bf16_to_f64", _bf16_shift8, pins.test_bf16_decoding_hand_values),
+    ("bf16_to_f64", _bf16_as_fp16, lambda: pins.test_short_context_equals_dense_attention(100)),
+    ("bf16_to_f64", _bf16_shift8, lambda: pins.test_short_context_equals_dense_attention(5)),
     ("draft_length", _draft_one_short, lambda: multi_pins.test_last_draft_token_sees_the_whole_context(2)),
     ("draft_length", _draft_sees_all, lambda: multi_pins.test_draft_tokens_are_causal(2)),
 ]
