@@ -16,8 +16,7 @@ import torch
 
 import oracle
 from sparse_attention_decode_qsa_amd import qsa
-from sparse_attention_decode_qsa_amd.inputs import (PAGE_SIZE, WORKLOADS, Workload, make_inputs,
-                                                    request_subset)
+from sparse_attention_decode_qsa_amd.inputs import PAGE_SIZE, WORKLOADS, Workload, make_inputs
 from tests.helpers import ATOL, RTOL, oracle_decode, tolerance_report
 
 pytestmark = pytest.mark.gpu
@@ -80,20 +79,6 @@ def check_properties(x, g, k=512):
         assert np.all(np.diff(s[:K]) > 0) and (K == 0 or (s[0] >= 0 and s[K - 1] < nblk))
         assert np.all(s[K:] == -1)
         assert np.all(np.isfinite(g["out"][b])) and np.all(np.isfinite(g["lse"][b]) | (L == 0))
-
-
-def spot_check_scores(x, g, n=64, seed=0):
-    """Scores of random blocks of every request, each computed by the oracle on its own."""
-    rng = random.Random(seed)
-    pt = x.page_table.cpu().numpy()
-    qi = x.q_idx.cpu().numpy()
-    for b, L in enumerate(x.lengths):
-        nblk = (L + 3) // 4
-        for j in [0, nblk - 1] + [rng.randrange(nblk) for _ in range(n)]:
-            toks = range(4 * j, min(4 * j + 4, L))
-            rows = np.stack([x.idx_cache[int(pt[b, t // PAGE_SIZE]), t % PAGE_SIZE].cpu().numpy() for t in toks])
-            ref = oracle.block_scores(qi[b], oracle.pooled_keys(rows))[0]
-            assert g["scores"][b, j] == ref, f"score of block {j} of request {b}"
 
 
 # ---------------------------------------------------------------- small, whole batches
@@ -287,9 +272,12 @@ def test_repeat_is_bitwise_and_workspace_is_reusable():
         check_request(g, b, r, x.lengths[b], what="plan")
 
 
-# ------------------------------------------------------ full-size workloads, sampled
+# ----------------------------------------------- full-size workloads, every request
 
-def _full(name, sample):
+def _full(name):
+    """A full-size workload through qsa_decode, then every request against the oracle: scores,
+    kept ids and counts bit for bit, partials and outputs within the two bounds."""
+    import time
     x = make_inputs(WORKLOADS[name], 0, "cuda")
     plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens,
                           x.workload.slices)
@@ -299,49 +287,43 @@ def _full(name, sample):
              po=plan.partial_out.cpu().numpy(), pl=plan.partial_lse.cpu().numpy(), out=plan.out.cpu().numpy(),
              lse=plan.out_lse.cpu().numpy())
     check_properties(x, g)
-    spot_check_scores(x, g)
-    rows = sample(x)
-    say(f"[{name}] lens={len(x.lengths)} requests, checking {rows}")
-    sub = request_subset(x, rows)
-    refs = oracle_decode(oracle, sub)
-    worst = 0.0
-    for i, b in enumerate(rows):
-        gi = {key: v[b:b + 1] for key, v in g.items()}
-        ok, ma, mr = check_request(gi, 0, refs[i], x.lengths[b], what=name)
-        worst = max(worst, ma)
-    say(f"[{name}] max abs err of out over sampled requests: {worst:.3g}")
+    say(f"[{name}] {x.batch} requests, lengths {min(x.lengths)}..{max(x.lengths)}: oracle on every request")
+    t0 = time.time()
+    refs = oracle_decode(oracle, x)
+    worst_abs = worst_rel = 0.0
+    for b, r in enumerate(refs):
+        ok, ma, mr = check_request(g, b, r, x.lengths[b], what=name)
+        worst_abs, worst_rel = max(worst_abs, ma), max(worst_rel, mr)
+    say(f"[{name}] all {x.batch} requests match; out max abs err {worst_abs:.3g}, max rel err {worst_rel:.3g}; "
+        f"oracle {time.time() - t0:.1f} s")
     return x, g
 
 
 def test_full_w2_planted_selection_everywhere():
-    x, g = _full("w2", lambda x: [0, 17, 31])
+    x, g = _full("w2")
     for b in range(x.batch):
         assert g["sel"][b].tolist() == x.planted[b]
 
 
 def test_full_w3():
-    _full("w3", lambda x: [0, 5])
+    _full("w3")
 
 
 def test_full_w4_all_requests():
-    _full("w4", lambda x: list(range(x.batch)))
+    _full("w4")
 
 
 def test_full_w4_fixed_max_context():
-    _full("w4_fixed", lambda x: [3])
+    _full("w4_fixed")
 
 
-@pytest.mark.skip(reason="faulted the GPU once (illegal memory access at the first synchronize after "
-                         "the w5 decode); no cause shown yet: kernel index ranges for these shapes check "
-                         "out on the CPU emulation, so the case stays off the GPU until a cause is shown")
-def test_full_w5_dense_and_sampled():
-    def pick(x):
-        L = x.lengths
-        dense = [b for b, v in enumerate(L) if v <= 2048]
-        assert dense, "the lognormal batch must hold a request of at most 2048 tokens"
-        extremes = [int(np.argmin(L)), int(np.argmax(L))]
-        return sorted(set(dense + extremes + [3, 64]))
-    _full("w5", pick)
+@pytest.mark.skip(reason="the first run of this batch (B = 128, caches of 2.75e9 K/V elements, with the "
+                         "first kernel design) ended in an illegal memory access; no cause has been shown, "
+                         "so the case stays off the GPU")
+def test_full_w5_every_request():
+    x, g = _full("w5")
+    dense = [b for b, L in enumerate(x.lengths) if L <= 2048]
+    assert dense, "the lognormal batch must hold a request of at most 2048 tokens"
 
 
 # ------------------------------------------- top-k on crafted score distributions
