@@ -67,7 +67,9 @@ typedef enum {
   QSA_ERR_SHAPE = 2,        /* sizes are negative or inconsistent                  */
   QSA_ERR_UNSUPPORTED = 3,  /* a size outside what the kernels are compiled for    */
   QSA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required          */
-  QSA_ERR_HIP = 5           /* the HIP runtime reported an error                   */
+  QSA_ERR_HIP = 5,          /* the HIP runtime reported an error                   */
+  QSA_ERR_SCRATCH = 6       /* qsa_decode_noalloc: the call needs more than the
+                               library's static scratch (QSA_NOALLOC_SCRATCH_BYTES)  */
 } qsa_status_t;
 
 /* Static description of a status code; never NULL. */
@@ -207,6 +209,35 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
                         float* partial_out, float* partial_lse, float* out, float* out_lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qsa_decode_noalloc - qsa_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same chain
+ * and the same results, bit for bit, with the workspace taken from a static device array of
+ * the library instead of a caller buffer. The caller still passes every input and output.
+ *
+ * The array holds QSA_NOALLOC_SCRATCH_BYTES bytes on each device the library runs on, from
+ * the library's load until the process ends. Its device address is looked up once per device
+ * (hipGetSymbolAddress, on the call's current device) at the first call there. A call whose
+ * qsa_decode_workspace_size(B, Hq, Hkv, max_blocks, k, P) exceeds the array returns
+ * QSA_ERR_SCRATCH and launches nothing. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Nothing in the array needs to start at zero: every word the
+ * chain reads there is written earlier in the same call.
+ *
+ * Every call on one device shares that device's array: calls that may overlap on one device
+ * (different streams, or one stream and another thread) race on it and must be serialised by
+ * the caller. Arguments and errors otherwise as qsa_decode.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+qsa_status_t qsa_decode_noalloc(const void* q, const int8_t* q_idx, const int8_t* idx_cache,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* page_table, const int32_t* context_lens,
+                                int B, int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim,
+                                int page_size, int max_pages_per_seq, int max_blocks, int k, int P,
+                                float softmax_scale,
+                                int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
+                                float* partial_out, float* partial_lse, float* out, float* out_lse,
+                                void* stream);
 
 /*
  * qsa_decode_multi - multi-token decode: T new tokens per request, 1 <= T <= 4096, B*T <= 65535

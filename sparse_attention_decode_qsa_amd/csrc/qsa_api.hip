@@ -1,7 +1,14 @@
 // qsa_api.hip - the C ABI of libqsa: argument checks, workspace sizing, launches.
 // Every check that can be made on the host runs before anything is enqueued.
+#include <mutex>
+
 #include "../../include/qsa.h"
 #include "qsa_device.h"
+
+// Static scratch of qsa_decode_noalloc (the workspace of the decode chain for callers that
+// cannot allocate). On the host the name is only a stand-in for the symbol: kernels get the
+// device address that hipGetSymbolAddress returns for the current device, never the name.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
 
 namespace qsa {
 hipError_t launch_index_score(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int,
@@ -111,6 +118,7 @@ const char* qsa_status_string(int s) {
     case QSA_ERR_UNSUPPORTED: return "size outside the compiled kernel shapes";
     case QSA_ERR_WORKSPACE: return "workspace missing or too small";
     case QSA_ERR_HIP: return "HIP runtime error";
+    case QSA_ERR_SCRATCH: return "the call needs more workspace than the static scratch holds";
     default: return "unknown status";
   }
 }
@@ -255,7 +263,61 @@ qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_
   return hip_status(e);
 }
 
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];   // device address of `scratch` per device, once looked up
+std::mutex g_scratch_mu;
+
+// Device address of the static scratch on the current device: looked up with
+// hipGetSymbolAddress on the first call on that device, then kept.
+qsa_status_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return QSA_ERR_UNSUPPORTED;
+  void* p = __atomic_load_n(&g_scratch[dev], __ATOMIC_ACQUIRE);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev];
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (p == nullptr) return QSA_ERR_HIP;
+      __atomic_store_n(&g_scratch[dev], p, __ATOMIC_RELEASE);
+    }
+  }
+  *out = p;
+  return QSA_OK;
+}
+
 }  // namespace
+
+qsa_status_t qsa_decode_noalloc(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const void* k_cache,
+                                const void* v_cache, const int32_t* page_table, const int32_t* context_lens, int B,
+                                int Hq, int Hkv, int head_dim, int n_idx_heads, int idx_dim, int page_size,
+                                int max_pages_per_seq, int max_blocks, int k, int P, float softmax_scale,
+                                int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count, float* partial_out,
+                                float* partial_lse, float* out, float* out_lse, void* stream) {
+  if (B < 0) return QSA_ERR_SHAPE;
+  if (B == 0) return QSA_OK;
+  // Argument checks first (the size query below assumes sane shapes); a call that fails them
+  // returns the same code as qsa_decode, before the scratch is looked up.
+  qsa_status_t st = check_index(q_idx, idx_cache, page_table, context_lens, B, n_idx_heads, idx_dim, page_size,
+                                max_pages_per_seq, max_blocks, block_scores);
+  if (st == QSA_OK) st = check_topk(block_scores, context_lens, B, max_blocks, k, sel_blocks, sel_count);
+  if (st == QSA_OK)
+    st = check_attn(q, k_cache, v_cache, page_table, context_lens, sel_blocks, sel_count, B, Hq, Hkv, head_dim,
+                    page_size, max_pages_per_seq, k, P, partial_out, partial_lse);
+  if (st == QSA_OK) st = check_merge(partial_out, partial_lse, B, P, Hq, head_dim, out);
+  if (st != QSA_OK) return st;
+  const size_t need = qsa_decode_workspace_size(B, Hq, Hkv, max_blocks, k, P);
+  if (need > QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != QSA_OK) return st;
+  return decode_chain(q, q_idx, idx_cache, nullptr, k_cache, v_cache, page_table, context_lens, B, 1, Hq, Hkv,
+                      head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
+                      block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, ws,
+                      QSA_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const void* k_cache,
                         const void* v_cache, const int32_t* page_table, const int32_t* context_lens, int B,

@@ -23,7 +23,8 @@ HEAD_DIM = 128
 MAX_K = 512
 
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPPORTED",
-          4: "QSA_ERR_WORKSPACE", 5: "QSA_ERR_HIP"}
+          4: "QSA_ERR_WORKSPACE", 5: "QSA_ERR_HIP", 6: "QSA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # QSA_NOALLOC_SCRATCH_BYTES of include/qsa.h
 
 # (name, restype, argtypes) of every symbol declared in include/qsa.h
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -41,6 +42,8 @@ SIGNATURES = {
     "qsa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "qsa_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                         _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "qsa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                _P, _P, _P, _P, _P, _P, _P, _P]),
     "qsa_workspace_clear": (_I, [_P, _Z, _P]),
     "qsa_check_pages": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
     "qsa_decode_multi_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -223,9 +226,11 @@ class DecodePlan:
     """
 
     def __init__(self, q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P, k=MAX_K,
-                 softmax_scale=None, max_blocks=None, pooled=None):
+                 softmax_scale=None, max_blocks=None, pooled=None, noalloc=False):
         """pooled: optional side cache of pooled keys (int16); the scan then reads it
-        (qsa_decode_pooled) instead of idx_cache, for the same results."""
+        (qsa_decode_pooled) instead of idx_cache, for the same results.
+        noalloc: run qsa_decode_noalloc, whose workspace is the library's static scratch (no
+        workspace is allocated here; calls that overlap on one device race on that scratch)."""
         for t, dt, n in ((q, torch.bfloat16, "q"), (q_idx, torch.int8, "q_idx"),
                          (idx_cache, torch.int8, "idx_cache"), (k_cache, torch.bfloat16, "k_cache"),
                          (v_cache, torch.bfloat16, "v_cache"), (page_table, torch.int32, "page_table"),
@@ -244,18 +249,24 @@ class DecodePlan:
         self.partial_lse = torch.empty((B, P, Hq), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         self.out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        self.workspace = Workspace(decode_workspace_size(B, Hq, Hkv, self.max_blocks, k, P), dev)
+        if noalloc and pooled is not None:
+            raise ValueError("noalloc runs qsa_decode_noalloc, which reads the int8 indexer keys")
+        self.workspace = None if noalloc else Workspace(decode_workspace_size(B, Hq, Hkv, self.max_blocks, k, P),
+                                                        dev)
         scale = D ** -0.5 if softmax_scale is None else softmax_scale
         if pooled is not None:
             _need(pooled, torch.int16, "pooled", 4)
-        self._fn = lib().qsa_decode if pooled is None else lib().qsa_decode_pooled
+        self._fn = (lib().qsa_decode_noalloc if noalloc else
+                    lib().qsa_decode if pooled is None else lib().qsa_decode_pooled)
         self._args = [
             _ptr(q), _ptr(q_idx), _ptr(idx_cache if pooled is None else pooled), _ptr(k_cache), _ptr(v_cache),
             _ptr(page_table),
             _ptr(context_lens), B, Hq, Hkv, D, q_idx.shape[1], q_idx.shape[2], k_cache.shape[1],
             max_pages, self.max_blocks, k, P, ctypes.c_float(scale), _ptr(self.scores), _ptr(self.sel),
             _ptr(self.sel_count), _ptr(self.partial_out), _ptr(self.partial_lse), _ptr(self.out),
-            _ptr(self.out_lse), self.workspace.ptr(), self.workspace.nbytes]
+            _ptr(self.out_lse)]
+        if not noalloc:
+            self._args += [self.workspace.ptr(), self.workspace.nbytes]
 
     def run(self, stream=None):
         s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()

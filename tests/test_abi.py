@@ -31,8 +31,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = qsa.lib()
-    for s in range(6):
-        assert L.qsa_status_string(s)
+    for s in range(7):
+        assert L.qsa_status_string(s) and L.qsa_status_string(s) != b"unknown status"
     assert L.qsa_status_string(99) == b"unknown status"
     assert L.qsa_version() >= 100
     assert L.qsa_last_hip_error() == 0
@@ -266,3 +266,29 @@ def test_decode_step_pooled_host_checks():
     assert f(*bad) == SHAPE                        # Hq % Hkv
     bad = list(args); bad[32] = 100
     assert f(*bad) == WS
+
+
+def test_decode_noalloc_host_checks():
+    """qsa_decode_noalloc: qsa_decode's argument checks, then the static scratch's limit; a
+    call that fails either returns its code before any device call (none runs here)."""
+    L = qsa.lib()
+    f = L.qsa_decode_noalloc
+    args = [FAKE] * 7 + [2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [None]
+    assert len(args) == len(qsa.SIGNATURES["qsa_decode_noalloc"][1])
+    assert f(*args[:7], 0, *args[8:]) == OK
+    bad = list(args); bad[7] = -1
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[0] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[8] = 33
+    assert f(*bad) == SHAPE                        # Hq % Hkv
+    bad = list(args); bad[10] = 64
+    assert f(*bad) == UNSUP                        # head_dim
+    # more workspace than the scratch holds: 4096 requests of up to 262,144 tokens
+    big = list(args); big[7], big[14], big[15] = 4096, 4096, 65536
+    need = L.qsa_decode_workspace_size(4096, 32, 4, 65536, 512, 4)
+    assert need > qsa.NOALLOC_SCRATCH_BYTES
+    assert f(*big) == 6                            # QSA_ERR_SCRATCH
+    # the w4 and 128-request shapes fit
+    assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) <= qsa.NOALLOC_SCRATCH_BYTES
+    assert L.qsa_decode_workspace_size(128, 32, 4, 65536, 512, 4) <= qsa.NOALLOC_SCRATCH_BYTES
