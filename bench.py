@@ -101,37 +101,68 @@ def mq_roofline(scan_ops, k1_bytes, ms_k1, D):
     return r
 
 
-def cpu_baseline(x, budget_s=12.0):
-    """The CPU oracle, as it stands, on the same batch (host copies of set 0), one thread."""
-    import torch
-    from threadpoolctl import threadpool_limits
-    import oracle
-    from sparse_attention_decode_qsa_amd.inputs import bf16_bits
+_CPU_BATCH = {}
 
-    a = dict(q=bf16_bits(x.q), q_idx=x.q_idx.cpu().numpy(), idx=x.idx_cache.cpu().numpy(),
-             k=bf16_bits(x.k_cache), v=bf16_bits(x.v_cache), pt=x.page_table.cpu().numpy())
-    calls, t_total = 0, 0.0
-    with threadpool_limits(limits=1):
-        torch.set_num_threads(1)
-        while t_total < budget_s:
-            t0 = time.perf_counter()
-            oracle.decode(a["q"], a["q_idx"], a["idx"], a["k"], a["v"], a["pt"], x.lengths,
-                          x.workload.slices, x.scale)
-            t_total += time.perf_counter() - t0
-            calls += 1
-    model = "unknown CPU"
+
+def _host_cpu():
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": calls / t_total, "unit": "calls/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} full calls on the benchmarked batch (all {x.batch} requests, input set 0), "
-                      f"numpy float64/int64 on one host thread of {model} ({os.cpu_count()} logical CPUs "
-                      f"visible), {t_total:.1f} s"}
+    return "unknown CPU"
+
+
+def _oracle_calls(budget_s):
+    """Whole-batch oracle calls on one host thread for about budget_s seconds: (calls, seconds)."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    a = _CPU_BATCH
+    calls, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_total < budget_s:
+            t0 = time.perf_counter()
+            oracle.decode(a["q"], a["q_idx"], a["idx"], a["k"], a["v"], a["pt"], a["lengths"], a["P"], a["scale"])
+            t_total += time.perf_counter() - t0
+            calls += 1
+    return calls, t_total
+
+
+def cpu_baseline(wl, seed, budget_s=12.0):
+    """The CPU oracle, as it stands, on a batch of the benchmarked workload drawn on the host
+    (the same lengths, shapes and value laws as the GPU's input sets), run before anything
+    touches the GPU: first on one host thread, then in one forked worker process per host core
+    available to this process, each on one thread, all calling the oracle on the whole batch."""
+    import multiprocessing as mp
+    import torch
+    from sparse_attention_decode_qsa_amd.inputs import bf16_bits, make_inputs
+
+    x = make_inputs(wl, seed, "cpu")
+    _CPU_BATCH.update(q=bf16_bits(x.q), q_idx=x.q_idx.numpy(), idx=x.idx_cache.numpy(), k=bf16_bits(x.k_cache),
+                      v=bf16_bits(x.v_cache), pt=x.page_table.numpy(), lengths=list(x.lengths),
+                      P=x.workload.slices, scale=x.scale)
+    del x
+    torch.set_num_threads(1)
+    calls1, t1 = _oracle_calls(budget_s)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        per = pool.map(_oracle_calls, [budget_s] * cores)
+    wall = time.perf_counter() - t0
+    rate_all = sum(c / t for c, t in per)
+    model = _host_cpu()
+    return {"value": rate_all, "unit": "calls/s", "cores": cores, "kind": "oracle",
+            "sample": f"the benchmarked workload's batch drawn on the host (same lengths and shapes as the GPU "
+                      f"sets; all {len(_CPU_BATCH['lengths'])} requests per call), numpy float64/int64: "
+                      f"{cores} worker processes of one thread each on {model}, "
+                      f"{sum(c for c, _ in per)} whole calls in {wall:.1f} s",
+            "one_core": {"value": calls1 / t1, "unit": "calls/s", "cores": 1,
+                         "sample": f"{calls1} whole calls on one thread in {t1:.1f} s"}}
 
 
 def main():
@@ -177,6 +208,12 @@ def main():
     wl = w.with_(lengths=("list",) + tuple(lengths))   # every rotated set keeps seed-0 lengths
     idx_bytes_per_set = IDX_TOKEN_BYTES * sum(lengths)
     sets = args.sets or default_sets(lengths, w.hkv, args.draft)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before anything touches the GPU, so that the forked workers carry no GPU state
+        print("# timing the CPU oracle on the same workload", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.seed)
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
@@ -261,8 +298,25 @@ def main():
     lat = sorted(a.elapsed_time(b) * 1000.0 for a, b in pairs)
     pct = lambda q: round(lat[min(len(lat) - 1, int(q * len(lat)))], 2)
 
-    # ---- the dominant kernel alone (indexer scan), same stream, same inputs
+    # ---- the dominant kernel (indexer scan), timed inside the chain: qsa_time_next_scan makes
+    # the scan launched by the next qsa_decode call record a pair of events at the kernel's own
+    # start and end (kernel timestamps, as a kernel trace takes them; no marker packets in the
+    # chain), on the stream it runs on. Every call of this pass is a whole qsa_decode call.
     k_iters = max(args.steps, 100)
+    D_single = args.draft == 1 and not args.pooled and not args.graph
+    if D_single:
+        marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k_iters)]
+        for a, b in marks:               # torch creates an event at its first record
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(10):
+            step(i)
+        for i, (a, b) in enumerate(marks):
+            qsa.time_next_scan(a, b)
+            step(i)
+        torch.cuda.synchronize()
+        ms_k1 = sum(a.elapsed_time(b) for a, b in marks) / k_iters
 
     def scan(i):
         x = inputs[i % sets]
@@ -274,15 +328,16 @@ def main():
         else:
             qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
 
-    for i in range(10):
-        scan(i)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(k_iters):
-        scan(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_k1 = e0.elapsed_time(e1) / k_iters
+    if not D_single:   # other modes: the scan alone, back to back, same stream and inputs
+        for i in range(10):
+            scan(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(k_iters):
+            scan(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_k1 = e0.elapsed_time(e1) / k_iters
 
     # ---- measured device ceilings, same stream: qsa_calib_copy of 1 GiB (read + write) and
     # qsa_calib_read of 1 GiB (the scan's kind of loads, read only)
@@ -385,6 +440,8 @@ def main():
             "frac_of_read_ceiling": round(k1_gbs / read_gbs, 4),
             "avg_launch_us": round(ms_k1 * 1000, 3),
             "bytes_per_launch": k1_bytes,
+            "timing": ("inside whole qsa_decode calls: events recorded at the scan kernel's own start and "
+                       "end (qsa_time_next_scan)" if D_single else "the scan alone, back to back"),
         }),
     }
     if args.copy_calibration:
@@ -397,9 +454,11 @@ def main():
         torch.cuda.synchronize()
         assert torch.equal(dst, src)
         print(f"# copy calibration: 3 copies of {n} bytes (read {n}, write {n} each)", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
-        print("# timing the CPU oracle on the same workload", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inputs[0])
+    if cpu is not None:
+        # the oracle's effective rate over the same algorithmic bytes per call
+        cpu["GBps"] = round(cpu["value"] * algo / 1e9, 3)
+        cpu["one_core"]["GBps"] = round(cpu["one_core"]["value"] * algo / 1e9, 4)
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -211,6 +211,16 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qsa_time_next_scan - measurement hook. The next launch of the indexer scan kernel made by
+ * this thread (through qsa_index_score, qsa_decode, qsa_decode_noalloc or qsa_decode_multi
+ * with T <= 4) records start_event when the kernel begins executing and stop_event when it
+ * ends (both hipEvent_t created with timing enabled, either may be NULL), so the kernel's own
+ * duration can be read with hipEventElapsedTime, inside a chain, without marker packets
+ * around it. Used once, then cleared; NULL, NULL clears it. Always returns QSA_OK.
+ */
+qsa_status_t qsa_time_next_scan(void* start_event, void* stop_event);
+
+/*
  * qsa_decode_noalloc - qsa_decode for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same chain
  * and the same results, bit for bit, with the workspace taken from a static device array of

@@ -26,6 +26,8 @@
 // Multi-token decode (T draft tokens per request, T <= 4): the page is read once and scored
 // against the T indexer queries q_idx[b][t]; draft token t sees the first L_b - (T-1-t)
 // tokens, and its scores and page maxima go to row b*T + t.
+#include <hip/hip_ext.h>
+
 #include "qsa_device.h"
 
 namespace qsa {
@@ -139,24 +141,45 @@ hipError_t launch_index_score_mq(const int8_t* q_idx, const int8_t* idx_cache, c
 
 constexpr int kScoreWaves = 16;
 
+namespace {
+// Events that the next launch of index_score_kernel on this thread records at its own start
+// and end (set by qsa_time_next_scan; used once, then cleared).
+thread_local hipEvent_t g_scan_start = nullptr, g_scan_stop = nullptr;
+
+template <int TT>
+void launch_scan(dim3 grid, hipStream_t stream, const int8_t* q_idx, const int8_t* idx_cache,
+                 const int32_t* page_table, const int32_t* lens, int max_pages, int max_blocks, int32_t* scores,
+                 int32_t* page_max) {
+  const hipEvent_t e0 = g_scan_start, e1 = g_scan_stop;
+  g_scan_start = g_scan_stop = nullptr;
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL((index_score_kernel<kScoreWaves, TT>), grid, dim3(kScoreWaves * 64), 0, stream, e0, e1,
+                          0, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
+  else
+    hipLaunchKernelGGL((index_score_kernel<kScoreWaves, TT>), grid, dim3(kScoreWaves * 64), 0, stream, q_idx,
+                       idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
+}
+}  // namespace
+
+void set_scan_events(hipEvent_t start, hipEvent_t stop) {
+  g_scan_start = start;
+  g_scan_stop = stop;
+}
+
 hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                               const int32_t* page_table, const int32_t* lens, int B,
                               int max_pages, int max_blocks, int32_t* scores, int32_t* page_max,
                               int T, hipStream_t stream) {
-  const unsigned gx = (unsigned)((max_pages + kScoreWaves - 1) / kScoreWaves);
-#define QSA_SCAN(TT)                                                                                      \
-  hipLaunchKernelGGL((index_score_kernel<kScoreWaves, TT>), dim3(gx, B), dim3(kScoreWaves * 64), 0, stream, \
-                     q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max)
+  const dim3 grid((unsigned)((max_pages + kScoreWaves - 1) / kScoreWaves), B);
   switch (T) {
-    case 1: QSA_SCAN(1); break;
-    case 2: QSA_SCAN(2); break;
-    case 3: QSA_SCAN(3); break;
-    case 4: QSA_SCAN(4); break;
+    case 1: launch_scan<1>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
+    case 2: launch_scan<2>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
+    case 3: launch_scan<3>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
+    case 4: launch_scan<4>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
     default:
       return launch_index_score_mq(q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, scores,
                                    page_max, T, stream);
   }
-#undef QSA_SCAN
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES
 namespace qsa {
 hipError_t launch_index_score(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int,
                               int, int32_t*, int32_t*, int, hipStream_t);   // ..., T, stream
+void set_scan_events(hipEvent_t start, hipEvent_t stop);
 size_t topk_workspace_bytes(int B, int max_blocks);
 constexpr int kMaxSelBlocks = 262144;
 hipError_t launch_topk_select(const int32_t*, const int32_t*, const int32_t*, int, int, int, int, int32_t*,
@@ -124,6 +125,11 @@ const char* qsa_status_string(int s) {
 }
 
 int qsa_last_hip_error(void) { return g_last_hip_error; }
+
+qsa_status_t qsa_time_next_scan(void* start_event, void* stop_event) {
+  set_scan_events(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+  return QSA_OK;
+}
 
 int qsa_version(void) { return 200; }   // 0.2.0: side cache, multi-token decode, page check
 

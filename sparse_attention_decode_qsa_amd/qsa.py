@@ -45,6 +45,7 @@ SIGNATURES = {
     "qsa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                 _P, _P, _P, _P, _P, _P, _P, _P]),
     "qsa_workspace_clear": (_I, [_P, _Z, _P]),
+    "qsa_time_next_scan": (_I, [_P, _P]),
     "qsa_check_pages": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
     "qsa_decode_multi_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "qsa_index_score_multi": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
@@ -217,6 +218,15 @@ def lse_merge(partial_out, partial_lse, out=None, out_lse=None, want_lse=True):
     _check(lib().qsa_lse_merge(_ptr(partial_out), _ptr(partial_lse), B, P, Hq, D, _ptr(out),
                                _ptr(out_lse), _stream()))
     return out, out_lse
+
+
+def time_next_scan(start, stop):
+    """The next indexer-scan launch of this thread records torch.cuda.Event `start` at the
+    kernel's start and `stop` at its end (events created with enable_timing=True and recorded
+    once before, so that torch has created them)."""
+    if not start.cuda_event or not stop.cuda_event:
+        raise ValueError("time_next_scan: the events must have been recorded once (torch creates them lazily)")
+    _check(lib().qsa_time_next_scan(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))
 
 
 class DecodePlan:
