@@ -154,8 +154,12 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
   }
 }
 
-// Grid (C * Hkv, P, B). With T draft tokens per request, b is the virtual request
-// b_req*T + t (page-table row b_req, length L - (T-1-t)). Writes the partial of share c of
+// Grid (C * Hkv * T, P, B_req): blockIdx.x = (t * Hkv + g) * C + c for new token t of request
+// b_req = blockIdx.z, slice p = blockIdx.y, and b = b_req*T + t is the virtual request
+// (page-table row b_req, length L - (T-1-t)). With many new tokens (a prefill chunk) the
+// workgroups of one (request, slice) are dispatched together, so the slice's K/V rows, kept
+// by several tokens each, are re-read while they sit in the 256 MB MALL instead of again from
+// HBM. With T = 1 it is the single-token grid (C * Hkv, P, B). Writes the partial of share c of
 // (b, p, KV head g) for the query heads of g: sub_out [B, P, C, Hq, 128] (normalised over the share), sub_lse [B, P, C, Hq]
 // (natural log; -inf for an empty share, whose output is 0).
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
@@ -164,7 +168,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int Hq, int Hkv,
     int max_pages, int k, int P, int C, int T, float scale_log2, float* __restrict__ sub_out,
     float* __restrict__ sub_lse) {
-  const int g = blockIdx.x / C, c = blockIdx.x - g * C, p = blockIdx.y, b = blockIdx.z;
+  const int gc = blockIdx.x % (C * Hkv), tq = blockIdx.x / (C * Hkv);
+  const int g = gc / C, c = gc - g * C, p = blockIdx.y, b = blockIdx.z * T + tq;
   const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
   const int i16 = lane & 15, q4 = lane >> 4;
   const int group = Hq / Hkv;
@@ -323,7 +328,8 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
   float* sub_out = static_cast<float*>(workspace);
   float* sub_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn_sub_out_bytes(B, Hq, Hkv, P));
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3(C * Hkv, P, B), dim3(kAttnThreads), 0, stream,
+  if ((long long)C * Hkv * T > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sparse_attn_kernel, dim3(C * Hkv * T, P, B / T), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), page_table, lens, sel, sel_count, Hq, Hkv,
                      max_pages, k, P, C, T, scale_log2, sub_out, sub_lse);
