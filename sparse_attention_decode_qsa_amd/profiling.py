@@ -80,6 +80,35 @@ def chain_span_us(trace_csv: str, skip: int = 20) -> float | None:
     return spans[len(spans) // 2]
 
 
+def chain_timeline(trace_csv: str, skip: int = 10) -> list[dict] | None:
+    """Median start and end of each kernel of a whole call (scan, selection, attention, merge),
+    in us from the start of the call's scan, over the calls of the trace (the first `skip`
+    calls left out)."""
+    tr = [r for r in csv.DictReader(open(trace_csv)) if "qsa::" in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    calls, i = [], 0
+    while i + 3 < len(tr):
+        names = [tr[i + d]["Kernel_Name"] for d in range(4)]
+        if ("index_score" in names[0] and "topk_select" in names[1] and "sparse_attn" in names[2]
+                and "merge" in names[3]):
+            t0 = int(tr[i]["Start_Timestamp"])
+            calls.append([(_short(names[d]), int(tr[i + d]["Start_Timestamp"]) - t0,
+                           int(tr[i + d]["End_Timestamp"]) - t0) for d in range(4)])
+            i += 4
+        else:
+            i += 1
+    calls = calls[skip:] or calls
+    if not calls:
+        return None
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2] / 1e3
+
+    return [dict(kernel=calls[0][d][0], start_us=med([c[d][1] for c in calls]), end_us=med([c[d][2] for c in calls]),
+                 dur_us=med([c[d][2] - c[d][1] for c in calls]), calls=len(calls)) for d in range(4)]
+
+
 def write_stats(dir_: str, prefix: str, command: str, out: str, title: str, note: str = "") -> None:
     rows = stats_table(os.path.join(dir_, f"{prefix}_kernel_stats.csv"))
     span = chain_span_us(os.path.join(dir_, f"{prefix}_kernel_trace.csv"))
@@ -91,6 +120,12 @@ def write_stats(dir_: str, prefix: str, command: str, out: str, title: str, note
     lines.append("")
     if span is not None:
         lines.append(f"Median span of one whole call (start of its first kernel to the end of the merge): {span:.2f} us.")
+    tl = chain_timeline(os.path.join(dir_, f"{prefix}_kernel_trace.csv"))
+    if tl:
+        lines += ["", f"Timeline of one call (medians over {tl[0]['calls']} whole calls, us from the start of the scan):", "",
+                  "| kernel | start | end | duration |", "|---|---|---|---|"]
+        for r in tl:
+            lines.append(f"| {r['kernel']} | {r['start_us']:.2f} | {r['end_us']:.2f} | {r['dur_us']:.2f} |")
     if note:
         lines += ["", note]
     open(out, "w").write("\n".join(lines) + "\n")
