@@ -162,7 +162,7 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
 // HBM. With T = 1 it is the single-token grid (C * Hkv, P, B). Writes the partial of share c of
 // (b, p, KV head g) for the query heads of g: sub_out [B, P, C, Hq, 128] (normalised over the share), sub_lse [B, P, C, Hq]
 // (natural log; -inf for an empty share, whose output is 0).
-__global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int Hq, int Hkv,
