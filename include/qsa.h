@@ -4,9 +4,9 @@
  * The method, as the article "Qwen 4 QSA gets decode context parallelism: inside vLLM's
  * draft PR for Qwen3.8-Flash-Next" (orcarouter.ai blog) describes it:
  *   - section "What the pull request actually changes", second paragraph: a light
- *     indexer compresses the keys into micro-blocks of 4 tokens and scores them; the 512
+ *     indexer pools the keys of every 4 consecutive tokens (a micro-block) and scores each pool; the 512
  *     best blocks (about 2,048 positions) are kept; the final softmax and the value
- *     aggregation run on the uncompressed K and V.
+ *     aggregation use the full K and V rows of the kept tokens, not pooled ones.
  *   - same section, first paragraph and bullets, and section "Questions worth answering
  *     directly" (DCP versus TP): under DCP every rank scans one contiguous piece of a
  *     request's context, and the per-piece attention partials are joined in a second
@@ -85,7 +85,7 @@ int qsa_version(void);
  * qsa_index_score - indexer scan, micro-block pooling and block scoring.
  *
  * Article, section "What the pull request actually changes", second paragraph: the
- * indexer compresses keys into micro-blocks of 4 tokens and scores them. With the
+ * indexer pools the keys of every 4 consecutive tokens and scores each pool. With the
  * compiled shapes, for request b of length L_b and block j < ceil(L_b/4):
  *     pooled[j][h][d] = sum of idx key[t][h][d] over tokens t = 4j .. min(4j+3, L_b-1)
  *     block_scores[b][j] = sum_h sum_d q_idx[b][h][d] * pooled[j][h][d]      (exact)
@@ -138,7 +138,7 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
  * qsa_sparse_attn_decode - attention of the decode query over the kept tokens, per slice.
  *
  * Article, same paragraph: the final softmax and the value aggregation use the
- * uncompressed K and V at the kept positions; section "What the pull request actually
+ * full (not pooled) K and V rows of the kept positions; section "What the pull request actually
  * changes", first paragraph and bullets: under DCP a rank attends over its own contiguous
  * piece of the context. Request b's pages are cut into P contiguous runs of S_b = ceil(ceil(L_b/64)/P)
  * pages; slice p covers tokens [64*p*S_b, min(64*(p+1)*S_b, L_b)). For each slice p and
@@ -294,7 +294,7 @@ qsa_status_t qsa_decode_multi(const void* q, const int8_t* q_idx, const int8_t* 
  * The indexer's side cache of pooled keys.
  *
  * Article, section "What the pull request actually changes": besides the main cache the
- * indexer keeps selector and side caches (second paragraph), in one cache group with the
+ * indexer keeps caches of its own, a selector cache and side caches (second paragraph), grouped with the
  * main cache, and synthetic batches must not write the side caches (bullets). The side cache
  * here holds the pooled key of every micro-block - the int sum of the int8 indexer keys of
  * its up to 4 tokens (|sum| <= 512), as int16 - so the scan reads 512 bytes per block instead

@@ -12,17 +12,17 @@ What it follows. The article "Qwen 4 QSA gets decode context parallelism: inside
 draft PR for Qwen3.8-Flash-Next" (orcarouter.ai blog):
 
   [QSA]   section "What the pull request actually changes", second paragraph: a light
-          indexer compresses the keys into micro-blocks of 4 tokens, scores those blocks,
+          indexer pools the keys of every 4 consecutive tokens into a micro-block, scores them,
           keeps the 512 best (about 2,048 token positions), and the final softmax and the
-          value aggregation still use the full, uncompressed K and V.
+          value aggregation use the full K and V rows of the kept tokens, not pooled ones.
   [SPLIT] same section, first paragraph and first bullets: with decode context
           parallelism the main KV cache is sharded by context position, a rank attends
           over its own contiguous piece, and a second step joins the pieces.
   [MERGE] section "Questions worth answering directly", answer on how DCP differs from
           tensor parallelism: the shards are pieces of the sequence rather than of the
           heads, so the per-piece attention partials have to be joined at the end.
-  [GROUP] section "What the pull request actually changes", bullets: the selector and the
-          main KV cache sit in one cache group (here: one page table and one length per
+  [GROUP] section "What the pull request actually changes", bullets: the selector's cache and
+          the main K/V cache belong to a single cache group (here: one page table and one length per
           request serve both the indexer keys and K/V).
 
 Readings where the pages leave a step open (each is repeated in the design notes):
@@ -47,7 +47,7 @@ Readings where the pages leave a step open (each is repeated in the design notes
                   an empty slice is (0, -inf). The merge skips -inf partials.
   R10 empty       a request of length 0 keeps nothing; its output is 0 and its lse -inf.
   R11 side cache  the side cache the indexer maintains ([QSA] paragraph: besides the main
-                  cache there are selector and side caches the indexer keeps) holds the
+                  cache the indexer keeps a selector cache and side caches of its own) holds the
                   pooled key (R1) of every micro-block, page-aligned like the main cache:
                   block j of a request sits in page page_table[j // (page/4)], slot
                   j % (page/4). Scores read from it are R2 on the stored keys.

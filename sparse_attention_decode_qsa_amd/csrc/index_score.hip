@@ -2,7 +2,7 @@
 //
 // Article "Qwen 4 QSA gets decode context parallelism: inside vLLM's draft PR for
 // Qwen3.8-Flash-Next", section "What the pull request actually changes", second
-// paragraph: the indexer compresses keys into micro-blocks of 4 tokens and scores them.
+// paragraph: the indexer pools the keys of every 4 consecutive tokens and scores each pool.
 // Block j of request b pools tokens 4j..4j+3 (those below L_b):
 //     S[b][j] = sum_h sum_d q_idx[b][h][d] * sum_t key[t][h][d]
 // The kernel forms the same integer by accumulating, token by token, int8 dot products

@@ -3,7 +3,7 @@
 //
 // Article "Qwen 4 QSA gets decode context parallelism: inside vLLM's draft PR for
 // Qwen3.8-Flash-Next", section "What the pull request actually changes": besides the main
-// cache the indexer keeps selector and side caches (second paragraph), in the same cache
+// cache the indexer keeps a selector cache and side caches of its own (second paragraph), in the same cache
 // group as the main cache, and synthetic batches must not write the side caches (bullets).
 // Here the side cache holds the pooled key of every micro-block (the int sum of the int8
 // keys of its up to 4 tokens, |sum| <= 512, stored as int16), page-aligned like the main

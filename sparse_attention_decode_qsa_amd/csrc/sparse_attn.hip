@@ -2,7 +2,7 @@
 //
 // Article "Qwen 4 QSA gets decode context parallelism: inside vLLM's draft PR for
 // Qwen3.8-Flash-Next", section "What the pull request actually changes": the softmax and
-// the value aggregation run on the uncompressed K and V of the kept positions (second
+// the value aggregation use the full (not pooled) K and V rows of the kept positions (second
 // paragraph); under decode context parallelism a rank attends over one contiguous piece
 // of the context (first paragraph and bullets). Slice p of request b covers the pages
 // [p*S_b, (p+1)*S_b) with S_b = ceil(ceil(L_b/64)/P); its partial is

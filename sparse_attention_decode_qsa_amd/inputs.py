@@ -7,7 +7,7 @@ oracle (through the tests) and the HIP library consume what it produces.
 Workloads follow the article "Qwen 4 QSA gets decode context parallelism: inside
 vLLM's draft PR for Qwen3.8-Flash-Next", section "What the pull request actually
 changes" (micro-blocks of 4 tokens, 512 kept blocks, softmax and value aggregation on
-the uncompressed K/V, each context read as slices whose partials are then joined), at the
+the full K/V rows, each context read as slices whose partials are then joined), at the
 shapes of the five decode workloads this library is measured on:
 
   w1  B=1,   L=4096,                       Hq/Hkv=16/2, identity pages, P=1
