@@ -254,6 +254,32 @@ def test_graph_replay_equals_eager(pooled):
             assert torch.equal(u.view(torch.int32), v.view(torch.int32)), (rep, name)
 
 
+def test_time_next_scan_records_the_scan_only():
+    """qsa_time_next_scan: the next scan of this thread records its start and end (a positive
+    duration no longer than the whole call's), is used once, and leaves every result as it was."""
+    x = make_inputs(W("timed", (70000, 3000, 20000), P=4), 16, "cuda")
+    plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4)
+    plan.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (plan.scores, plan.sel, plan.out, plan.out_lse)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()                         # torch creates an event at its first record
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        qsa.time_next_scan(torch.cuda.Event(enable_timing=True), ev[1])
+    ev[2].record()
+    qsa.time_next_scan(ev[0], ev[1])
+    plan.run()
+    plan.run()                             # not timed: the hook is used once
+    ev[3].record()
+    torch.cuda.synchronize()
+    scan_ms, all_ms = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    assert 0.0 < scan_ms < all_ms, (scan_ms, all_ms)
+    for u, v in zip(ref, (plan.scores, plan.sel, plan.out, plan.out_lse)):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
 def test_repeat_is_bitwise_and_workspace_is_reusable():
     x = make_inputs(W("rep", (70000, 3000, 20000), P=4), 10, "cuda")
     plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4)

@@ -33,3 +33,31 @@ def test_traffic_scaling(tmp_path):
     back = profiling.read_traffic(str(out))
     assert back == r and back["source_hash"] == profiling.scan_source_hash()
     assert profiling.read_traffic(str(tmp_path / "missing.md")) is None
+
+
+def test_chain_timeline_medians(tmp_path):
+    """The per-call timeline: calls are found as scan, selection, attention, merge in a row;
+    other kernels in between break a call; offsets are from each call's scan start."""
+    names = ["void qsa::index_score_kernel<16, 1>(...)", "void qsa::topk_select_kernel<1>(...)",
+             "qsa::sparse_attn_kernel(...)", "qsa::slice_merge_kernel(...)"]
+    rows, t = [], 1000
+    for call in range(5):
+        durs = [30 + call, 9, 10, 4]                      # us
+        for n, d in zip(names, durs):
+            rows.append((n, t, t + d * 1000))
+            t += d * 1000 + 100                           # 0.1 us gap after each kernel
+        t += 5000
+    scan1_end = rows[4][2]                                # call 1's scan
+    rows.append(("qsa::lse_merge_kernel(...)", scan1_end + 10, scan1_end + 20))   # breaks call 1
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, ["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for n, a, b in sorted(rows, key=lambda r: r[1]):
+            w.writerow(dict(Kernel_Name=n, Start_Timestamp=a, End_Timestamp=b))
+    tl = profiling.chain_timeline(str(path), skip=0)
+    assert [r["kernel"] for r in tl] == ["qsa::index_score_kernel<16, 1>", "qsa::topk_select_kernel<1>",
+                                         "qsa::sparse_attn_kernel", "qsa::slice_merge_kernel"]
+    assert tl[0]["calls"] == 4
+    assert tl[0]["start_us"] == 0.0 and tl[1]["dur_us"] == 9.0 and tl[3]["dur_us"] == 4.0
+    assert abs(tl[1]["start_us"] - (tl[0]["dur_us"] + 0.1)) < 1e-9
