@@ -8,6 +8,9 @@ score ties, and an all-zero indexer query where every block ties). Every request
 scores, kept blocks and outputs are compared with the CPU oracle through the C ABI, the
 four separate calls and qsa_decode must agree bit for bit, and the unused rows of each
 request's last page hold poison (NaN K/V, indexer keys 127) that must not reach a result.
+Multi-token decode: up to 3 requests, T from 1 to 8 or 20 new tokens. Wider shapes: up to 6
+requests of up to 80,000 tokens, group sizes 16, 3 and 1, up to 64 slices, k below 512 and
+page tables with spare capacity.
 """
 import numpy as np
 import pytest
@@ -70,3 +73,24 @@ def test_multi_token_matches_oracle_on_random_shapes(lens, T, gqa, P, alphabet, 
         for t in range(T):
             r = b * T + t
             check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"prop T{T} b{b} t{t}")
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(lens=st.lists(st.one_of(st.integers(0, 3000), st.integers(2000, 80000)), min_size=1, max_size=6),
+       gqa=st.sampled_from(GQA + [(64, 4), (12, 4), (16, 16)]), P=st.sampled_from([1, 2, 3, 5, 8, 16, 64]),
+       k=st.sampled_from([1, 100, 511, 512]), alphabet=st.sampled_from(ALPHABETS),
+       extra_pages=st.sampled_from([0, 1, 80]), seed=st.integers(0, 2**16))
+def test_chain_matches_oracle_on_wider_shapes(lens, gqa, P, k, alphabet, extra_pages, seed):
+    """Longer contexts (up to 80,000 tokens, several slices and shares per request), group
+    sizes 16, 3 and 1, up to 64 slices, k below 512, and page tables with spare capacity: the
+    four separate calls against the oracle, every request."""
+    hq, hkv = gqa
+    cap = max(lens) + 64 * extra_pages
+    w = Workload("propw", len(lens), ("list",) + tuple(lens), hq, hkv, P, alphabet=alphabet, max_context=cap, k=k)
+    x = make_inputs(w, seed, "cuda")
+    say(f"[prop wide] lens={lens} Hq/Hkv={hq}/{hkv} P={P} k={k} alphabet={alphabet} cap={cap} seed={seed}")
+    g = run_chain(x, P, k)
+    refs = oracle_decode(oracle, x, P=P, k=k)
+    for b, r in enumerate(refs):
+        check_request(g, b, r, x.lengths[b], k, what="prop wide")
