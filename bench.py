@@ -303,7 +303,7 @@ def main():
     # start and end (kernel timestamps, as a kernel trace takes them; no marker packets in the
     # chain), on the stream it runs on. Every call of this pass is a whole qsa_decode call.
     k_iters = max(args.steps, 100)
-    D_single = args.draft == 1 and not args.pooled and not args.graph
+    D_single = args.draft == 1 and not args.graph   # int8 or side-cache scan inside whole calls
     if D_single:
         marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k_iters)]
         for a, b in marks:               # torch creates an event at its first record
@@ -440,8 +440,9 @@ def main():
             "frac_of_read_ceiling": round(k1_gbs / read_gbs, 4),
             "avg_launch_us": round(ms_k1 * 1000, 3),
             "bytes_per_launch": k1_bytes,
-            "timing": ("inside whole qsa_decode calls: events recorded at the scan kernel's own start and "
-                       "end (qsa_time_next_scan)" if D_single else "the scan alone, back to back"),
+            "timing": (("inside whole qsa_decode_step_pooled calls" if args.pooled else "inside whole qsa_decode calls")
+                       + ": events recorded at the scan kernel's own start and end (qsa_time_next_scan)"
+                       if D_single else "the scan alone, back to back"),
         }),
     }
     if args.copy_calibration:

@@ -211,9 +211,10 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * qsa_time_next_scan - measurement hook. The next launch of the indexer scan kernel made by
- * this thread (through qsa_index_score, qsa_decode, qsa_decode_noalloc or qsa_decode_multi
- * with T <= 4) records start_event when the kernel begins executing and stop_event when it
+ * qsa_time_next_scan - measurement hook. The next launch of an indexer scan kernel made by
+ * this thread (through qsa_index_score, qsa_decode, qsa_decode_noalloc, qsa_decode_multi
+ * with T <= 4, or the side-cache scan of qsa_index_score_pooled, qsa_decode_pooled and
+ * qsa_decode_step_pooled) records start_event when the kernel begins executing and stop_event when it
  * ends (both hipEvent_t created with timing enabled, either may be NULL), so the kernel's own
  * duration can be read with hipEventElapsedTime, inside a chain, without marker packets
  * around it. Used once, then cleared; NULL, NULL clears it. Always returns QSA_OK.

@@ -166,6 +166,13 @@ void set_scan_events(hipEvent_t start, hipEvent_t stop) {
   g_scan_stop = stop;
 }
 
+// The events set for the next scan launch of this thread (cleared): for the side-cache scan.
+void take_scan_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_scan_start;
+  *stop = g_scan_stop;
+  g_scan_start = g_scan_stop = nullptr;
+}
+
 hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                               const int32_t* page_table, const int32_t* lens, int B,
                               int max_pages, int max_blocks, int32_t* scores, int32_t* page_max,

@@ -11,9 +11,13 @@
 // slot j % 16 (a 64-token page holds 16 blocks). A score read from it is the same integer
 // as the scan over the int8 keys computes, from half the bytes (512 B per block instead of
 // 4 x 256 B).
+#include <hip/hip_ext.h>
+
 #include "qsa_device.h"
 
 namespace qsa {
+
+void take_scan_events(hipEvent_t* start, hipEvent_t* stop);   // index_score.hip
 
 constexpr int kSlotsPerPage = kPageSize / kTokensPerBlock;   // 16
 constexpr int kPooledBlockBytes = kIdxTokenBytes * 2;        // 512
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
   }
 }
 
-constexpr int kSideWaves = 16;
+constexpr int kSideWaves = 8;   // 8 pages per workgroup: the pooled scan ran 0.5-0.9 us faster than with 16
 
 hipError_t launch_pool_build(const int8_t* idx_cache, const int32_t* page_table, const int32_t* lens, int B,
                              int max_pages, int16_t* pooled, hipStream_t stream) {
@@ -274,9 +278,16 @@ hipError_t launch_index_score_pooled(const int8_t* q_idx, const int16_t* pooled,
   const unsigned gx = (unsigned)((max_pages + kSideWaves * kPagesPerWave - 1) / (kSideWaves * kPagesPerWave));
   const StepWrite step{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), idx_new, write,
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), idx_cache, Hkv};
-  hipLaunchKernelGGL((index_score_pooled_kernel<kSideWaves, kPagesPerWave>), dim3(gx, B), dim3(kSideWaves * 64), 0,
-                     stream, q_idx, const_cast<int16_t*>(pooled), page_table, lens, max_pages, max_blocks, scores,
-                     page_max, step);
+  hipEvent_t e0, e1;   // kernel-timestamp events of qsa_time_next_scan, if set
+  take_scan_events(&e0, &e1);
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL((index_score_pooled_kernel<kSideWaves, kPagesPerWave>), dim3(gx, B), dim3(kSideWaves * 64),
+                          0, stream, e0, e1, 0, q_idx, const_cast<int16_t*>(pooled), page_table, lens, max_pages,
+                          max_blocks, scores, page_max, step);
+  else
+    hipLaunchKernelGGL((index_score_pooled_kernel<kSideWaves, kPagesPerWave>), dim3(gx, B), dim3(kSideWaves * 64), 0,
+                       stream, q_idx, const_cast<int16_t*>(pooled), page_table, lens, max_pages, max_blocks, scores,
+                       page_max, step);
   return hipGetLastError();
 }
 
