@@ -11,7 +11,7 @@
 //
 // Mapping. Grid (page groups, B): wave w of workgroup x scores page x*WAVES + w of
 // request blockIdx.y (workgroups past the request's pages exit at once), one 16 KiB
-// page = 16 blocks per wave:
+// page = 16 blocks per wave; WAVES is 16, or 4 or 1 for batches with few pages in all:
 //   lane = 16*r4 + c  (r4 = DPP row 0..3, c = 0..15)
 //   load i (i = 0..15) of the lane reads the 16 bytes at offset 16*c of token
 //   16*r4 + i of the page, so every load instruction reads four contiguous 256-byte
@@ -139,25 +139,42 @@ hipError_t launch_index_score_mq(const int8_t* q_idx, const int8_t* idx_cache, c
                                  const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                                  int32_t* page_max, int T, hipStream_t stream);
 
-constexpr int kScoreWaves = 16;
+constexpr int kScoreWaves = 16;     // waves (pages) per workgroup when the batch has pages enough
+constexpr long long kFillGroups = 256;   // workgroups that put every CU to work
 
 namespace {
 // Events that the next launch of index_score_kernel on this thread records at its own start
 // and end (set by qsa_time_next_scan; used once, then cleared).
 thread_local hipEvent_t g_scan_start = nullptr, g_scan_stop = nullptr;
 
-template <int TT>
-void launch_scan(dim3 grid, hipStream_t stream, const int8_t* q_idx, const int8_t* idx_cache,
-                 const int32_t* page_table, const int32_t* lens, int max_pages, int max_blocks, int32_t* scores,
-                 int32_t* page_max) {
+template <int WAVES, int TT>
+void launch_scan_w(int B, hipStream_t stream, const int8_t* q_idx, const int8_t* idx_cache,
+                   const int32_t* page_table, const int32_t* lens, int max_pages, int max_blocks, int32_t* scores,
+                   int32_t* page_max) {
+  const dim3 grid((unsigned)((max_pages + WAVES - 1) / WAVES), B);
   const hipEvent_t e0 = g_scan_start, e1 = g_scan_stop;
   g_scan_start = g_scan_stop = nullptr;
   if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL((index_score_kernel<kScoreWaves, TT>), grid, dim3(kScoreWaves * 64), 0, stream, e0, e1,
-                          0, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
+    hipExtLaunchKernelGGL((index_score_kernel<WAVES, TT>), grid, dim3(WAVES * 64), 0, stream, e0, e1, 0, q_idx,
+                          idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
   else
-    hipLaunchKernelGGL((index_score_kernel<kScoreWaves, TT>), grid, dim3(kScoreWaves * 64), 0, stream, q_idx,
-                       idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
+    hipLaunchKernelGGL((index_score_kernel<WAVES, TT>), grid, dim3(WAVES * 64), 0, stream, q_idx, idx_cache,
+                       page_table, lens, max_pages, max_blocks, scores, page_max);
+}
+
+// A small batch (few pages in all, e.g. one request of 4K tokens) gets smaller workgroups so
+// that its pages spread over many CUs instead of being streamed by a handful of them.
+template <int TT>
+void launch_scan(int B, hipStream_t stream, const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
+                 const int32_t* lens, int max_pages, int max_blocks, int32_t* scores, int32_t* page_max) {
+  const long long pages = (long long)B * max_pages;
+  if (pages >= kFillGroups * kScoreWaves)
+    launch_scan_w<kScoreWaves, TT>(B, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores,
+                                   page_max);
+  else if (pages >= kFillGroups * 4)
+    launch_scan_w<4, TT>(B, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
+  else
+    launch_scan_w<1, TT>(B, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max);
 }
 }  // namespace
 
@@ -177,12 +194,11 @@ hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache,
                               const int32_t* page_table, const int32_t* lens, int B,
                               int max_pages, int max_blocks, int32_t* scores, int32_t* page_max,
                               int T, hipStream_t stream) {
-  const dim3 grid((unsigned)((max_pages + kScoreWaves - 1) / kScoreWaves), B);
   switch (T) {
-    case 1: launch_scan<1>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
-    case 2: launch_scan<2>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
-    case 3: launch_scan<3>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
-    case 4: launch_scan<4>(grid, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
+    case 1: launch_scan<1>(B, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
+    case 2: launch_scan<2>(B, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
+    case 3: launch_scan<3>(B, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
+    case 4: launch_scan<4>(B, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, scores, page_max); break;
     default:
       return launch_index_score_mq(q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, scores,
                                    page_max, T, stream);

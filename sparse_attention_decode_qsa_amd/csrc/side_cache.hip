@@ -268,26 +268,38 @@ hipError_t launch_cache_append(const void* k_new, const void* v_new, const int8_
   return hipGetLastError();
 }
 
-// k_new == nullptr: the scan alone; otherwise it also makes the decode step's cache writes.
+template <int WAVES>
+void launch_pooled_w(int B, hipStream_t stream, hipEvent_t e0, hipEvent_t e1, const int8_t* q_idx,
+                     const int16_t* pooled, const int32_t* page_table, const int32_t* lens, int max_pages,
+                     int max_blocks, int32_t* scores, int32_t* page_max, const StepWrite& step) {
+  const dim3 grid((unsigned)((max_pages + WAVES - 1) / WAVES), B);
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL((index_score_pooled_kernel<WAVES, 1>), grid, dim3(WAVES * 64), 0, stream, e0, e1, 0, q_idx,
+                          const_cast<int16_t*>(pooled), page_table, lens, max_pages, max_blocks, scores, page_max,
+                          step);
+  else
+    hipLaunchKernelGGL((index_score_pooled_kernel<WAVES, 1>), grid, dim3(WAVES * 64), 0, stream, q_idx,
+                       const_cast<int16_t*>(pooled), page_table, lens, max_pages, max_blocks, scores, page_max, step);
+}
+
+// k_new == nullptr: the scan alone; otherwise it also makes the decode step's cache writes. One
+// page per wave; a batch with few pages in all gets one-wave workgroups, so that its pages
+// spread over many CUs.
 hipError_t launch_index_score_pooled(const int8_t* q_idx, const int16_t* pooled, const int32_t* page_table,
                                      const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                                      int32_t* page_max, const void* k_new, const void* v_new, const int8_t* idx_new,
                                      const int32_t* write, void* k_cache, void* v_cache, int8_t* idx_cache, int Hkv,
                                      hipStream_t stream) {
-  constexpr int kPagesPerWave = 1;
-  const unsigned gx = (unsigned)((max_pages + kSideWaves * kPagesPerWave - 1) / (kSideWaves * kPagesPerWave));
   const StepWrite step{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), idx_new, write,
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), idx_cache, Hkv};
   hipEvent_t e0, e1;   // kernel-timestamp events of qsa_time_next_scan, if set
   take_scan_events(&e0, &e1);
-  if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL((index_score_pooled_kernel<kSideWaves, kPagesPerWave>), dim3(gx, B), dim3(kSideWaves * 64),
-                          0, stream, e0, e1, 0, q_idx, const_cast<int16_t*>(pooled), page_table, lens, max_pages,
-                          max_blocks, scores, page_max, step);
+  if ((long long)B * max_pages >= 256LL * kSideWaves)
+    launch_pooled_w<kSideWaves>(B, stream, e0, e1, q_idx, pooled, page_table, lens, max_pages, max_blocks, scores,
+                                page_max, step);
   else
-    hipLaunchKernelGGL((index_score_pooled_kernel<kSideWaves, kPagesPerWave>), dim3(gx, B), dim3(kSideWaves * 64), 0,
-                       stream, q_idx, const_cast<int16_t*>(pooled), page_table, lens, max_pages, max_blocks, scores,
-                       page_max, step);
+    launch_pooled_w<1>(B, stream, e0, e1, q_idx, pooled, page_table, lens, max_pages, max_blocks, scores, page_max,
+                       step);
   return hipGetLastError();
 }
 
