@@ -206,14 +206,16 @@ def main():
     w = WORKLOADS[args.workload]
     lengths = draw_lengths(w, args.seed)
     wl = w.with_(lengths=("list",) + tuple(lengths))   # every rotated set keeps seed-0 lengths
-    idx_bytes_per_set = IDX_TOKEN_BYTES * sum(lengths)
     sets = args.sets or default_sets(lengths, w.hkv, args.draft)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.draft == 1:
         # before anything touches the GPU, so that the forked workers carry no GPU state
         print("# timing the CPU oracle on the same workload", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, args.seed)
+    elif not args.no_cpu_baseline:
+        print("# no CPU baseline with several new tokens per request (the oracle would take minutes per call)",
+              file=sys.stderr, flush=True)
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
@@ -303,8 +305,8 @@ def main():
     # start and end (kernel timestamps, as a kernel trace takes them; no marker packets in the
     # chain), on the stream it runs on. Every call of this pass is a whole qsa_decode call.
     k_iters = max(args.steps, 100)
-    D_single = args.draft == 1 and not args.graph   # int8 or side-cache scan inside whole calls
-    if D_single:
+    in_call_timing = args.draft == 1 and not args.graph   # int8 or side-cache scan inside whole calls
+    if in_call_timing:
         marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k_iters)]
         for a, b in marks:               # torch creates an event at its first record
             a.record(stream)
@@ -328,7 +330,7 @@ def main():
         else:
             qsa.index_score(x.q_idx, x.idx_cache, x.page_table, x.context_lens, out=plans[i % sets].scores)
 
-    if not D_single:   # other modes: the scan alone, back to back, same stream and inputs
+    if not in_call_timing:   # other modes: the scan alone, back to back, same stream and inputs
         for i in range(10):
             scan(i)
         torch.cuda.synchronize()
@@ -442,7 +444,7 @@ def main():
             "bytes_per_launch": k1_bytes,
             "timing": (("inside whole qsa_decode_step_pooled calls" if args.pooled else "inside whole qsa_decode calls")
                        + ": events recorded at the scan kernel's own start and end (qsa_time_next_scan)"
-                       if D_single else "the scan alone, back to back"),
+                       if in_call_timing else "the scan alone, back to back"),
         }),
     }
     if args.copy_calibration:
