@@ -21,8 +21,10 @@
  *
  * Conventions for every entry point
  *   Memory     every pointer is device memory of the current HIP device, unless noted.
- *              The caller owns every buffer. The library allocates no device memory and
- *              keeps no pointer, view or handle after a call returns.
+ *              The caller owns every buffer. No call allocates device memory or keeps a
+ *              pointer, view or handle of the caller's after it returns; the one memory of
+ *              the library's own is the static scratch array of qsa_decode_noalloc (a
+ *              device symbol of the code object, per device, from load to process end).
  *   Streams    `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *              work and return; they never synchronize. Buffers must stay alive until the
  *              stream has passed the work. Inputs are read-only; outputs must not alias
