@@ -42,3 +42,35 @@ def test_noalloc_equals_decode_twice_second_smaller():
                 u = torch.cat([u[b, :(L + 3) // 4] for b, L in enumerate(x.lengths)])
                 v = torch.cat([v[b, :(L + 3) // 4] for b, L in enumerate(x.lengths)])
             assert torch.equal(u.view(torch.int32), v.view(torch.int32)), f"{name}: {key} differs"
+
+
+def test_noalloc_replays_from_a_hip_graph():
+    """The allocation-free call captured in a HIP graph (its workspace address is fixed, so the
+    graph holds no allocation): every replay, with eager work in between, gives qsa_decode's bits."""
+    x, ref, na = _case((9000, 70000, 2049), 4, 23)
+    ref.run()
+    torch.cuda.synchronize()
+    want = _results(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        na.run()                                         # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        na.run()
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        for t in (na.sel, na.partial_out, na.out, na.out_lse):
+            t.fill_(-7)
+        junk.mul_(1.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key, u, v in zip(("scores", "sel", "count", "partial_out", "partial_lse", "out", "lse"), want,
+                             _results(na)):
+            if key == "scores":
+                u = torch.cat([u[b, :(L + 3) // 4] for b, L in enumerate(x.lengths)])
+                v = torch.cat([v[b, :(L + 3) // 4] for b, L in enumerate(x.lengths)])
+            assert torch.equal(u.view(torch.int32), v.view(torch.int32)), f"replay {rep}: {key} differs"
