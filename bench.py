@@ -188,6 +188,10 @@ def main():
     ap.add_argument("--draft", type=int, default=1, metavar="T",
                     help="multi-token decode: T new tokens per request (qsa_decode_multi; drafts for T <= 4, "
                          "a prefill chunk beyond); a call then decodes B*T tokens")
+    ap.add_argument("--spread", type=int, default=None, metavar="D",
+                    help="with --draft T: correlated chunk queries, each new token's indexer query = the "
+                         "request's query + a uniform offset in {-D..D} per element (default: independent "
+                         "queries), so that neighbouring tokens keep overlapping blocks")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 copies of MIB MiB each with qsa_calib_copy (the scan's "
                          "kind of loads and stores), so that hardware byte counters can be scaled "
@@ -243,7 +247,7 @@ def main():
         elif args.draft > 1:
             if args.pooled:
                 raise SystemExit("--draft and --pooled do not combine")
-            dq, dqi = draft_queries(x, args.draft, args.seed + 1000 * r)
+            dq, dqi = draft_queries(x, args.draft, args.seed + 1000 * r, spread=args.spread)
             plans.append(qsa.MultiDecodePlan(dq, dqi, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
                                              x.context_lens, w.slices))
         else:
@@ -421,6 +425,7 @@ def main():
                        f" (qsa_decode_multi, T={D}, per call)" if D > 1 else " (qsa_decode per call)"),
             "indexer_keys": "pooled int16 side cache" if args.pooled else "int8 per token, pooled in the scan",
             "draft_tokens_per_request": D,
+            "chunk_query_spread": args.spread if D > 1 else None,
             "tokens_per_s": round(1000.0 / ms_step * len(lengths) * D, 1),
         },
         "call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": n_lat},

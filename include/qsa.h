@@ -256,7 +256,9 @@ qsa_status_t qsa_decode_noalloc(const void* q, const int8_t* q_idx, const int8_t
  * qsa_decode_multi - multi-token decode: T new tokens per request, 1 <= T <= 4096, B*T <= 65535
  * (draft tokens of speculative decoding with a multi-token-prediction head, T <= 4, or a
  * prefill chunk). For T <= 4 the scan uses int8 dot products per query; for larger T it runs
- * as an int8 matrix product of the T queries with every page's keys on the matrix cores.
+ * as an int8 matrix product of the T queries with every page's keys on the matrix cores. From
+ * T = 16 on, at Hq = 8*Hkv, neighbouring new tokens share attention workgroups that read the
+ * union of their kept blocks once; the results are defined exactly as below either way.
  *
  * The T new tokens are the last T positions of each request's cache (context_lens counts them
  * all). Draft token t, at position L_b - T + t, is decoded exactly as qsa_decode decodes a

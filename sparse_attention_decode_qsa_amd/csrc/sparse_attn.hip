@@ -51,6 +51,7 @@ constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kTilesInFlight = 4;        // tiles whose loads a wave issues before computing
 constexpr int kAttnTargetGroups = 512;   // two workgroups per CU
 constexpr int kMaxSplit = 32;            // shares per slice (tiny batches: one request, few heads)
+constexpr int kPairMinTokens = 16;       // chunks of at least this many new tokens use the pair kernel
 static_assert(kMaxK <= 2 * kAttnThreads, "two kept slots per thread");
 
 // Shares per slice for a launch of B requests, Hkv KV heads and P slices: the largest power
@@ -74,13 +75,17 @@ struct Tile {
   bf16x8 k[4];   // K operand: token i16, dims 32s + 8*q4 .. +7
   u16x8 v[4];    // V rows: token 4*q4 + v, dims 8*i16 .. +7
   bool tv[4];    // token 4*q4 + v exists
+  bool sv[4];    // (pair kernel) ... and is kept by the lane's column's new token
 };
 
 // Tile of 4 kept blocks starting at share slot bbase (share slots [0, nslot)); block ids and
-// their page ids come from LDS.
+// their page ids come from LDS. Rows at or past L are not loaded. PAIR: the lane's column
+// belongs to new token tk of a pair, of length Lc <= L, which keeps a block of the share
+// when bit tk of its s_mask entry is set.
+template <bool PAIR>
 __device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const int* s_sel, const int* s_page,
-                                          int L, const uint16_t* kc, const uint16_t* vc, int Hkv, int g,
-                                          int i16, int q4) {
+                                          const int* s_mask, int L, int Lc, int tk, const uint16_t* kc,
+                                          const uint16_t* vc, int Hkv, int g, int i16, int q4) {
   {
     const int slot = bbase + (i16 >> 2);
     const int tok = slot < nslot ? 4 * s_sel[slot] + (i16 & 3) : L;
@@ -108,9 +113,15 @@ __device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const i
       T.v[v] = u16x8{};
     }
   }
+  if (PAIR) {
+    const bool own = blk >= 0 && ((s_mask[slot] >> tk) & 1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) T.sv[v] = own && 4 * blk + v < Lc;
+  }
 }
 
 // One tile into the wave's online softmax state (m_run, l_run in base-2 units; acc = O^T).
+template <bool PAIR>
 __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, float scale_log2, float& m_run,
                                             float& l_run, f32x4* acc) {
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -119,7 +130,7 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
 
   float sv[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) sv[v] = T.tv[v] ? sc[v] * scale_log2 : -INFINITY;
+  for (int v = 0; v < 4; ++v) sv[v] = (PAIR ? T.sv[v] : T.tv[v]) ? sc[v] * scale_log2 : -INFINITY;
   float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
@@ -260,12 +271,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int m = 0; m < kTilesInFlight; ++m) {
       const int ti = r0 + kAttnWaves * m;
-      if (ti < nt) load_tile(T[m], 4 * ti, nslot, s_sel, s_page, L, kc, vc, Hkv, g, i16, q4);
+      if (ti < nt) load_tile<false>(T[m], 4 * ti, nslot, s_sel, s_page, nullptr, L, L, 0, kc, vc, Hkv, g, i16, q4);
     }
 #pragma unroll
     for (int m = 0; m < kTilesInFlight; ++m) {
       const int ti = r0 + kAttnWaves * m;
-      if (ti < nt) attend_tile(T[m], qa, scale_log2, m_run, l_run, acc);
+      if (ti < nt) attend_tile<false>(T[m], qa, scale_log2, m_run, l_run, acc);
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -305,6 +316,247 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
   }
 }
 
+// Exclusive prefix sum of one value per thread over the workgroup, with the total in *tot.
+// Every thread must reach it; s_tmp holds kAttnWaves ints.
+__device__ __forceinline__ int block_scan(int x, int* s_tmp, int* tot) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(x);
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) {
+    const int v = s_tmp[w];
+    before += w < wave ? v : 0;
+    all += v;
+  }
+  __syncthreads();
+  *tot = all;
+  return before + inc - x;
+}
+
+// Number of entries of the ascending array a[0, n) below v.
+__device__ __forceinline__ int lower_bound_lds(const int* a, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Chunks of new tokens with 8 query heads per KV head: new tokens 2m and 2m+1 of a request
+// (virtual requests b*T + 2m and b*T + 2m + 1) share one workgroup per (KV head, slice, share).
+// The 16 MFMA columns of the single-token kernel, half of them empty at a group of 8, hold
+// the two tokens' heads (column i16: token i16/8, head i16%8), and the kernel gathers the
+// union of the two tokens' kept blocks inside the slice once: each block is marked with the
+// tokens that keep it, and a column's scores are -inf on the blocks its token does not keep
+// or past its length. A block kept by both tokens is read once instead of twice; with
+// unrelated selections the union is the two lists side by side and the work is the same as
+// two single-token workgroups'. Each token's slice is its own (its page count can differ by
+// one from its neighbour's). The share partials written are exactly the single-token
+// kernel's, per virtual request. Grid (C * Hkv * ceil(T/2), P, B_req).
+__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int Hq, int Hkv,
+    int max_pages, int k, int P, int C, int T, float scale_log2, float* __restrict__ sub_out,
+    float* __restrict__ sub_lse) {
+  constexpr int G = 8;   // query heads per KV head
+  const int gc = blockIdx.x % (C * Hkv), m = blockIdx.x / (C * Hkv);
+  const int g = gc / C, c = gc - g * C, p = blockIdx.y, breq = blockIdx.z;
+  const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
+  const int i16 = lane & 15, q4 = lane >> 4;
+  const int ntok = min(2, T - 2 * m);   // 1 for the last token of an odd chunk
+  const int vr0 = breq * T + 2 * m;
+  int jraw[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int slot = t + kAttnThreads * r;
+      jraw[i][r] = i < ntok && slot < k ? sel[(size_t)(vr0 + i) * k + slot] : 0;
+    }
+  int Lt[2], Kt[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    Lt[i] = i < ntok ? draft_length(lens, vr0 + i, T) : 0;
+    Kt[i] = i < ntok ? sel_count[vr0 + i] : 0;
+  }
+  const int32_t* ptab = page_table + (size_t)breq * max_pages;
+
+  __shared__ int s_cnt[kAttnWaves][2][2];
+  __shared__ int s_tmp[kAttnWaves];
+  __shared__ int s_run[2][kMaxK];       // each token's kept ids inside its slice p
+  __shared__ int s_runp[2][kMaxK];      // and their pages
+  __shared__ int s_sel[2 * kMaxK];      // the share's part of the union of the two runs
+  __shared__ int s_page[2 * kMaxK];
+  __shared__ int s_mask[2 * kMaxK];     // bit i: token i keeps the block
+  __shared__ float s_m[kAttnWaves][kMaxGroup];
+  __shared__ float s_l[kAttnWaves][kMaxGroup];
+  __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim + 4];
+
+  int jr[2][2], pr[2][2];
+  bool inr[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int npages = (Lt[i] + kPageSize - 1) / kPageSize;
+    const int S = (npages + P - 1) / P;
+    const int pg0 = min(p * S, npages), pg1 = min((p + 1) * S, npages);
+    int nbefore = 0, ninside = 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int slot = t + kAttnThreads * r;
+      const bool valid = slot < Kt[i];
+      const int j = valid ? jraw[i][r] : 0;
+      const int pg = j / kBlocksPerPage;
+      inr[i][r] = valid && pg >= pg0 && pg < pg1;
+      jr[i][r] = j;
+      pr[i][r] = inr[i][r] ? ptab[pg] : 0;
+      nbefore += __builtin_popcountll(__ballot(valid && pg < pg0));
+      ninside += __builtin_popcountll(__ballot(inr[i][r]));
+    }
+    if (lane == 0) { s_cnt[wave][i][0] = nbefore; s_cnt[wave][i][1] = ninside; }
+  }
+  // Q operand: column i16 = head g*8 + i16%8 of new token i16/8, dims 32s + 8*q4 .. +7.
+  const int tk = i16 >> 3;
+  bf16x8 qa[4];
+  if (tk < ntok) {
+    const uint16_t* qrow = q + ((size_t)(vr0 + tk) * Hq + (size_t)g * G + (i16 & 7)) * kHeadDim + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = bf16x8{};
+  }
+  __syncthreads();
+  int seg0[2] = {0, 0}, nin[2] = {0, 0};
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) { seg0[i] += s_cnt[w][i][0]; nin[i] += s_cnt[w][i][1]; }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int ls = t + kAttnThreads * r - seg0[i];
+      if (inr[i][r]) { s_run[i][ls] = jr[i][r]; s_runp[i][ls] = pr[i][r]; }
+    }
+  __syncthreads();
+
+  // Union of the two ascending runs. Entry ls of run i lands at ls + (number of entries of
+  // the other run below it) - (number of entries before it that both runs hold); an entry of
+  // run 1 that run 0 also holds is not placed again (run 0's copy carries both bits).
+  int lb[2][2];
+  bool both[2][2];
+  int pref[2][2], nboth = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int run_tot = 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int ls = t + kAttnThreads * r;
+      lb[i][r] = 0;
+      both[i][r] = false;
+      if (ls < nin[i]) {
+        const int id = s_run[i][ls];
+        lb[i][r] = lower_bound_lds(s_run[1 - i], nin[1 - i], id);
+        both[i][r] = lb[i][r] < nin[1 - i] && s_run[1 - i][lb[i][r]] == id;
+      }
+      int tot;
+      pref[i][r] = run_tot + block_scan(both[i][r] ? 1 : 0, s_tmp, &tot);
+      run_tot += tot;
+    }
+    if (i == 0) nboth = run_tot;
+  }
+  const int nU = nin[0] + nin[1] - nboth;
+  const int ntiles = (nU + 3) / 4;
+  const int tps = (ntiles + C - 1) / C;            // tiles per share
+  const int tile0 = min(c * tps, ntiles), nt = min(tile0 + tps, ntiles) - tile0;
+  const int slot0 = 4 * tile0, nslot = min(4 * (tile0 + nt), nU) - slot0;
+
+  if (nt == 0) {   // empty share for both tokens
+    for (int i = t; i < ntok * G * 32; i += kAttnThreads) {
+      const int tt = i / (G * 32), h = (i >> 5) % G, d4 = i & 31;
+      const size_t share = ((size_t)(vr0 + tt) * P + p) * C + c;
+      *reinterpret_cast<f32x4*>(sub_out + (share * Hq + (size_t)g * G + h) * kHeadDim + 4 * d4) =
+          f32x4{0.f, 0.f, 0.f, 0.f};
+      if (d4 == 0) sub_lse[share * Hq + (size_t)g * G + h] = -INFINITY;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int ls = t + kAttnThreads * r;
+      if (ls < nin[i] && !(i == 1 && both[i][r])) {
+        const int u = ls + lb[i][r] - pref[i][r] - slot0;
+        if (u >= 0 && u < nslot) {
+          s_sel[u] = s_run[i][ls];
+          s_page[u] = s_runp[i][ls];
+          s_mask[u] = i == 0 ? (both[i][r] ? 3 : 1) : 2;
+        }
+      }
+    }
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int Lmax = max(Lt[0], Lt[1]), Lc = Lt[tk];
+  for (int r0 = wave; r0 < nt; r0 += kAttnWaves * kTilesInFlight) {
+    Tile Ts[kTilesInFlight];
+#pragma unroll
+    for (int mm = 0; mm < kTilesInFlight; ++mm) {
+      const int ti = r0 + kAttnWaves * mm;
+      if (ti < nt)
+        load_tile<true>(Ts[mm], 4 * ti, nslot, s_sel, s_page, s_mask, Lmax, Lc, tk, kc, vc, Hkv, g, i16, q4);
+    }
+#pragma unroll
+    for (int mm = 0; mm < kTilesInFlight; ++mm) {
+      const int ti = r0 + kAttnWaves * mm;
+      if (ti < nt) attend_tile<true>(Ts[mm], qa, scale_log2, m_run, l_run, acc);
+    }
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+
+  // Merge of the 4 wave partials, as in the single-token kernel, over the 16 columns.
+  if (q4 == 0) { s_m[wave][i16] = m_run; s_l[wave][i16] = l_tot; }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_o[wave][i16][8 * (4 * q4 + r) + u] = acc[u][r];
+  __syncthreads();
+  const int h = t >> 4, d0 = 8 * (t & 15), th = h >> 3;
+  if (th < ntok) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float l = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = exp2f(s_m[w][h] - Mu);
+      l += s_l[w][h] * f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += s_o[w][h][d0 + e] * f;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t share = ((size_t)(vr0 + th) * P + p) * C + c;
+    const int hg = g * G + (h & 7);
+    float* dst = sub_out + (share * Hq + hg) * kHeadDim + d0;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+    if (d0 == 0)
+      sub_lse[share * Hq + hg] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
 size_t attn_sub_out_bytes(int B, int Hq, int Hkv, int P) {
   return align256((size_t)B * P * attn_split(B, Hkv, P) * Hq * kHeadDim * sizeof(float));
 }
@@ -329,10 +581,17 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
   float* sub_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn_sub_out_bytes(B, Hq, Hkv, P));
   const float scale_log2 = scale * 1.4426950408889634f;
   if ((long long)C * Hkv * T > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (T >= kPairMinTokens && Hq == 8 * Hkv) {
+    hipLaunchKernelGGL(sparse_attn_pair_kernel, dim3(C * Hkv * ((T + 1) / 2), P, B / T), dim3(kAttnThreads), 0,
+                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                       static_cast<const uint16_t*>(vc), page_table, lens, sel, sel_count, Hq, Hkv, max_pages, k,
+                       P, C, T, scale_log2, sub_out, sub_lse);
+  } else {
   hipLaunchKernelGGL(sparse_attn_kernel, dim3(C * Hkv * T, P, B / T), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), page_table, lens, sel, sel_count, Hq, Hkv,
                      max_pages, k, P, C, T, scale_log2, sub_out, sub_lse);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_slice_merge(sub_out, sub_lse, B, P, C, Hq, part_out, part_lse, out, out_lse, stream);

@@ -215,20 +215,31 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> DecodeInputs:
         lengths=lens, planted=planted)
 
 
-def draft_queries(x: DecodeInputs, T: int, seed: int = 0):
+def draft_queries(x: DecodeInputs, T: int, seed: int = 0, spread: int | None = None):
     """Queries of T draft tokens per request: (q [B, T, Hq, 128] bf16, q_idx [B, T, 4, 64] int8),
     drawn like the single query (bf16 of N(0,1); indexer values from the workload's alphabet)
-    from one generator per request."""
+    from one generator per request, independently for every token.
+
+    spread = d (correlated chunk queries): token t's indexer query is instead the request's own
+    query x.q_idx[b] plus an offset drawn uniformly from {-d..d} per element, clipped to the
+    alphabet's range, so the tokens of a chunk select overlapping block sets (d = 0: all the
+    same query). The attention queries stay independent."""
     w = x.workload
     device = x.q.device
     B = x.batch
     q = torch.empty((B, T, w.hq, HEAD_DIM), dtype=torch.bfloat16, device=device)
     q_idx = torch.empty((B, T, IDX_HEADS, IDX_DIM), dtype=torch.int8, device=device)
     alphabet = "u127" if w.alphabet == "zero_q" else w.alphabet
+    lo, hi = (-2, 2) if alphabet == "u2" else (-127, 127)
     for b in range(B):
         g = _gen(device, _request_seed(seed ^ 0x7D1F, b))
         q[b] = torch.randn((T, w.hq, HEAD_DIM), generator=g, device=device).to(torch.bfloat16)
-        qi = _int_values((T, IDX_HEADS, IDX_DIM), alphabet, g, device)
+        if spread is None:
+            qi = _int_values((T, IDX_HEADS, IDX_DIM), alphabet, g, device)
+        else:
+            off = torch.randint(-spread, spread + 1, (T, IDX_HEADS, IDX_DIM), generator=g, device=device,
+                                dtype=torch.int16)
+            qi = (x.q_idx[b].to(torch.int16)[None] + off).clamp_(lo, hi).to(torch.int8)
         if w.alphabet == "zero_q":
             qi.zero_()
         q_idx[b] = qi

@@ -148,6 +148,34 @@ def test_many_queries_match_oracle(T, lens):
             check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"T{T} b{b} t{t}")
 
 
+@pytest.mark.parametrize("T,spread,P,gqa", [(16, 0, 2, (32, 4)), (17, 4, 3, (16, 2)), (33, 16, 1, (8, 1)),
+                                             (64, 2, 4, (32, 4)), (20, None, 2, (16, 2))])
+def test_chunk_pairs_with_overlapping_selections(T, spread, P, gqa):
+    """Chunks of 16 or more new tokens at 8 query heads per KV head run the pair kernel (two
+    neighbouring tokens gather the union of their kept blocks once). With correlated chunk
+    queries (spread d) neighbours keep mostly the same blocks, so most union entries carry
+    both tokens; with d = 0 all tokens share one indexer query. Every (request, token)
+    against the oracle, odd T (a last token without a partner) included."""
+    hq, hkv = gqa
+    lens = (70, 2049, 5000, 12000)
+    x = make_inputs(Workload("pair", len(lens), ("list",) + lens, hq, hkv, P), 60 + T, "cuda")
+    q, qi = draft_queries(x, T, 60 + T, spread=spread)
+    say(f"[pairs T={T} spread={spread} P={P} Hq/Hkv={hq}/{hkv}] lens={lens}")
+    _, g = _run(x, q, qi, P)
+    a = oracle_arrays(x)
+    refs = oracle.decode_multi(bf16_bits(q), qi.cpu().numpy(), a["idx_cache"], a["k_cache"], a["v_cache"],
+                               a["page_table"], a["lengths"], T, P, x.scale)
+    shared = []
+    for b, L in enumerate(lens):
+        for t in range(T):
+            r = b * T + t
+            check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"pairs T{T} b{b} t{t}")
+            if t % 2 == 1 and len(refs[r]["kept"]) == 512:
+                shared.append(len(np.intersect1d(refs[r - 1]["kept"], refs[r]["kept"])) / 512)
+    if spread is not None and spread <= 4:
+        assert np.mean(shared) > 0.5, f"neighbouring tokens share only {np.mean(shared):.2f} of their blocks"
+
+
 def test_prefill_chunk_1024_tokens():
     """A prefill chunk: the last 1024 tokens of an 8192-token request; sampled tokens against
     the oracle, every token's selection against the single-token decode at its length."""

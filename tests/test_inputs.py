@@ -1,7 +1,7 @@
 """The seeded input generator: determinism, shapes, the length laws and the poison rows."""
 import torch
 
-from sparse_attention_decode_qsa_amd.inputs import (PAGE_SIZE, WORKLOADS, Workload, draw_lengths,
+from sparse_attention_decode_qsa_amd.inputs import (PAGE_SIZE, WORKLOADS, Workload, draft_queries, draw_lengths,
                                                     make_inputs, request_subset)
 
 
@@ -68,3 +68,21 @@ def test_request_subset_keeps_request_content():
             assert torch.equal(x.idx_cache[p_old, t % PAGE_SIZE], s.idx_cache[p_new, t % PAGE_SIZE])
             assert torch.equal(x.k_cache[p_old, t % PAGE_SIZE].view(torch.int16),
                                s.k_cache[p_new, t % PAGE_SIZE].view(torch.int16))
+
+
+def test_correlated_chunk_queries():
+    """spread = d: every new token's indexer query is the request's own query plus an offset
+    in {-d..d}, clipped to the alphabet; d = 0 repeats the request's query; the attention
+    queries are the independent ones either way."""
+    for alphabet, lim in (("u127", 127), ("u2", 2)):
+        x = make_inputs(Workload("cq", 2, ("list", 300, 70), 16, 2, 1, alphabet=alphabet), 3, "cpu")
+        q_ind, qi_ind = draft_queries(x, 5, 9)
+        q0, qi0 = draft_queries(x, 5, 9, spread=0)
+        assert torch.equal(qi0, x.q_idx[:, None].expand(-1, 5, -1, -1))
+        assert torch.equal(q0, q_ind)
+        _, qi3 = draft_queries(x, 5, 9, spread=3)
+        _, qi3b = draft_queries(x, 5, 9, spread=3)
+        assert torch.equal(qi3, qi3b)
+        d = qi3.to(torch.int16) - x.q_idx[:, None].to(torch.int16)
+        assert int(d.abs().max()) <= 3 and int(qi3.abs().max()) <= lim
+        assert bool((d != 0).any()) and not torch.equal(qi3, qi_ind)
