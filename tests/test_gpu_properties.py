@@ -8,7 +8,8 @@ score ties, and an all-zero indexer query where every block ties). Every request
 scores, kept blocks and outputs are compared with the CPU oracle through the C ABI, the
 four separate calls and qsa_decode must agree bit for bit, and the unused rows of each
 request's last page hold poison (NaN K/V, indexer keys 127) that must not reach a result.
-Multi-token decode: up to 3 requests, T from 1 to 8 or 20 new tokens. Wider shapes: up to 6
+Multi-token decode: up to 3 requests, T from 1 to 8 or 16 to 40 new tokens, independent or
+correlated indexer queries. Wider shapes: up to 6
 requests of up to 80,000 tokens, group sizes 16, 3 and 1, up to 64 slices, k below 512 and
 page tables with spare capacity.
 """
@@ -55,16 +56,19 @@ def test_chain_matches_oracle_on_random_shapes(lens, gqa, P, alphabet, seed):
 @settings(max_examples=30, deadline=None, derandomize=True, database=None,
           suppress_health_check=[HealthCheck.too_slow])
 @given(lens=st.lists(st.integers(0, 3000), min_size=1, max_size=3),
-       T=st.one_of(st.integers(1, 8), st.just(20)), gqa=st.sampled_from(GQA), P=st.integers(1, 4),
-       alphabet=st.sampled_from(ALPHABETS), seed=st.integers(0, 2**16))
-def test_multi_token_matches_oracle_on_random_shapes(lens, T, gqa, P, alphabet, seed):
-    """Several new tokens per request (T <= 4 on the per-query scan, 5..8 and 20 on the
-    matrix-core scan): every (request, token) against the oracle's causal reading."""
+       T=st.one_of(st.integers(1, 8), st.integers(16, 40)), gqa=st.sampled_from(GQA), P=st.integers(1, 4),
+       alphabet=st.sampled_from(ALPHABETS), spread=st.sampled_from([None, None, 0, 3, 20]),
+       seed=st.integers(0, 2**16))
+def test_multi_token_matches_oracle_on_random_shapes(lens, T, gqa, P, alphabet, spread, seed):
+    """Several new tokens per request (T <= 4 on the per-query scan, 5..8 and 16..40 on the
+    matrix-core scan, 16..40 with neighbouring tokens paired in the attention), with
+    independent or correlated indexer queries: every (request, token) against the oracle's
+    causal reading."""
     hq, hkv = gqa
     w = Workload("propm", len(lens), ("list",) + tuple(lens), hq, hkv, P, alphabet=alphabet)
     x = make_inputs(w, seed, "cuda")
-    q, qi = draft_queries(x, T, seed)
-    say(f"[prop multi] lens={lens} T={T} Hq/Hkv={hq}/{hkv} P={P} alphabet={alphabet} seed={seed}")
+    q, qi = draft_queries(x, T, seed, spread=spread)
+    say(f"[prop multi] lens={lens} T={T} Hq/Hkv={hq}/{hkv} P={P} alphabet={alphabet} spread={spread} seed={seed}")
     _, g = run_multi(x, q, qi, P)
     a = oracle_arrays(x)
     refs = oracle.decode_multi(bf16_bits(q), qi.cpu().numpy(), a["idx_cache"], a["k_cache"], a["v_cache"],
