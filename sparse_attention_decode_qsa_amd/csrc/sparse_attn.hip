@@ -20,7 +20,8 @@
 // Inside a workgroup: every thread reads two kept slots (loaded together with sel_count and
 // the length), counts (by wave ballots) the slots before and inside the slice and, for a
 // slot inside, loads its physical page at once, so the only dependent global loads before
-// the K/V rows are the ids and the page-table entries. The share's ids and pages go to LDS; tiles are dealt round-robin to the waves;
+// the K/V rows are the ids and the page-table entries. The share's ids and the physical rows
+// of their blocks' first tokens go to LDS; tiles are dealt round-robin to the waves;
 // a wave issues the loads of up to kTilesInFlight tiles before it computes on the first,
 // and keeps an online softmax over its tiles. The 4 wave partials are merged in one LDS
 // round, each thread finishing 8 output dims of one query head.
@@ -64,9 +65,12 @@ int attn_split(int B, int Hkv, int P) {
   return c;
 }
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs only (here 0 <= f <= 1)
+// Two floats to a packed bf16 pair (lo in bits 0-15), round to nearest even, in one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xFFFFu) | (hi16 << 16); }
@@ -79,19 +83,21 @@ struct Tile {
 };
 
 // Tile of 4 kept blocks starting at share slot bbase (share slots [0, nslot)); block ids and
-// their page ids come from LDS. Rows at or past L are not loaded. PAIR: the lane's column
+// the physical rows of their first tokens (page * 64 + row, below 2^32 for any cache that fits
+// in memory) come from LDS. kg and vg point at the lane's 16 bytes of row 0 of the caches
+// (KV head g; dims 8*q4 for K, 8*i16 for V), rs is the row stride in elements. Rows at or
+// past L are not loaded. PAIR: the lane's column
 // belongs to new token tk of a pair, of length Lc <= L, which keeps a block of the share
 // when bit tk of its s_mask entry is set.
 template <bool PAIR>
-__device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const int* s_sel, const int* s_page,
-                                          const int* s_mask, int L, int Lc, int tk, const uint16_t* kc,
-                                          const uint16_t* vc, int Hkv, int g, int i16, int q4) {
+__device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const int* s_sel, const uint32_t* s_ptok,
+                                          const int* s_mask, int L, int Lc, int tk, const uint16_t* kg,
+                                          const uint16_t* vg, uint32_t rs, int i16, int q4) {
   {
     const int slot = bbase + (i16 >> 2);
     const int tok = slot < nslot ? 4 * s_sel[slot] + (i16 & 3) : L;
     if (tok < L) {
-      const int page = s_page[slot];
-      const uint16_t* krow = kc + (((size_t)page * kPageSize + (tok & 63)) * Hkv + g) * kHeadDim + 8 * q4;
+      const uint16_t* krow = kg + (size_t)(s_ptok[slot] + (i16 & 3)) * rs;
 #pragma unroll
       for (int s = 0; s < 4; ++s) T.k[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
     } else {
@@ -101,13 +107,13 @@ __device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const i
   }
   const int slot = bbase + q4;
   const int blk = slot < nslot ? s_sel[slot] : -1;
-  const int page = blk >= 0 ? s_page[slot] : 0;
+  const uint32_t row0 = blk >= 0 ? s_ptok[slot] : 0u;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int tok = 4 * blk + v;
     T.tv[v] = blk >= 0 && tok < L;
     if (T.tv[v]) {
-      const uint16_t* vrow = vc + (((size_t)page * kPageSize + (tok & 63)) * Hkv + g) * kHeadDim + 8 * i16;
+      const uint16_t* vrow = vg + (size_t)(row0 + v) * rs;
       T.v[v] = *reinterpret_cast<const u16x8*>(vrow);
     } else {
       T.v[v] = u16x8{};
@@ -135,27 +141,31 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
   const float m_new = fmaxf(m_run, mt);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = exp2f(m_run - m_use);
-  float pv[4];
-  uint32_t ph[4], pl[4];
+  // The state is rescaled only when some lane's maximum moved (a wave-uniform branch):
+  // otherwise the factor is exp2(0) = 1 exactly and the multiplications would change no bit.
+  if (__ballot(m_new != m_run)) {
+    const float alpha = exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+    l_run *= alpha;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    pv[v] = exp2f(sv[v] - m_use);
-    ph[v] = bf16_bits_rne(pv[v]);
-    pl[v] = bf16_bits_rne(pv[v] - __uint_as_float(ph[v] << 16));
+    for (int u = 0; u < 8; ++u) acc[u] *= alpha;
+    m_run = m_new;
   }
-  l_run = l_run * alpha + (pv[0] + pv[1]) + (pv[2] + pv[3]);
-  m_run = m_new;
-
+  const float m_use = m_run == -INFINITY ? 0.f : m_run;
+  // p = 2^(s - m) <= 1 on v_exp_f32; P enters the PV product as a bf16 pair (hi = bf16(p),
+  // lo = bf16(p - hi)), so the weights keep ~16 bits.
+  float pv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) pv[v] = __builtin_amdgcn_exp2f(sv[v] - m_use);
+  l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
   union { uint32_t w[4]; bf16x8 v; } bp;
-  bp.w[0] = pack2(ph[0], ph[1]);
-  bp.w[1] = pack2(ph[2], ph[3]);
-  bp.w[2] = pack2(pl[0], pl[1]);
-  bp.w[3] = pack2(pl[2], pl[3]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    bp.w[i] = cvt_bf16x2(pv[2 * i], pv[2 * i + 1]);
+    bp.w[2 + i] = cvt_bf16x2(pv[2 * i] - __uint_as_float(bp.w[i] << 16),
+                             pv[2 * i + 1] - __uint_as_float(bp.w[i] & 0xFFFF0000u));
+  }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    acc[u] *= alpha;
     union { uint32_t w[4]; bf16x8 v; } va;
     va.w[0] = pack2(T.v[0][u], T.v[1][u]);
     va.w[1] = pack2(T.v[2][u], T.v[3][u]);
@@ -200,7 +210,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 
   __shared__ int s_cnt[kAttnWaves][2];
   __shared__ int s_sel[kMaxK];      // kept block ids of the share
-  __shared__ int s_page[kMaxK];     // and their physical pages
+  __shared__ uint32_t s_ptok[kMaxK];   // and the physical rows of their first tokens
   __shared__ float s_m[kAttnWaves][kMaxGroup];
   __shared__ float s_l[kAttnWaves][kMaxGroup];
   __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim + 4];
@@ -209,8 +219,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
   const int S = (npages + P - 1) / P;
   const int pg0 = min(p * S, npages), pg1 = min((p + 1) * S, npages);
 
-  // Kept slots t and t + 256: block id, position relative to the slice, page if inside.
-  int jr[2], pr[2];
+  // Kept slots t and t + 256: block id, position relative to the slice, physical row of the
+  // block's first token if inside.
+  int jr[2];
+  uint32_t pr[2];
   bool inr[2];
   int nbefore = 0, ninside = 0;
 #pragma unroll
@@ -221,7 +233,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     const int pg = j / kBlocksPerPage;
     inr[r] = valid && pg >= pg0 && pg < pg1;
     jr[r] = j;
-    pr[r] = inr[r] ? ptab[pg] : 0;
+    pr[r] = inr[r] ? (uint32_t)ptab[pg] * kPageSize + kTokensPerBlock * (j % kBlocksPerPage) : 0u;
     nbefore += __builtin_popcountll(__ballot(valid && pg < pg0));
     ninside += __builtin_popcountll(__ballot(inr[r]));
   }
@@ -257,10 +269,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int ls = t + kAttnThreads * r - seg0 - slot0;
-    if (inr[r] && ls >= 0 && ls < nslot) { s_sel[ls] = jr[r]; s_page[ls] = pr[r]; }
+    if (inr[r] && ls >= 0 && ls < nslot) { s_sel[ls] = jr[r]; s_ptok[ls] = pr[r]; }
   }
   __syncthreads();
 
+  const uint16_t* kg = kc + (size_t)g * kHeadDim + 8 * q4;
+  const uint16_t* vg = vc + (size_t)g * kHeadDim + 8 * i16;
+  const uint32_t rs = (uint32_t)Hkv * kHeadDim;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[8];
 #pragma unroll
@@ -271,7 +286,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int m = 0; m < kTilesInFlight; ++m) {
       const int ti = r0 + kAttnWaves * m;
-      if (ti < nt) load_tile<false>(T[m], 4 * ti, nslot, s_sel, s_page, nullptr, L, L, 0, kc, vc, Hkv, g, i16, q4);
+      if (ti < nt) load_tile<false>(T[m], 4 * ti, nslot, s_sel, s_ptok, nullptr, L, L, 0, kg, vg, rs, i16, q4);
     }
 #pragma unroll
     for (int m = 0; m < kTilesInFlight; ++m) {
@@ -388,15 +403,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
   __shared__ int s_cnt[kAttnWaves][2][2];
   __shared__ int s_tmp[kAttnWaves];
   __shared__ int s_run[2][kMaxK];       // each token's kept ids inside its slice p
-  __shared__ int s_runp[2][kMaxK];      // and their pages
+  __shared__ uint32_t s_runp[2][kMaxK]; // and the physical rows of their first tokens
   __shared__ int s_sel[2 * kMaxK];      // the share's part of the union of the two runs
-  __shared__ int s_page[2 * kMaxK];
+  __shared__ uint32_t s_ptok[2 * kMaxK];
   __shared__ int s_mask[2 * kMaxK];     // bit i: token i keeps the block
   __shared__ float s_m[kAttnWaves][kMaxGroup];
   __shared__ float s_l[kAttnWaves][kMaxGroup];
   __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim + 4];
 
-  int jr[2][2], pr[2][2];
+  int jr[2][2];
+  uint32_t pr[2][2];
   bool inr[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -412,7 +428,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
       const int pg = j / kBlocksPerPage;
       inr[i][r] = valid && pg >= pg0 && pg < pg1;
       jr[i][r] = j;
-      pr[i][r] = inr[i][r] ? ptab[pg] : 0;
+      pr[i][r] = inr[i][r] ? (uint32_t)ptab[pg] * kPageSize + kTokensPerBlock * (j % kBlocksPerPage) : 0u;
       nbefore += __builtin_popcountll(__ballot(valid && pg < pg0));
       ninside += __builtin_popcountll(__ballot(inr[i][r]));
     }
@@ -494,13 +510,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
         const int u = ls + lb[i][r] - pref[i][r] - slot0;
         if (u >= 0 && u < nslot) {
           s_sel[u] = s_run[i][ls];
-          s_page[u] = s_runp[i][ls];
+          s_ptok[u] = s_runp[i][ls];
           s_mask[u] = i == 0 ? (both[i][r] ? 3 : 1) : 2;
         }
       }
     }
   __syncthreads();
 
+  const uint16_t* kg = kc + (size_t)g * kHeadDim + 8 * q4;
+  const uint16_t* vg = vc + (size_t)g * kHeadDim + 8 * i16;
+  const uint32_t rs = (uint32_t)Hkv * kHeadDim;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[8];
 #pragma unroll
@@ -512,7 +531,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
     for (int mm = 0; mm < kTilesInFlight; ++mm) {
       const int ti = r0 + kAttnWaves * mm;
       if (ti < nt)
-        load_tile<true>(Ts[mm], 4 * ti, nslot, s_sel, s_page, s_mask, Lmax, Lc, tk, kc, vc, Hkv, g, i16, q4);
+        load_tile<true>(Ts[mm], 4 * ti, nslot, s_sel, s_ptok, s_mask, Lmax, Lc, tk, kg, vg, rs, i16, q4);
     }
 #pragma unroll
     for (int mm = 0; mm < kTilesInFlight; ++mm) {
