@@ -17,8 +17,8 @@ pytestmark = pytest.mark.gpu
 LENS = (3, 4, 5, 64, 65, 66, 67, 130, 2049, 9000, 40001)
 
 
-def _run(x, q, qi, P):
-    plan = qsa.MultiDecodePlan(q, qi, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, P)
+def _run(x, q, qi, P, k=512):
+    plan = qsa.MultiDecodePlan(q, qi, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, P, k=k)
     plan.run()
     torch.cuda.synchronize()
     return plan, dict(scores=plan.scores.cpu().numpy(), sel=plan.sel.cpu().numpy(), cnt=plan.sel_count.cpu().numpy(),
@@ -148,30 +148,32 @@ def test_many_queries_match_oracle(T, lens):
             check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"T{T} b{b} t{t}")
 
 
-@pytest.mark.parametrize("T,spread,P,gqa", [(16, 0, 2, (32, 4)), (17, 4, 3, (16, 2)), (33, 16, 1, (8, 1)),
-                                             (64, 2, 4, (32, 4)), (20, None, 2, (16, 2))])
-def test_chunk_pairs_with_overlapping_selections(T, spread, P, gqa):
+@pytest.mark.parametrize("T,spread,P,gqa,k", [(16, 0, 2, (32, 4), 512), (17, 4, 3, (16, 2), 512),
+                                               (33, 16, 1, (8, 1), 512), (64, 2, 4, (32, 4), 512),
+                                               (20, None, 2, (16, 2), 512), (18, 4, 2, (32, 4), 100),
+                                               (21, 1, 5, (16, 2), 511)])
+def test_chunk_pairs_with_overlapping_selections(T, spread, P, gqa, k):
     """Chunks of 16 or more new tokens at 8 query heads per KV head run the pair kernel (two
     neighbouring tokens gather the union of their kept blocks once). With correlated chunk
     queries (spread d) neighbours keep mostly the same blocks, so most union entries carry
     both tokens; with d = 0 all tokens share one indexer query. Every (request, token)
-    against the oracle, odd T (a last token without a partner) included."""
+    against the oracle, odd T (a last token without a partner) and k below 512 included."""
     hq, hkv = gqa
     lens = (70, 2049, 5000, 12000)
     x = make_inputs(Workload("pair", len(lens), ("list",) + lens, hq, hkv, P), 60 + T, "cuda")
     q, qi = draft_queries(x, T, 60 + T, spread=spread)
-    say(f"[pairs T={T} spread={spread} P={P} Hq/Hkv={hq}/{hkv}] lens={lens}")
-    _, g = _run(x, q, qi, P)
+    say(f"[pairs T={T} spread={spread} P={P} Hq/Hkv={hq}/{hkv} k={k}] lens={lens}")
+    _, g = _run(x, q, qi, P, k)
     a = oracle_arrays(x)
     refs = oracle.decode_multi(bf16_bits(q), qi.cpu().numpy(), a["idx_cache"], a["k_cache"], a["v_cache"],
-                               a["page_table"], a["lengths"], T, P, x.scale)
+                               a["page_table"], a["lengths"], T, P, x.scale, k)
     shared = []
     for b, L in enumerate(lens):
         for t in range(T):
             r = b * T + t
-            check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"pairs T{T} b{b} t{t}")
-            if t % 2 == 1 and len(refs[r]["kept"]) == 512:
-                shared.append(len(np.intersect1d(refs[r - 1]["kept"], refs[r]["kept"])) / 512)
+            check_request(g, r, refs[r], oracle.draft_length(L, T, t), k, what=f"pairs T{T} b{b} t{t}")
+            if t % 2 == 1 and len(refs[r]["kept"]) == k:
+                shared.append(len(np.intersect1d(refs[r - 1]["kept"], refs[r]["kept"])) / k)
     if spread is not None and spread <= 4:
         assert np.mean(shared) > 0.5, f"neighbouring tokens share only {np.mean(shared):.2f} of their blocks"
 
