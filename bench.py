@@ -228,7 +228,12 @@ def main():
         x = make_inputs(wl, args.seed + 1000 * r, dev)
         inputs.append(x)
         side = None
-        if args.pooled:
+        if args.pooled and args.draft > 1:
+            if args.draft > 4:
+                raise SystemExit("--pooled takes at most 4 draft tokens (--draft 1..4)")
+            side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens)   # pools the draft rows too
+            pooled.append(side)
+        elif args.pooled:
             # the side cache as prefill leaves it, and the step's new rows = the rows at L-1 (so
             # every call rewrites the same values and the inputs stay fixed)
             side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens)
@@ -241,15 +246,13 @@ def main():
                 appends.append(qsa.AppendPlan(k_new, v_new, i_new, x.k_cache, x.v_cache, x.idx_cache,
                                               x.page_table, x.context_lens, pooled=side))
             pooled.append(side)
-        if args.pooled and not args.separate_append:
+        if args.pooled and args.draft == 1 and not args.separate_append:
             plans.append(qsa.StepPlan(k_new, v_new, i_new, x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache,
                                       x.page_table, x.context_lens, side, w.slices))
         elif args.draft > 1:
-            if args.pooled:
-                raise SystemExit("--draft and --pooled do not combine")
             dq, dqi = draft_queries(x, args.draft, args.seed + 1000 * r, spread=args.spread)
             plans.append(qsa.MultiDecodePlan(dq, dqi, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
-                                             x.context_lens, w.slices))
+                                             x.context_lens, w.slices, pooled=side))
         else:
             plans.append(qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table,
                                         x.context_lens, w.slices, pooled=side))
@@ -309,7 +312,9 @@ def main():
     # start and end (kernel timestamps, as a kernel trace takes them; no marker packets in the
     # chain), on the stream it runs on. Every call of this pass is a whole qsa_decode call.
     k_iters = max(args.steps, 100)
-    in_call_timing = args.draft == 1 and not args.graph   # int8 or side-cache scan inside whole calls
+    # int8 or side-cache scan inside whole calls (draft tokens on the side cache too: that scan has
+    # no entry point of its own)
+    in_call_timing = (args.draft == 1 or args.pooled) and not args.graph
     if in_call_timing:
         marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k_iters)]
         for a, b in marks:               # torch creates an event at its first record
@@ -378,12 +383,15 @@ def main():
     algo += T_exact * w.hkv * 512 - sum(min(4 * min(512, (L + 3) // 4), L) for L in lengths) * w.hkv * 512
     k1_bytes = index_bytes(lengths) + (D - 1) * sum(256 + 4 * ((L + 3) // 4) for L in lengths)
     if args.pooled:
-        # the scan reads 512 B per block instead of 256 B per token; the append writes the K/V
-        # rows (2*Hkv*256 B), the indexer row (256 B) and one side-cache entry (512 B) per request
-        # and reads up to 3 earlier indexer rows
+        # the scan reads 512 B per block instead of 256 B per token (with draft tokens, the one or
+        # two pages holding draft positions are read as int8 rows instead: traffic, not counted
+        # here); the single-token step's append writes the K/V rows (2*Hkv*256 B), the indexer
+        # row (256 B) and one side-cache entry (512 B) per request and reads up to 3 earlier
+        # indexer rows
         pooled_keys = sum(512 * ((L + 3) // 4) for L in lengths)
         algo += pooled_keys - IDX_TOKEN_BYTES * sum(lengths)
-        algo += sum(2 * w.hkv * 256 + 256 + 512 + 256 * ((L - 1) % 4) for L in lengths if L)
+        if D == 1:
+            algo += sum(2 * w.hkv * 256 + 256 + 512 + 256 * ((L - 1) % 4) for L in lengths if L)
         k1_bytes += pooled_keys - IDX_TOKEN_BYTES * sum(lengths)
     gbs = algo / (ms_step * 1e-3) / 1e9
     # With more than 4 new tokens per request the scan is an int8 matrix product on the matrix
@@ -420,7 +428,8 @@ def main():
             "parallelism": f"1 GPU, P={w.slices} slices merged by LSE",
             "rotated_input_sets": sets,
             "launch": ("hip graph replay" if args.graph else "stream launches") +
-                      ((" (qsa_cache_append + qsa_decode_pooled per call)" if args.separate_append else
+                      (f" (qsa_decode_multi_pooled, T={D}, per call)" if args.pooled and D > 1 else
+                       (" (qsa_cache_append + qsa_decode_pooled per call)" if args.separate_append else
                         " (qsa_decode_step_pooled: cache writes in the scan, per call)") if args.pooled else
                        f" (qsa_decode_multi, T={D}, per call)" if D > 1 else " (qsa_decode per call)"),
             "indexer_keys": "pooled int16 side cache" if args.pooled else "int8 per token, pooled in the scan",
@@ -435,7 +444,9 @@ def main():
         "read_ceiling_GBps": round(read_gbs, 1),
         "algorithmic_bytes_per_call": algo,
         "roofline": (mq_roofline(scan_ops, k1_bytes, ms_k1, D) if D > 4 else {
-            "kernel": ("index_score_pooled_kernel (side-cache scan + scores)" if args.pooled
+            "kernel": (f"index_score_pooled_multi_kernel<T={D}> (side-cache scan + scores of {D} draft tokens)"
+                       if args.pooled and D > 1
+                       else "index_score_pooled_kernel (side-cache scan + scores)" if args.pooled
                        else f"index_score_kernel<T={D}> (indexer scan + pooling + scores of {D} draft tokens)"
                        if D > 1 else "index_score_kernel (indexer scan + pooling + scores)"),
             "bound": "hbm",
@@ -447,7 +458,8 @@ def main():
             "frac_of_read_ceiling": round(k1_gbs / read_gbs, 4),
             "avg_launch_us": round(ms_k1 * 1000, 3),
             "bytes_per_launch": k1_bytes,
-            "timing": (("inside whole qsa_decode_step_pooled calls" if args.pooled else "inside whole qsa_decode calls")
+            "timing": (("inside whole qsa_decode_multi_pooled calls" if args.pooled and D > 1
+                        else "inside whole qsa_decode_step_pooled calls" if args.pooled else "inside whole qsa_decode calls")
                        + ": events recorded at the scan kernel's own start and end (qsa_time_next_scan)"
                        if in_call_timing else "the scan alone, back to back"),
         }),

@@ -16,8 +16,8 @@
  * One decode step of one QSA layer is the chain
  *     qsa_index_score -> qsa_topk_select -> qsa_sparse_attn_decode -> qsa_lse_merge
  * (or qsa_decode, which runs the four on one stream). The indexer's side cache of pooled keys
- * (qsa_pool_build, qsa_cache_append, qsa_index_score_pooled, qsa_decode_pooled) gives the
- * same chain with a scan that reads half the bytes.
+ * (qsa_pool_build, qsa_cache_append, qsa_index_score_pooled, qsa_decode_pooled,
+ * qsa_decode_multi_pooled) gives the same chain with a scan that reads half the bytes.
  *
  * Conventions for every entry point
  *   Memory     every pointer is device memory of the current HIP device, unless noted.
@@ -215,8 +215,8 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
 /*
  * qsa_time_next_scan - measurement hook. The next launch of an indexer scan kernel made by
  * this thread (through qsa_index_score, qsa_decode, qsa_decode_noalloc, qsa_decode_multi
- * with T <= 4, or the side-cache scan of qsa_index_score_pooled, qsa_decode_pooled and
- * qsa_decode_step_pooled) records start_event when the kernel begins executing and stop_event when it
+ * with T <= 4, or the side-cache scan of qsa_index_score_pooled, qsa_decode_pooled,
+ * qsa_decode_multi_pooled and qsa_decode_step_pooled) records start_event when the kernel begins executing and stop_event when it
  * ends (both hipEvent_t created with timing enabled, either may be NULL), so the kernel's own
  * duration can be read with hipEventElapsedTime, inside a chain, without marker packets
  * around it. Used once, then cleared; NULL, NULL clears it. Always returns QSA_OK.
@@ -353,6 +353,26 @@ qsa_status_t qsa_decode_pooled(const void* q, const int8_t* q_idx, const int16_t
                                int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
                                float* partial_out, float* partial_lse, float* out, float* out_lse,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* qsa_decode_multi with the scan reading the side cache: 2 <= T <= 4 draft tokens per request
+ * (T = 1 is qsa_decode_pooled), the same results bit for bit as qsa_decode_multi. The T draft
+ * tokens' rows are already in all caches, pooled_cache included (its entry for a block holds
+ * the sum of every indexer row of the block below context_lens), so the side-cache entries of
+ * the blocks holding draft positions pool keys that earlier draft tokens must not see: the
+ * scan reads those pages (the pages within T-1 tokens of L_b, at most two per request) from
+ * idx_cache instead, token by token, and every other page from pooled_cache. Arguments,
+ * workspace (qsa_decode_multi_workspace_size) and results as qsa_decode_multi, plus
+ * pooled_cache; T > 4 returns QSA_ERR_UNSUPPORTED. */
+qsa_status_t qsa_decode_multi_pooled(const void* q, const int8_t* q_idx, const int8_t* idx_cache,
+                                     const int16_t* pooled_cache, const void* k_cache,
+                                     const void* v_cache, const int32_t* page_table,
+                                     const int32_t* context_lens, int B, int T, int Hq, int Hkv,
+                                     int head_dim, int n_idx_heads, int idx_dim, int page_size,
+                                     int max_pages_per_seq, int max_blocks, int k, int P,
+                                     float softmax_scale, int32_t* block_scores, int32_t* sel_blocks,
+                                     int32_t* sel_count, float* partial_out, float* partial_lse,
+                                     float* out, float* out_lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* One decode step on the side cache: qsa_cache_append (with pooled_cache) followed by
  * qsa_decode_pooled, in one call and with the same results. The cache writes are made by the

@@ -29,7 +29,7 @@ hipError_t launch_cache_append(const void*, const void*, const int8_t*, const in
                                int16_t*, const int32_t*, const int32_t*, int, int, int, hipStream_t);
 hipError_t launch_index_score_pooled(const int8_t*, const int16_t*, const int32_t*, const int32_t*, int, int, int,
                                      int32_t*, int32_t*, const void*, const void*, const int8_t*, const int32_t*,
-                                     void*, void*, int8_t*, int, hipStream_t);
+                                     void*, void*, int8_t*, int, hipStream_t, int T, const int8_t* idx_keys);
 
 namespace {
 
@@ -131,7 +131,7 @@ qsa_status_t qsa_time_next_scan(void* start_event, void* stop_event) {
   return QSA_OK;
 }
 
-int qsa_version(void) { return 200; }   // 0.2.0: side cache, multi-token decode, page check
+int qsa_version(void) { return 210; }   // 0.2.1: multi-token decode over the side cache
 
 qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
                              const int32_t* context_lens, int B, int n_idx_heads, int idx_dim,
@@ -220,10 +220,11 @@ struct StepIn {
   int8_t* idx_cache;
 };
 
-// The chain of qsa_decode, qsa_decode_pooled, qsa_decode_step_pooled and qsa_decode_multi: the
-// scan reads idx_cache (int8 keys, T draft queries per request) or, when pooled is given, the
-// side cache of pooled keys (and makes the step's cache writes when step is given); the
-// selection, attention and merge run on the B*T virtual requests.
+// The chain of qsa_decode, qsa_decode_pooled, qsa_decode_step_pooled, qsa_decode_multi and
+// qsa_decode_multi_pooled: the scan reads idx_cache (int8 keys, T draft queries per request)
+// or, when pooled is given, the side cache of pooled keys (and makes the step's cache writes
+// when step is given; with 2 <= T <= 4 draft tokens it also reads idx_cache on the pages that
+// hold draft positions); the selection, attention and merge run on the B*T virtual requests.
 qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_cache, const int16_t* pooled,
                           const void* k_cache, const void* v_cache, const int32_t* page_table,
                           const int32_t* context_lens, int B, int T, int Hq, int Hkv, int head_dim, int n_idx_heads,
@@ -232,8 +233,9 @@ qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_
                           float* partial_out, float* partial_lse, float* out, float* out_lse, void* workspace,
                           size_t workspace_bytes, void* stream, const StepIn* step = nullptr) {
   const int8_t* keys = pooled ? reinterpret_cast<const int8_t*>(pooled) : idx_cache;
-  if (T < 1 || (pooled && T != 1)) return QSA_ERR_SHAPE;
-  if (T > kMaxQueries) return QSA_ERR_UNSUPPORTED;
+  if (T < 1 || (pooled && step && T != 1)) return QSA_ERR_SHAPE;
+  if (T > kMaxQueries || (pooled && T > 4)) return QSA_ERR_UNSUPPORTED;
+  if (pooled && T > 1 && B > 0 && (!idx_cache || misaligned(idx_cache))) return idx_cache ? QSA_ERR_SHAPE : QSA_ERR_NULL;
   const int BT = B * T;   // virtual requests (request, draft token)
   qsa_status_t st = check_index(q_idx, keys, page_table, context_lens, B, n_idx_heads, idx_dim, page_size,
                                 max_pages_per_seq, max_blocks, block_scores);
@@ -256,7 +258,7 @@ qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_
                                                     step ? step->k_new : nullptr, step ? step->v_new : nullptr,
                                                     step ? step->idx_new : nullptr, step ? step->write : nullptr,
                                                     step ? step->k_cache : nullptr, step ? step->v_cache : nullptr,
-                                                    step ? step->idx_cache : nullptr, Hkv, s)
+                                                    step ? step->idx_cache : nullptr, Hkv, s, T, idx_cache)
                         : launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
                                              max_blocks, block_scores, page_max, T, s);
   if (e == hipSuccess)
@@ -385,6 +387,22 @@ qsa_status_t qsa_decode_multi(const void* q, const int8_t* q_idx, const int8_t* 
                       workspace_bytes, stream);
 }
 
+qsa_status_t qsa_decode_multi_pooled(const void* q, const int8_t* q_idx, const int8_t* idx_cache,
+                                     const int16_t* pooled_cache, const void* k_cache, const void* v_cache,
+                                     const int32_t* page_table, const int32_t* context_lens, int B, int T, int Hq,
+                                     int Hkv, int head_dim, int n_idx_heads, int idx_dim, int page_size,
+                                     int max_pages_per_seq, int max_blocks, int k, int P, float softmax_scale,
+                                     int32_t* block_scores, int32_t* sel_blocks, int32_t* sel_count,
+                                     float* partial_out, float* partial_lse, float* out, float* out_lse,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!pooled_cache || !idx_cache)) return QSA_ERR_NULL;
+  if (B > 0 && T > 0 && (long long)B * T > 65535) return QSA_ERR_UNSUPPORTED;
+  return decode_chain(q, q_idx, idx_cache, pooled_cache, k_cache, v_cache, page_table, context_lens, B, T, Hq, Hkv,
+                      head_dim, n_idx_heads, idx_dim, page_size, max_pages_per_seq, max_blocks, k, P, softmax_scale,
+                      block_scores, sel_blocks, sel_count, partial_out, partial_lse, out, out_lse, workspace,
+                      workspace_bytes, stream);
+}
+
 qsa_status_t qsa_decode_step_pooled(const void* k_new, const void* v_new, const int8_t* idx_new, const int32_t* write,
                                     void* k_cache, void* v_cache, int8_t* idx_cache, int16_t* pooled_cache,
                                     const void* q, const int8_t* q_idx, const int32_t* page_table,
@@ -445,7 +463,7 @@ qsa_status_t qsa_index_score_pooled(const int8_t* q_idx, const int16_t* pooled_c
   if (st != QSA_OK || B == 0) return st;
   return hip_status(launch_index_score_pooled(q_idx, pooled_cache, page_table, context_lens, B, max_pages_per_seq,
                                               max_blocks, block_scores, page_max, nullptr, nullptr, nullptr, nullptr,
-                                              nullptr, nullptr, nullptr, 0, (hipStream_t)stream));
+                                              nullptr, nullptr, nullptr, 0, (hipStream_t)stream, 1, nullptr));
 }
 
 qsa_status_t qsa_check_pages(const int32_t* page_table, const int32_t* context_lens, int B,

@@ -248,6 +248,115 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_kernel(
   }
 }
 
+// Multi-token decode over the side cache: T (2..4) draft tokens per request, draft token t
+// seeing the first L_b - (T-1-t) tokens. A wave scores one page for all T queries, with the
+// lane layout of the scan above (lane 32*hf + c: keys 8c .. 8c+7 of block 2i + hf). A page
+// that holds no position some draft token must not see is read once from the side cache; a
+// page within T-1 tokens of L_b (at most two per request) is read from its int8 indexer rows
+// instead, token by token, each token's dot product kept for the draft tokens that see it:
+// the side-cache entries of its blocks pool the draft tokens' keys as well. Scores and page
+// maxima of draft token t go to row b*T + t, as in the int8 multi-token scan.
+template <int WAVES, int T>
+__global__ __launch_bounds__(WAVES * 64) void index_score_pooled_multi_kernel(
+    const int8_t* __restrict__ q_idx, const int16_t* __restrict__ pooled, const int8_t* __restrict__ idx_cache,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages, int max_blocks,
+    int32_t* __restrict__ scores, int32_t* __restrict__ page_max) {
+  const int b = blockIdx.y, lane = lane_id(), wave = threadIdx.x >> 6;
+  const int p = blockIdx.x * WAVES + wave;
+  // length and page entry in one round trip, as in the single-token scans
+  const int L = lens[b];
+  const int page = page_table[(size_t)b * max_pages + __builtin_amdgcn_readfirstlane(min(p, max_pages - 1))];
+  asm volatile("" ::"s"(page));
+  const int npages = (L + kPageSize - 1) / kPageSize;
+  if (p >= npages) return;
+  const int hf = lane >> 5, c = lane & 31;
+  const int valid = L - p * kPageSize;                 // tokens of this page below L (>= 1)
+  const bool mixed = valid < kPageSize + T - 1;        // the same for the whole wave
+  int2 q8[T];                                          // query values 8c .. 8c+7, int8
+#pragma unroll
+  for (int t = 0; t < T; ++t) q8[t] = *reinterpret_cast<const int2*>(q_idx + ((size_t)b * T + t) * kIdxTokenBytes + 8 * c);
+  int part[T][8];                                      // the lane's part of block 2i+hf's score
+  if (!mixed) {
+    i32x4 v[8];
+    const int8_t* base = reinterpret_cast<const int8_t*>(pooled) + (size_t)page * kPooledPageBytes + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + 1024 * i));
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      short2v qd[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = e < 2 ? q8[t].x : q8[t].y;
+        const int k0 = 2 * (e & 1);
+        qd[e] = short2v{(short)sbyte(w, k0), (short)sbyte(w, k0 + 1)};
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int a = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int w = v[i][e];
+          a = __builtin_amdgcn_sdot2(__builtin_bit_cast(short2v, w), qd[e], a, false);
+        }
+        part[t][i] = a;
+      }
+    }
+  } else {
+    const int8_t* rows = idx_cache + (size_t)page * kIdxPageBytes + 8 * c;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) part[t][i] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int u = 0; u < kTokensPerBlock; ++u) {
+        const int row = kTokensPerBlock * (2 * i + hf) + u;   // row of the page
+        const int2 kv = row < valid ? *reinterpret_cast<const int2*>(rows + row * kIdxTokenBytes) : int2{0, 0};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          int d = __builtin_amdgcn_sdot4(kv.x, q8[t].x, 0, false);
+          d = __builtin_amdgcn_sdot4(kv.y, q8[t].y, d, false);
+          part[t][i] += row < valid - (T - 1 - t) ? d : 0;
+        }
+      }
+  }
+  int tot[T][8];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int a = row16_sum(part[t][i]);
+      tot[t][i] = a + __shfl_xor(a, 16, 64);   // the half's other row
+    }
+  // lane c = 8*tq + j of each half writes draft token tq's block 2j + hf
+  const int first = p * kSlotsPerPage;
+  const int tq = c >> 3, j = c & 7;
+  if (tq < T) {
+    int mine = tot[0][0];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mine = (tq == t && j == i) ? tot[t][i] : mine;
+    const int Lt = L - (T - 1 - tq);
+    const int nblk = Lt > 0 ? (Lt + kTokensPerBlock - 1) / kTokensPerBlock : 0;
+    const int blk = first + 2 * j + hf;
+    if (blk < nblk) scores[((size_t)b * T + tq) * max_blocks + blk] = mine;
+  }
+  if (page_max != nullptr) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int Lt = L - (T - 1 - t);
+      const int nblk = Lt > 0 ? (Lt + kTokensPerBlock - 1) / kTokensPerBlock : 0;
+      int m = (int)0x80000000;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = first + 2 * i + hf < nblk ? max(m, tot[t][i]) : m;
+      m = max(m, __shfl_xor(m, 32, 64));
+      if (lane == 0) page_max[((size_t)b * T + t) * max_pages + p] = m;
+    }
+  }
+}
+
 constexpr int kSideWaves = 8;   // 8 pages per workgroup: the pooled scan ran 0.5-0.9 us faster than with 16
 
 hipError_t launch_pool_build(const int8_t* idx_cache, const int32_t* page_table, const int32_t* lens, int B,
@@ -285,15 +394,56 @@ void launch_pooled_w(int B, hipStream_t stream, hipEvent_t e0, hipEvent_t e1, co
 // k_new == nullptr: the scan alone; otherwise it also makes the decode step's cache writes. One
 // page per wave; a batch with few pages in all gets one-wave workgroups, so that its pages
 // spread over many CUs.
+template <int WAVES, int T>
+void launch_pooled_multi_w(int B, hipStream_t stream, hipEvent_t e0, hipEvent_t e1, const int8_t* q_idx,
+                           const int16_t* pooled, const int8_t* idx_keys, const int32_t* page_table,
+                           const int32_t* lens, int max_pages, int max_blocks, int32_t* scores, int32_t* page_max) {
+  const dim3 grid((unsigned)((max_pages + WAVES - 1) / WAVES), B);
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL((index_score_pooled_multi_kernel<WAVES, T>), grid, dim3(WAVES * 64), 0, stream, e0, e1, 0,
+                          q_idx, pooled, idx_keys, page_table, lens, max_pages, max_blocks, scores, page_max);
+  else
+    hipLaunchKernelGGL((index_score_pooled_multi_kernel<WAVES, T>), grid, dim3(WAVES * 64), 0, stream, q_idx, pooled,
+                       idx_keys, page_table, lens, max_pages, max_blocks, scores, page_max);
+}
+
+template <int T>
+void launch_pooled_multi(int B, hipStream_t stream, hipEvent_t e0, hipEvent_t e1, const int8_t* q_idx,
+                         const int16_t* pooled, const int8_t* idx_keys, const int32_t* page_table, const int32_t* lens,
+                         int max_pages, int max_blocks, int32_t* scores, int32_t* page_max) {
+  if ((long long)B * max_pages >= 256LL * kSideWaves)
+    launch_pooled_multi_w<kSideWaves, T>(B, stream, e0, e1, q_idx, pooled, idx_keys, page_table, lens, max_pages,
+                                         max_blocks, scores, page_max);
+  else
+    launch_pooled_multi_w<1, T>(B, stream, e0, e1, q_idx, pooled, idx_keys, page_table, lens, max_pages, max_blocks,
+                                scores, page_max);
+}
+
+// T = 1: k_new == nullptr gives the scan alone; otherwise it also makes the decode step's cache
+// writes (idx_cache is then where the new indexer row goes). T = 2..4: draft tokens, scored
+// from the side cache and, on the pages holding draft positions, from idx_keys (the int8
+// indexer cache); no writes.
 hipError_t launch_index_score_pooled(const int8_t* q_idx, const int16_t* pooled, const int32_t* page_table,
                                      const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                                      int32_t* page_max, const void* k_new, const void* v_new, const int8_t* idx_new,
                                      const int32_t* write, void* k_cache, void* v_cache, int8_t* idx_cache, int Hkv,
-                                     hipStream_t stream) {
+                                     hipStream_t stream, int T, const int8_t* idx_keys) {
   const StepWrite step{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), idx_new, write,
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), idx_cache, Hkv};
   hipEvent_t e0, e1;   // kernel-timestamp events of qsa_time_next_scan, if set
   take_scan_events(&e0, &e1);
+  if (T > 1) {
+    switch (T) {
+      case 2: launch_pooled_multi<2>(B, stream, e0, e1, q_idx, pooled, idx_keys, page_table, lens, max_pages,
+                                     max_blocks, scores, page_max); break;
+      case 3: launch_pooled_multi<3>(B, stream, e0, e1, q_idx, pooled, idx_keys, page_table, lens, max_pages,
+                                     max_blocks, scores, page_max); break;
+      case 4: launch_pooled_multi<4>(B, stream, e0, e1, q_idx, pooled, idx_keys, page_table, lens, max_pages,
+                                     max_blocks, scores, page_max); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if ((long long)B * max_pages >= 256LL * kSideWaves)
     launch_pooled_w<kSideWaves>(B, stream, e0, e1, q_idx, pooled, page_table, lens, max_pages, max_blocks, scores,
                                 page_max, step);

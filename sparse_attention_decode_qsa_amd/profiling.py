@@ -26,7 +26,8 @@ SCAN_SOURCES = ("csrc/index_score.hip", "csrc/qsa_device.h")
 SCAN_KERNEL = "index_score_kernel"
 CALIB_KERNEL = "calib_copy_kernel"
 CHAIN = ("cache_append_kernel", "index_score_kernel", "index_score_pooled_kernel", "index_score_mq_kernel",
-         "topk_select_kernel", "sparse_attn_kernel", "sparse_attn_pair_kernel", "slice_merge_kernel",
+         "index_score_pooled_multi_kernel", "topk_select_kernel", "sparse_attn_kernel", "sparse_attn_pair_kernel",
+         "slice_merge_kernel",
          "slice_merge_v4_kernel",
          "lse_merge_kernel")
 

@@ -51,6 +51,8 @@ SIGNATURES = {
     "qsa_index_score_multi": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "qsa_decode_multi": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                               _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "qsa_decode_multi_pooled": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                     _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "qsa_decode_step_pooled": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                     _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "qsa_pool_build": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
@@ -382,10 +384,12 @@ class MultiDecodePlan:
     """Multi-token decode: T draft tokens per request, one qsa_decode_multi call per run().
 
     q [B, T, Hq, 128] bf16, q_idx [B, T, 4, 64] int8; the results hold one row per
-    (request, draft token) in the order b*T + t (e.g. out [B*T, Hq, 128])."""
+    (request, draft token) in the order b*T + t (e.g. out [B*T, Hq, 128]). With pooled (the
+    side cache, T <= 4) each run() is one qsa_decode_multi_pooled call instead: the same
+    results from the side cache."""
 
     def __init__(self, q, q_idx, idx_cache, k_cache, v_cache, page_table, context_lens, P, k=MAX_K,
-                 softmax_scale=None, max_blocks=None):
+                 softmax_scale=None, max_blocks=None, pooled=None):
         _need(q, torch.bfloat16, "q", 4)
         _need(q_idx, torch.int8, "q_idx", 4)
         for t, dt, n in ((idx_cache, torch.int8, "idx_cache"), (k_cache, torch.bfloat16, "k_cache"),
@@ -409,9 +413,12 @@ class MultiDecodePlan:
         self.out_lse = torch.empty((BT, Hq), dtype=torch.float32, device=dev)
         self.workspace = Workspace(lib().qsa_decode_multi_workspace_size(B, T, Hq, Hkv, self.max_blocks, k, P), dev)
         scale = D ** -0.5 if softmax_scale is None else softmax_scale
-        self._fn = lib().qsa_decode_multi
+        if pooled is not None:
+            _need(pooled, torch.int16, "pooled", 4)
+        self._fn = lib().qsa_decode_multi if pooled is None else lib().qsa_decode_multi_pooled
+        keys = [_ptr(idx_cache)] if pooled is None else [_ptr(idx_cache), _ptr(pooled)]
         self._args = [
-            _ptr(q), _ptr(q_idx), _ptr(idx_cache), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+            _ptr(q), _ptr(q_idx), *keys, _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
             _ptr(context_lens), B, T, Hq, Hkv, D, q_idx.shape[2], q_idx.shape[3], k_cache.shape[1],
             max_pages, self.max_blocks, k, P, ctypes.c_float(scale), _ptr(self.scores), _ptr(self.sel),
             _ptr(self.sel_count), _ptr(self.partial_out), _ptr(self.partial_lse), _ptr(self.out),

@@ -241,6 +241,24 @@ def test_decode_multi_host_checks():
     assert d(*bad) == WS
 
 
+def test_decode_multi_pooled_host_checks():
+    """qsa_decode_multi_pooled: qsa_decode_multi's checks, both key caches required, T <= 4."""
+    d = qsa.lib().qsa_decode_multi_pooled
+    args = [FAKE] * 8 + [2, 2, 32, 4, 128, 4, 64, 64, 16, 256, 512, 4, 0.1] + [FAKE] * 7 + [FAKE, 1 << 26, None]
+    assert len(args) == len(qsa.SIGNATURES["qsa_decode_multi_pooled"][1])
+    assert d(*args[:8], 0, *args[9:]) == OK        # B = 0
+    bad = list(args); bad[3] = None
+    assert d(*bad) == NULL                         # no side cache
+    bad = list(args); bad[2] = None
+    assert d(*bad) == NULL                         # no int8 keys for the pages with draft positions
+    bad = list(args); bad[9] = 0
+    assert d(*bad) == SHAPE                        # T = 0
+    bad = list(args); bad[9] = 5
+    assert d(*bad) == UNSUP                        # more than 4 draft tokens
+    bad = list(args); bad[29] = 100
+    assert d(*bad) == WS
+
+
 def test_index_score_multi_host_checks():
     L = qsa.lib()
     f = L.qsa_index_score_multi

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from sparse_attention_decode_qsa_amd import qsa
-from sparse_attention_decode_qsa_amd.inputs import WORKLOADS, Workload, make_inputs
+from sparse_attention_decode_qsa_amd.inputs import WORKLOADS, Workload, bf16_bits, draft_queries, make_inputs
 from tests.helpers import oracle_arrays, oracle_decode
 from tests.test_gpu_parity import check_request, say
 
@@ -194,3 +194,53 @@ def test_fused_step_equals_append_then_decode(masked):
     for b, L in enumerate(lens):
         n = (L + 3) // 4
         assert torch.equal(a.scores[b, :n], bplan.scores[b, :n]), b
+
+
+def _multi(x, q, qi, P, pooled=None):
+    plan = qsa.MultiDecodePlan(q, qi, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, P,
+                               pooled=pooled)
+    plan.run()
+    return plan
+
+
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_multi_pooled_equals_multi(T):
+    """qsa_decode_multi_pooled (draft tokens scored from the side cache, the pages holding
+    draft positions from the int8 rows) against qsa_decode_multi: scores of every draft token,
+    selections, partials and outputs bit for bit, at lengths whose draft positions cross a
+    block or a page boundary or cover a whole short request; the side cache pools every row
+    below L_b, the draft tokens' included. Every (request, draft token) against the oracle."""
+    lens = (1, 2, 3, 4, 5, 6, 63, 64, 65, 66, 67, 129, 130, 2049, 9000, 40001)
+    x = make_inputs(W(lens), 40 + T, "cuda")
+    q, qi = draft_queries(x, T, 40 + T)
+    side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens)
+    say(f"[multi pooled T={T}] lens={lens}")
+    plain, fast = _multi(x, q, qi, 3), _multi(x, q, qi, 3, pooled=side)
+    torch.cuda.synchronize()
+    for name in ("sel", "sel_count", "partial_out", "partial_lse", "out", "out_lse"):
+        u, v = getattr(plain, name), getattr(fast, name)
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32)), name
+    a = oracle_arrays(x)
+    refs = oracle.decode_multi(bf16_bits(q), qi.cpu().numpy(), a["idx_cache"], a["k_cache"], a["v_cache"],
+                               a["page_table"], a["lengths"], T, 3, x.scale)
+    g = dict(scores=fast.scores.cpu().numpy(), sel=fast.sel.cpu().numpy(), cnt=fast.sel_count.cpu().numpy(),
+             po=fast.partial_out.cpu().numpy(), pl=fast.partial_lse.cpu().numpy(), out=fast.out.cpu().numpy(),
+             lse=fast.out_lse.cpu().numpy())
+    for b, L in enumerate(lens):
+        for t in range(T):
+            r = b * T + t
+            Lt = oracle.draft_length(L, T, t)
+            n = (Lt + 3) // 4
+            assert torch.equal(plain.scores[r, :n], fast.scores[r, :n]), (b, t)
+            check_request(g, r, refs[r], Lt, what=f"multi pooled T{T} b{b} t{t}")
+
+
+def test_multi_pooled_full_w4():
+    """Four draft tokens on the 256K batch: the side-cache path against the int8 path."""
+    x = make_inputs(WORKLOADS["w4"], 0, "cuda")
+    q, qi = draft_queries(x, 4, 0)
+    side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens)
+    plain, fast = _multi(x, q, qi, 4), _multi(x, q, qi, 4, pooled=side)
+    torch.cuda.synchronize()
+    for name in ("sel", "sel_count", "out", "out_lse"):
+        assert torch.equal(getattr(plain, name).view(torch.int32), getattr(fast, name).view(torch.int32)), name
