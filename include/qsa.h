@@ -161,7 +161,8 @@ qsa_status_t qsa_topk_select(const int32_t* block_scores, const int32_t* context
  *                largest power of two <= min(32, ceil(512 / (B*Hkv*P))) (at least 1); the
  *                workspace holds the share partials, B*P*C*Hq*head_dim + B*P*C*Hq floats
  *                (each part rounded up to 256 bytes), which are merged into the slice
- *                partials by log-sum-exp.
+ *                partials by log-sum-exp. With C = 1 the size is 0 (the slice partials
+ *                are written directly).
  */
 size_t qsa_attn_workspace_size(int B, int Hq, int Hkv, int k, int P);
 qsa_status_t qsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kHeadDim) void lse_merge_kernel(const float* __rest
   if (out_lse && d == 0) out_lse[(size_t)b * Hq + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
-// so [B, P, C, Hq, 128], sl [B, P, C, Hq] -> part_out [B, P, Hq, 128], part_lse [B, P, Hq];
+// so [B, P, C, Hq, 128], sl [B, P, C, Hq] -> part_out [B, P, Hq, 128], part_lse [B, P, Hq]
+// (not written when part_out is NULL: with C = 1 the attention kernel wrote them as so, sl);
 // then, when out != NULL, out [B, Hq, 128] and (when out_lse != NULL) out_lse [B, Hq].
 // Slice p: Mp = max_c lse_pc, w_c = exp(lse_pc - Mp) over the finite shares,
 //   part_out = sum_c w_c o_pc / sum_c w_c,  part_lse = Mp + ln(sum_c w_c)   (0, -inf if none)
@@ -114,8 +115,10 @@ __device__ __forceinline__ void slice_merge_regs(const float* __restrict__ so, c
       }
     }
     const float o = ws > 0.f ? a / ws : 0.f;
-    part_out[(((size_t)b * P + p) * Hq + h) * kHeadDim + d] = o;
-    if (d == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp[p];
+    if (part_out) {
+      part_out[(((size_t)b * P + p) * Hq + h) * kHeadDim + d] = o;
+      if (d == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp[p];
+    }
     if (M != -INFINITY && lp[p] != -INFINITY) {
       const float w = __expf(lp[p] - M);
       wsum += w;
@@ -200,8 +203,10 @@ __global__ __launch_bounds__(128) void slice_merge_v4_kernel(const float* __rest
     f32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = ws > 0.f ? a[e] / ws : 0.f;
-    *reinterpret_cast<f32x4*>(part_out + (((size_t)b * P + p) * Hq + h) * kHeadDim + d0) = o;
-    if (d0 == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp[p];
+    if (part_out) {
+      *reinterpret_cast<f32x4*>(part_out + (((size_t)b * P + p) * Hq + h) * kHeadDim + d0) = o;
+      if (d0 == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp[p];
+    }
     if (M != -INFINITY && lp[p] != -INFINITY) {
       const float w = __expf(lp[p] - M);
       wsum += w;
@@ -271,8 +276,10 @@ __device__ __forceinline__ void slice_merge_lds(const float* __restrict__ so, co
     }
     const float o = ws > 0.f ? a / ws : 0.f;
     const float lp = s_slice_lse[p];
-    part_out[(((size_t)b * P + p) * Hq + h) * kHeadDim + d] = o;
-    if (d == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp;
+    if (part_out) {
+      part_out[(((size_t)b * P + p) * Hq + h) * kHeadDim + d] = o;
+      if (d == 0) part_lse[((size_t)b * P + p) * Hq + h] = lp;
+    }
     if (M != -INFINITY && lp != -INFINITY) {
       const float w = __expf(lp - M);
       wsum += w;

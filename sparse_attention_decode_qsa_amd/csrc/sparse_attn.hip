@@ -580,24 +580,29 @@ size_t attn_sub_out_bytes(int B, int Hq, int Hkv, int P) {
   return align256((size_t)B * P * attn_split(B, Hkv, P) * Hq * kHeadDim * sizeof(float));
 }
 
+// One share per slice needs no workspace: the attention kernel writes the slice partials.
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int P) {
+  if (attn_split(B, Hkv, P) == 1) return 0;
   return attn_sub_out_bytes(B, Hq, Hkv, P) +
          align256((size_t)B * P * attn_split(B, Hkv, P) * Hq * sizeof(float));
 }
 
 hipError_t launch_slice_merge(const float* so, const float* sl, int B, int P, int C, int Hq, float* part_out,
                               float* part_lse, float* out, float* out_lse, hipStream_t stream);
-
-// The shares' partials go to the workspace; slice_merge_kernel then writes the slice
-// partials and, when out != NULL, the merge of the slices.
+// Several shares per slice: their partials go to the workspace, and slice_merge_kernel then
+// writes the slice partials and, when out != NULL, the merge of the slices. One share per
+// slice (a share partial is then the slice partial, bit for bit): the attention kernel writes
+// the slice partials itself and, when out != NULL, the same merge kernel reads them in place
+// and writes only the merged result.
 hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* page_table,
                               const int32_t* lens, const int32_t* sel, const int32_t* sel_count, int B,
                               int Hq, int Hkv, int max_pages, int k, int P, float scale,
                               float* part_out, float* part_lse, float* out, float* out_lse,
                               void* workspace, int T, hipStream_t stream) {
   const int C = attn_split(B, Hkv, P);
-  float* sub_out = static_cast<float*>(workspace);
-  float* sub_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn_sub_out_bytes(B, Hq, Hkv, P));
+  float* sub_out = C == 1 ? part_out : static_cast<float*>(workspace);
+  float* sub_lse = C == 1 ? part_lse
+                          : reinterpret_cast<float*>(static_cast<char*>(workspace) + attn_sub_out_bytes(B, Hq, Hkv, P));
   const float scale_log2 = scale * 1.4426950408889634f;
   if ((long long)C * Hkv * T > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (T >= kPairMinTokens && Hq == 8 * Hkv) {
@@ -613,6 +618,9 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (C == 1)
+    return out != nullptr ? launch_slice_merge(part_out, part_lse, B, P, 1, Hq, nullptr, nullptr, out, out_lse, stream)
+                          : e;
   return launch_slice_merge(sub_out, sub_lse, B, P, C, Hq, part_out, part_lse, out, out_lse, stream);
 }
 
