@@ -321,23 +321,30 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_multi_kernel(
         }
       }
   }
-  int tot[T][8];
+  // Sums over the 32 lanes of each half, T values per block. First the two 16-lane rows of a
+  // half trade halves of the token range (row 0 keeps tokens [0, H), row 1 tokens [H, 2H); T
+  // odd gets a zero token), so each row then sums H values per block instead of T.
+  constexpr int H = (T + 1) / 2;
+  const bool row1 = (lane >> 4) & 1;
+  int red[H][8];
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int k = 0; k < H; ++k)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int a = row16_sum(part[t][i]);
-      tot[t][i] = a + __shfl_xor(a, 16, 64);   // the half's other row
+      const int lo = part[k][i], hi = H + k < T ? part[H + k][i] : 0;
+      const int keep = row1 ? hi : lo, send = row1 ? lo : hi;
+      red[k][i] = row16_sum(keep + __shfl_xor(send, 16, 64));
     }
-  // lane c = 8*tq + j of each half writes draft token tq's block 2j + hf
+  // red[k][i] in row r of half hf: draft token r*H + k, block 2i + hf. Lane cc = 8*k + j of
+  // the row writes token r*H + k, block 2j + hf.
   const int first = p * kSlotsPerPage;
-  const int tq = c >> 3, j = c & 7;
-  if (tq < T) {
-    int mine = tot[0][0];
+  const int cc = lane & 15, kq = cc >> 3, j = cc & 7, tq = (row1 ? H : 0) + kq;
+  if (kq < H && tq < T) {
+    int mine = red[0][0];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int k = 0; k < H; ++k)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mine = (tq == t && j == i) ? tot[t][i] : mine;
+      for (int i = 0; i < 8; ++i) mine = (kq == k && j == i) ? red[k][i] : mine;
     const int Lt = L - (T - 1 - tq);
     const int nblk = Lt > 0 ? (Lt + kTokensPerBlock - 1) / kTokensPerBlock : 0;
     const int blk = first + 2 * j + hf;
@@ -345,14 +352,15 @@ __global__ __launch_bounds__(WAVES * 64) void index_score_pooled_multi_kernel(
   }
   if (page_max != nullptr) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int k = 0; k < H; ++k) {
+      const int t = (row1 ? H : 0) + k;
       const int Lt = L - (T - 1 - t);
       const int nblk = Lt > 0 ? (Lt + kTokensPerBlock - 1) / kTokensPerBlock : 0;
       int m = (int)0x80000000;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = first + 2 * i + hf < nblk ? max(m, tot[t][i]) : m;
-      m = max(m, __shfl_xor(m, 32, 64));
-      if (lane == 0) page_max[((size_t)b * T + t) * max_pages + p] = m;
+      for (int i = 0; i < 8; ++i) m = first + 2 * i + hf < nblk ? max(m, red[k][i]) : m;
+      m = max(m, __shfl_xor(m, 32, 64));          // the other half's blocks
+      if (hf == 0 && cc == 0 && t < T) page_max[((size_t)b * T + t) * max_pages + p] = m;
     }
   }
 }
