@@ -85,42 +85,34 @@ struct Tile {
 // Tile of 4 kept blocks starting at share slot bbase (share slots [0, nslot)); block ids and
 // the physical rows of their first tokens (page * 64 + row, below 2^32 for any cache that fits
 // in memory) come from LDS. kg and vg point at the lane's 16 bytes of row 0 of the caches
-// (KV head g; dims 8*q4 for K, 8*i16 for V), rs is the row stride in elements. Rows at or
-// past L are not loaded. PAIR: the lane's column
-// belongs to new token tk of a pair, of length Lc <= L, which keeps a block of the share
-// when bit tk of its s_mask entry is set.
+// (KV head g; dims 8*q4 for K, 8*i16 for V), rs is the row stride in elements. A token past
+// the share or at or past L (a poisoned or unrelated row) is not read: its lane loads the
+// row of the tile's first token instead (always present, so finite), and the token is marked
+// absent, which gives it a score of -inf and so a weight of exactly 0. Every lane loads, with
+// no branch. PAIR: the lane's column belongs to new token tk of a pair, of length Lc <= L,
+// which keeps a block of the share when bit tk of its s_mask entry is set.
 template <bool PAIR>
 __device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const int* s_sel, const uint32_t* s_ptok,
                                           const int* s_mask, int L, int Lc, int tk, const uint16_t* kg,
                                           const uint16_t* vg, uint32_t rs, int i16, int q4) {
+  const uint32_t safe = s_ptok[bbase];   // token 0 of the tile's first block
   {
-    const int slot = bbase + (i16 >> 2);
-    const int tok = slot < nslot ? 4 * s_sel[slot] + (i16 & 3) : L;
-    if (tok < L) {
-      const uint16_t* krow = kg + (size_t)(s_ptok[slot] + (i16 & 3)) * rs;
+    const int slot = bbase + (i16 >> 2), cs = min(slot, nslot - 1);
+    const bool ok = slot < nslot && 4 * s_sel[cs] + (i16 & 3) < L;
+    const uint16_t* krow = kg + (size_t)(ok ? s_ptok[cs] + (i16 & 3) : safe) * rs;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) T.k[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) T.k[s] = bf16x8{};
-    }
+    for (int s = 0; s < 4; ++s) T.k[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
   }
-  const int slot = bbase + q4;
-  const int blk = slot < nslot ? s_sel[slot] : -1;
-  const uint32_t row0 = blk >= 0 ? s_ptok[slot] : 0u;
+  const int slot = bbase + q4, cs = min(slot, nslot - 1);
+  const int blk = slot < nslot ? s_sel[cs] : -1;
+  const uint32_t row0 = s_ptok[cs];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int tok = 4 * blk + v;
-    T.tv[v] = blk >= 0 && tok < L;
-    if (T.tv[v]) {
-      const uint16_t* vrow = vg + (size_t)(row0 + v) * rs;
-      T.v[v] = *reinterpret_cast<const u16x8*>(vrow);
-    } else {
-      T.v[v] = u16x8{};
-    }
+    T.tv[v] = blk >= 0 && 4 * blk + v < L;
+    T.v[v] = *reinterpret_cast<const u16x8*>(vg + (size_t)(T.tv[v] ? row0 + v : safe) * rs);
   }
   if (PAIR) {
-    const bool own = blk >= 0 && ((s_mask[slot] >> tk) & 1);
+    const bool own = blk >= 0 && ((s_mask[cs] >> tk) & 1);
 #pragma unroll
     for (int v = 0; v < 4; ++v) T.sv[v] = own && 4 * blk + v < Lc;
   }
