@@ -53,6 +53,8 @@ constexpr int kTilesInFlight = 4;        // tiles whose loads a wave issues befo
 constexpr int kAttnTargetGroups = 512;   // two workgroups per CU
 constexpr int kMaxSplit = 32;            // shares per slice (tiny batches: one request, few heads)
 constexpr int kPairMinTokens = 16;       // chunks of at least this many new tokens use the pair kernel
+constexpr int kPairHeads = 4;            // at most this many KV heads per pair-kernel workgroup
+constexpr int kPairMinGroups = 4096;     // ... as long as the launch keeps this many workgroups
 static_assert(kMaxK <= 2 * kAttnThreads, "two kept slots per thread");
 
 // Shares per slice for a launch of B requests, Hkv KV heads and P slices: the largest power
@@ -362,16 +364,18 @@ __device__ __forceinline__ int lower_bound_lds(const int* a, int n, int v) {
 // unrelated selections the union is the two lists side by side and the work is the same as
 // two single-token workgroups'. Each token's slice is its own (its page count can differ by
 // one from its neighbour's). The share partials written are exactly the single-token
-// kernel's, per virtual request. Grid (C * Hkv * ceil(T/2), P, B_req).
+// kernel's, per virtual request. A workgroup takes hpw KV heads in turn (the union, its rows
+// and masks are built once for them). Grid (C * (Hkv/hpw) * ceil(T/2), P, B_req).
 __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int Hq, int Hkv,
-    int max_pages, int k, int P, int C, int T, float scale_log2, float* __restrict__ sub_out,
+    int max_pages, int k, int P, int C, int T, int hpw, float scale_log2, float* __restrict__ sub_out,
     float* __restrict__ sub_lse) {
   constexpr int G = 8;   // query heads per KV head
-  const int gc = blockIdx.x % (C * Hkv), m = blockIdx.x / (C * Hkv);
-  const int g = gc / C, c = gc - g * C, p = blockIdx.y, breq = blockIdx.z;
+  const int HG = Hkv / hpw;   // KV-head groups; this workgroup takes heads g0 .. g0+hpw-1
+  const int gc = blockIdx.x % (C * HG), m = blockIdx.x / (C * HG);
+  const int g0 = (gc / C) * hpw, c = gc % C, p = blockIdx.y, breq = blockIdx.z;
   const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
   const int i16 = lane & 15, q4 = lane >> 4;
   const int ntok = min(2, T - 2 * m);   // 1 for the last token of an odd chunk
@@ -426,17 +430,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
     }
     if (lane == 0) { s_cnt[wave][i][0] = nbefore; s_cnt[wave][i][1] = ninside; }
   }
-  // Q operand: column i16 = head g*8 + i16%8 of new token i16/8, dims 32s + 8*q4 .. +7.
-  const int tk = i16 >> 3;
-  bf16x8 qa[4];
-  if (tk < ntok) {
-    const uint16_t* qrow = q + ((size_t)(vr0 + tk) * Hq + (size_t)g * G + (i16 & 7)) * kHeadDim + 8 * q4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qa[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qa[s] = bf16x8{};
-  }
+  const int tk = i16 >> 3;   // the lane's column belongs to new token tk
   __syncthreads();
   int seg0[2] = {0, 0}, nin[2] = {0, 0};
 #pragma unroll
@@ -483,13 +477,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
   const int tile0 = min(c * tps, ntiles), nt = min(tile0 + tps, ntiles) - tile0;
   const int slot0 = 4 * tile0, nslot = min(4 * (tile0 + nt), nU) - slot0;
 
-  if (nt == 0) {   // empty share for both tokens
-    for (int i = t; i < ntok * G * 32; i += kAttnThreads) {
-      const int tt = i / (G * 32), h = (i >> 5) % G, d4 = i & 31;
+  if (nt == 0) {   // empty share for both tokens, every head of the workgroup
+    for (int i = t; i < ntok * hpw * G * 32; i += kAttnThreads) {
+      const int tt = i / (hpw * G * 32), hh = (i >> 5) % (hpw * G), d4 = i & 31;
       const size_t share = ((size_t)(vr0 + tt) * P + p) * C + c;
-      *reinterpret_cast<f32x4*>(sub_out + (share * Hq + (size_t)g * G + h) * kHeadDim + 4 * d4) =
+      *reinterpret_cast<f32x4*>(sub_out + (share * Hq + (size_t)g0 * G + hh) * kHeadDim + 4 * d4) =
           f32x4{0.f, 0.f, 0.f, 0.f};
-      if (d4 == 0) sub_lse[share * Hq + (size_t)g * G + h] = -INFINITY;
+      if (d4 == 0) sub_lse[share * Hq + (size_t)g0 * G + hh] = -INFINITY;
     }
     return;
   }
@@ -509,49 +503,82 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
     }
   __syncthreads();
 
+  const uint32_t rs = (uint32_t)Hkv * kHeadDim;
+  const int Lmax = max(Lt[0], Lt[1]), Lc = Lt[tk];
+  // The union, its rows and masks serve the workgroup's hpw KV heads at once: wph = 4/hpw waves
+  // per head, wave `wave` on head g0 + wave/wph, taking every wph-th tile of the share.
+  const int wph = kAttnWaves / hpw, g = g0 + wave / wph, sub = wave % wph;
+  // Q operand: column i16 = head g*8 + i16%8 of new token tk, dims 32s + 8*q4 .. +7.
+  bf16x8 qa[4];
+  if (tk < ntok) {
+    const uint16_t* qrow = q + ((size_t)(vr0 + tk) * Hq + (size_t)g * G + (i16 & 7)) * kHeadDim + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = bf16x8{};
+  }
   const uint16_t* kg = kc + (size_t)g * kHeadDim + 8 * q4;
   const uint16_t* vg = vc + (size_t)g * kHeadDim + 8 * i16;
-  const uint32_t rs = (uint32_t)Hkv * kHeadDim;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int Lmax = max(Lt[0], Lt[1]), Lc = Lt[tk];
-  for (int r0 = wave; r0 < nt; r0 += kAttnWaves * kTilesInFlight) {
+  for (int r0 = sub; r0 < nt; r0 += wph * kTilesInFlight) {
     Tile Ts[kTilesInFlight];
 #pragma unroll
     for (int mm = 0; mm < kTilesInFlight; ++mm) {
-      const int ti = r0 + kAttnWaves * mm;
+      const int ti = r0 + wph * mm;
       if (ti < nt)
         load_tile<true>(Ts[mm], 4 * ti, nslot, s_sel, s_ptok, s_mask, Lmax, Lc, tk, kg, vg, rs, i16, q4);
     }
 #pragma unroll
     for (int mm = 0; mm < kTilesInFlight; ++mm) {
-      const int ti = r0 + kAttnWaves * mm;
+      const int ti = r0 + wph * mm;
       if (ti < nt) attend_tile<true>(Ts[mm], qa, scale_log2, m_run, l_run, acc);
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
 
-  // Merge of the 4 wave partials, as in the single-token kernel, over the 16 columns.
+  if (wph == 1) {
+    // The wave holds its head's whole share: lane (q4, i16) writes column i16's dims
+    // 8*(4*q4 + r) .. +7 from acc[0..7][r], normalised, and lanes q4 = 0 the lse.
+    if (tk < ntok) {
+      const size_t share = ((size_t)(vr0 + tk) * P + p) * C + c;
+      const int hg = g * G + (i16 & 7);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* dst = sub_out + (share * Hq + hg) * kHeadDim + 32 * q4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<f32x4*>(dst + 8 * r) =
+            f32x4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
+        *reinterpret_cast<f32x4*>(dst + 8 * r + 4) =
+            f32x4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
+      }
+      if (q4 == 0)
+        sub_lse[share * Hq + hg] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+    return;
+  }
+  // Several waves per head: their partials merge through LDS, as in the single-token kernel.
   if (q4 == 0) { s_m[wave][i16] = m_run; s_l[wave][i16] = l_tot; }
 #pragma unroll
   for (int u = 0; u < 8; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) s_o[wave][i16][8 * (4 * q4 + r) + u] = acc[u][r];
   __syncthreads();
-  const int h = t >> 4, d0 = 8 * (t & 15), th = h >> 3;
-  if (th < ntok) {
+  for (int it = t; it < hpw * 16 * 16; it += kAttnThreads) {   // (head of the group, column, 8 dims)
+    const int gi = it >> 8, h = (it >> 4) & 15, d0 = 8 * (it & 15), th = h >> 3;
+    if (th >= ntok) continue;
+    const int w0 = gi * wph;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = w0; w < w0 + wph; ++w) M = fmaxf(M, s_m[w][h]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float l = 0.f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
+    for (int w = w0; w < w0 + wph; ++w) {
       const float f = exp2f(s_m[w][h] - Mu);
       l += s_l[w][h] * f;
 #pragma unroll
@@ -559,7 +586,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t share = ((size_t)(vr0 + th) * P + p) * C + c;
-    const int hg = g * G + (h & 7);
+    const int hg = (g0 + gi) * G + (h & 7);
     float* dst = sub_out + (share * Hq + hg) * kHeadDim + d0;
     *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
     *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
@@ -598,10 +625,17 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
   const float scale_log2 = scale * 1.4426950408889634f;
   if ((long long)C * Hkv * T > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (T >= kPairMinTokens && Hq == 8 * Hkv) {
-    hipLaunchKernelGGL(sparse_attn_pair_kernel, dim3(C * Hkv * ((T + 1) / 2), P, B / T), dim3(kAttnThreads), 0,
-                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                       static_cast<const uint16_t*>(vc), page_table, lens, sel, sel_count, Hq, Hkv, max_pages, k,
-                       P, C, T, scale_log2, sub_out, sub_lse);
+    // KV heads per workgroup: 4 or 2 when it divides Hkv and still leaves kPairMinGroups
+    // workgroups (fewer, larger workgroups share the union's setup but need enough of them in
+    // flight), else 1.
+    const long long per_head = (long long)C * ((T + 1) / 2) * P * (B / T);
+    int hpw = 1;
+    for (int h = kPairHeads; h > 1; h /= 2)   // 4 or 2 (the 4 waves split evenly over the heads)
+      if (Hkv % h == 0 && per_head * (Hkv / h) >= kPairMinGroups) { hpw = h; break; }
+    hipLaunchKernelGGL(sparse_attn_pair_kernel, dim3(C * (Hkv / hpw) * ((T + 1) / 2), P, B / T),
+                       dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), page_table, lens, sel,
+                       sel_count, Hq, Hkv, max_pages, k, P, C, T, hpw, scale_log2, sub_out, sub_lse);
   } else {
   hipLaunchKernelGGL(sparse_attn_kernel, dim3(C * Hkv * T, P, B / T), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
