@@ -178,6 +178,26 @@ def test_chunk_pairs_with_overlapping_selections(T, spread, P, gqa, k):
         assert np.mean(shared) > 0.5, f"neighbouring tokens share only {np.mean(shared):.2f} of their blocks"
 
 
+@pytest.mark.parametrize("spread", [None, 4])
+def test_chunk_pairs_four_heads_per_workgroup(spread):
+    """A chunk large enough (4 requests x 512 new tokens, 4 KV heads, P = 4) that each pair
+    workgroup takes all four KV heads, one wave per head, writing its partials from registers:
+    every third token of every request (both members of many pairs) against the oracle."""
+    T, lens = 512, (700, 1300, 2100, 3000)
+    x = make_inputs(Workload("pair4", len(lens), ("list",) + lens, 32, 4, 4), 70, "cuda")
+    q, qi = draft_queries(x, T, 70, spread=spread)
+    say(f"[pairs 4 heads T={T} spread={spread}] lens={lens}")
+    _, g = _run(x, q, qi, 4)
+    a = oracle_arrays(x)
+    qb, qin = bf16_bits(q), qi.cpu().numpy()
+    for b, L in enumerate(lens):
+        for t in list(range(0, T, 3)) + [T - 1]:
+            Lt = oracle.draft_length(L, T, t)
+            ref = oracle.decode_request(qb[b, t], qin[b, t], a["idx_cache"], a["k_cache"], a["v_cache"],
+                                        a["page_table"][b], Lt, 4, x.scale)
+            check_request(g, b * T + t, ref, Lt, what=f"pairs4 b{b} t{t}")
+
+
 def test_prefill_chunk_1024_tokens():
     """A prefill chunk: the last 1024 tokens of an 8192-token request; sampled tokens against
     the oracle, every token's selection against the single-token decode at its length."""
