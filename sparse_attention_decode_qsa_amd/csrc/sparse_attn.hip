@@ -355,8 +355,8 @@ __device__ __forceinline__ int lower_bound_lds(const int* a, int n, int v) {
 }
 
 // Chunks of new tokens with 8 query heads per KV head: new tokens 2m and 2m+1 of a request
-// (virtual requests b*T + 2m and b*T + 2m + 1) share one workgroup per (KV head, slice, share).
-// The 16 MFMA columns of the single-token kernel, half of them empty at a group of 8, hold
+// (virtual requests b*T + 2m and b*T + 2m + 1) share one workgroup per (slice, share, group of
+// hpw KV heads). The 16 MFMA columns of the single-token kernel, half of them empty at a group of 8, hold
 // the two tokens' heads (column i16: token i16/8, head i16%8), and the kernel gathers the
 // union of the two tokens' kept blocks inside the slice once: each block is marked with the
 // tokens that keep it, and a column's scores are -inf on the blocks its token does not keep
@@ -364,8 +364,10 @@ __device__ __forceinline__ int lower_bound_lds(const int* a, int n, int v) {
 // unrelated selections the union is the two lists side by side and the work is the same as
 // two single-token workgroups'. Each token's slice is its own (its page count can differ by
 // one from its neighbour's). The share partials written are exactly the single-token
-// kernel's, per virtual request. A workgroup takes hpw KV heads in turn (the union, its rows
-// and masks are built once for them). Grid (C * (Hkv/hpw) * ceil(T/2), P, B_req).
+// kernel's, per virtual request. The union, its rows and masks are built once for the hpw KV
+// heads (1, 2 or 4): 4/hpw waves per head split the tiles and merge through LDS, or with one
+// wave per head the wave writes its head's partial from its registers. Grid
+// (C * (Hkv/hpw) * ceil(T/2), P, B_req).
 __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens,
