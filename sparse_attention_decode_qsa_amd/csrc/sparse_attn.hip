@@ -169,6 +169,60 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
   }
 }
 
+// Two tiles at once: one softmax update over their 32 tokens (one maximum, one rescale), and
+// the PV product with the lane's 8 distinct tokens (its 4 of tile A, then its 4 of tile B) on
+// the 32 k-slots, hi and lo parts of P as two products with the same V operand, so V needs
+// no duplication.
+template <bool PAIR>
+__device__ __forceinline__ void attend_two(const Tile& A, const Tile& B, const bf16x8* qa, float scale_log2,
+                                           float& m_run, float& l_run, f32x4* acc) {
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[s], qa[s], sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(B.k[s], qa[s], sb, 0, 0, 0);
+  }
+  float sv[8];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sv[v] = (PAIR ? A.sv[v] : A.tv[v]) ? sa[v] * scale_log2 : -INFINITY;
+    sv[4 + v] = (PAIR ? B.sv[v] : B.tv[v]) ? sb[v] * scale_log2 : -INFINITY;
+  }
+  float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = fmaxf(m_run, mt);
+  if (__ballot(m_new != m_run)) {   // as in attend_tile
+    const float alpha = exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+    l_run *= alpha;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = m_run == -INFINITY ? 0.f : m_run;
+  float pv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+  l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+  union { uint32_t w[4]; bf16x8 v; } ph, pl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ph.w[i] = cvt_bf16x2(pv[2 * i], pv[2 * i + 1]);
+    pl.w[i] = cvt_bf16x2(pv[2 * i] - __uint_as_float(ph.w[i] << 16),
+                         pv[2 * i + 1] - __uint_as_float(ph.w[i] & 0xFFFF0000u));
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    union { uint32_t w[4]; bf16x8 v; } va;
+    va.w[0] = pack2(A.v[0][u], A.v[1][u]);
+    va.w[1] = pack2(A.v[2][u], A.v[3][u]);
+    va.w[2] = pack2(B.v[0][u], B.v[1][u]);
+    va.w[3] = pack2(B.v[2][u], B.v[3][u]);
+    acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, ph.v, acc[u], 0, 0, 0);
+    acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pl.v, acc[u], 0, 0, 0);
+  }
+}
+
 // Grid (C * Hkv * T, P, B_req): blockIdx.x = (t * Hkv + g) * C + c for new token t of request
 // b_req = blockIdx.z, slice p = blockIdx.y, and b = b_req*T + t is the virtual request
 // (page-table row b_req, length L - (T-1-t)). With many new tokens (a prefill chunk) the
@@ -283,9 +337,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
       if (ti < nt) load_tile<false>(T[m], 4 * ti, nslot, s_sel, s_ptok, nullptr, L, L, 0, kg, vg, rs, i16, q4);
     }
 #pragma unroll
-    for (int m = 0; m < kTilesInFlight; ++m) {
+    for (int m = 0; m < kTilesInFlight; m += 2) {
       const int ti = r0 + kAttnWaves * m;
-      if (ti < nt) attend_tile<false>(T[m], qa, scale_log2, m_run, l_run, acc);
+      if (ti + kAttnWaves < nt) attend_two<false>(T[m], T[m + 1], qa, scale_log2, m_run, l_run, acc);
+      else if (ti < nt) attend_tile<false>(T[m], qa, scale_log2, m_run, l_run, acc);
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -535,9 +590,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
         load_tile<true>(Ts[mm], 4 * ti, nslot, s_sel, s_ptok, s_mask, Lmax, Lc, tk, kg, vg, rs, i16, q4);
     }
 #pragma unroll
-    for (int mm = 0; mm < kTilesInFlight; ++mm) {
+    for (int mm = 0; mm < kTilesInFlight; mm += 2) {
       const int ti = r0 + wph * mm;
-      if (ti < nt) attend_tile<true>(Ts[mm], qa, scale_log2, m_run, l_run, acc);
+      if (ti + wph < nt) attend_two<true>(Ts[mm], Ts[mm + 1], qa, scale_log2, m_run, l_run, acc);
+      else if (ti < nt) attend_tile<true>(Ts[mm], qa, scale_log2, m_run, l_run, acc);
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
