@@ -55,15 +55,16 @@ constexpr int kSelBins = 2048;
 // Candidate list capacity: 8192 when each thread owns one chunk (contexts up to 256K
 // tokens), else 4096 (the mask words of longer contexts take the LDS).
 constexpr int list_cap(int R) { return R == 1 ? 8192 : 4096; }
+constexpr int kManyRequests = 512;               // from this many requests on, two workgroups per CU
 constexpr int kWavePages = 256;                  // candidate pages one wave can hold
 constexpr int kStridedOut = 8192;                // requests up to this many blocks write ids per block
 constexpr int kMaxSelBlocks = 262144;            // contexts up to 1,048,576 tokens
 
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
 
-template <int R>
+template <int R, int CAP>
 struct SelShared {
-  static constexpr int kListCap = list_cap(R);
+  static constexpr int kListCap = CAP;
   uint32_t hbuf[2][kSelBins + 64];  // double-buffered histogram (+ one dummy bin per lane)
   uint32_t list_u[kListCap];
   int list_j[kListCap];
@@ -212,8 +213,8 @@ __device__ __forceinline__ bool narrow_step(SH& sh, int& hsel, int shift, uint32
 
 // Narrow [lo, hi] over the LDS candidate list (all candidates are >= lo), then write the
 // kept and tie masks of the candidates into the per-chunk words (zero on entry).
-template <int R>
-__device__ __forceinline__ void narrow_list_and_mark(SelShared<R>& sh, int& hsel, uint32_t ncand, uint32_t lo, uint32_t hi,
+template <int R, int CAP>
+__device__ __forceinline__ void narrow_list_and_mark(SelShared<R, CAP>& sh, int& hsel, uint32_t ncand, uint32_t lo, uint32_t hi,
                                                      uint32_t* need_io, bool* all_io, uint32_t* lo_out,
                                                      uint64_t* kept_w, uint64_t* tie_w) {
   const int t = threadIdx.x;
@@ -241,7 +242,7 @@ __device__ __forceinline__ void narrow_list_and_mark(SelShared<R>& sh, int& hsel
   *lo_out = lo;
 }
 
-template <int R>
+template <int R, int CAP = list_cap(R)>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t* __restrict__ scores,
                                                                   const int32_t* __restrict__ lens,
                                                                   const int32_t* __restrict__ page_max,
@@ -249,8 +250,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
                                                                   int32_t* __restrict__ sel,
                                                                   int32_t* __restrict__ sel_count, int T) {
   extern __shared__ uint64_t s_words[];  // [2][1024*R]: kept and tie masks per chunk
-  __shared__ SelShared<R> sh;
-  constexpr int kListCap = SelShared<R>::kListCap;
+  __shared__ SelShared<R, CAP> sh;
+  constexpr int kListCap = CAP;
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = lane_id();
   // The page maxima are loaded at clamped indices (in bounds whatever the length) together
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const int32_t*
   }
   if (have_list && !masks_done) {
     uint32_t llo = lo;
-    narrow_list_and_mark<R>(sh, hsel, ncand, lo, hi, &need, &all_of_bucket, &llo, kept_w, tie_w);
+    narrow_list_and_mark<R, CAP>(sh, hsel, ncand, lo, hi, &need, &all_of_bucket, &llo, kept_w, tie_w);
     lo = llo;
   }
   __syncthreads();
@@ -684,8 +685,15 @@ hipError_t launch_topk_select(const int32_t* scores, const int32_t* lens, const 
                               int T, hipStream_t stream) {
   const int chunks = (max_blocks + kChunk - 1) / kChunk;
   const int R = chunks <= kSelThreads ? 1 : chunks <= 2 * kSelThreads ? 2 : 4;
-  const size_t lds = 2 * (size_t)kSelThreads * R * sizeof(uint64_t);
-  if (R == 1)
+  // Many requests (prefill chunks): the R = 2 form with a 1,024-entry list (53 VGPRs, 78 KB of
+  // LDS) fits two workgroups per CU where the R = 1 form (113 VGPRs, 119 KB) fits one; a
+  // request whose candidates overflow the list takes the narrowing over all its keys instead.
+  const bool many = B >= kManyRequests && R <= 2;
+  const size_t lds = 2 * (size_t)kSelThreads * (many ? 2 : R) * sizeof(uint64_t);
+  if (many)
+    hipLaunchKernelGGL((topk_select_kernel<2, 1024>), dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
+                       page_max, max_blocks, max_pages, k, sel, sel_count, T);
+  else if (R == 1)
     hipLaunchKernelGGL(topk_select_kernel<1>, dim3(B), dim3(kSelThreads), lds, stream, scores, lens,
                        page_max, max_blocks, max_pages, k, sel, sel_count, T);
   else if (R == 2)

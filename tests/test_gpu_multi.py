@@ -198,6 +198,29 @@ def test_chunk_pairs_four_heads_per_workgroup(spread):
             check_request(g, b * T + t, ref, Lt, what=f"pairs4 b{b} t{t}")
 
 
+@pytest.mark.parametrize("alphabet", ["u2", "zero_q"])
+def test_chunk_selection_with_ties_many_requests(alphabet):
+    """Indexer values in {-2..2} (ties at the 512th place) or an all-zero query (every block
+    ties) over 4 requests x 256 new tokens: with this many virtual requests the selection runs
+    two workgroups per CU with a short candidate list, which ties overflow, so the narrowing
+    over every key decides. Every 5th token's scores and selection against the oracle's, and
+    a few tokens in full."""
+    T, lens = 256, (3000, 5200, 700, 9000)
+    x = make_inputs(Workload("ties", len(lens), ("list",) + lens, 32, 4, 2, alphabet=alphabet), 71, "cuda")
+    q, qi = draft_queries(x, T, 71)
+    say(f"[ties many requests T={T} {alphabet}] lens={lens}")
+    _, g = _run(x, q, qi, 2)
+    a = oracle_arrays(x)
+    qb = bf16_bits(q)
+    for b, L in enumerate(lens):
+        _check_scores_and_selection(g, qi, a, b, L, T, range(0, T, 5))
+        for t in (0, T // 2, T - 1):
+            Lt = oracle.draft_length(L, T, t)
+            ref = oracle.decode_request(qb[b, t], qi[b, t].cpu().numpy(), a["idx_cache"], a["k_cache"],
+                                        a["v_cache"], a["page_table"][b], Lt, 2, x.scale)
+            check_request(g, b * T + t, ref, Lt, what=f"ties b{b} t{t}")
+
+
 def test_prefill_chunk_1024_tokens():
     """A prefill chunk: the last 1024 tokens of an 8192-token request; sampled tokens against
     the oracle, every token's selection against the single-token decode at its length."""
