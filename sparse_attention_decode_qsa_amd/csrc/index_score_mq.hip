@@ -18,30 +18,102 @@ namespace qsa {
 // r = 4*g4 + v holds token 16*g4 + 4*tt + v, so the lane's rows are block 4*g4 + tt, the
 // block score is the sum of its four values, and over the four tiles the lane holds the four
 // consecutive blocks 4*g4 .. 4*g4+3 (one 16-byte store per lane; a query's 16 blocks of the
-// page are 64 contiguous bytes). Grid (page groups, B), 8 waves per workgroup (two
-// workgroups share a CU, so one's loads overlap the other's compute), one page per wave: the wave keeps its page's 64 keys in registers in the A layout (16 loads of 16 bytes;
-// lane i16 of tile tt: token 16*(i16/4) + 4*tt + i16%4, bytes 64*s + 16*g4 .. +15) and runs
-// every 16-query tile of the request against them, so the keys are read once. The queries go
-// through LDS in chunks of kQueryChunk, loaded once per workgroup (the first chunk's loads
-// are issued before the keys', and the page id comes by a scalar load, so neither waits on
-// the other). Causal masking (query m sees tokens < L_b - T + 1 + m) is applied only on
-// pages that reach into the new tokens.
-constexpr int kMqWaves = 8;
+// page are 64 contiguous bytes). Grid (page groups, B), one page per wave: the wave keeps its
+// page's 64 keys in registers in the A layout (16 loads of 16 bytes; lane i16 of tile tt:
+// token 16*(i16/4) + 4*tt + i16%4, bytes 64*s + 16*g4 .. +15) and runs every 16-query tile of
+// the request against them, so the keys are read once. The queries go through LDS in chunks
+// of kQueryChunk, loaded once per workgroup (the first chunk's loads are issued before the
+// keys', and the page id comes by a scalar load, so neither waits on the other). Causal
+// masking (query m sees tokens < L_b - T + 1 + m) is applied only on pages that reach into
+// the new tokens.
+//
+// Up to one chunk of queries (T <= kQueryChunk), 8-wave workgroups (two per CU) write each
+// query's page maximum directly. With more, 16-wave workgroups fold the page maxima into LDS
+// words and write a query's 16 consecutive page maxima together after each chunk (one 64-byte
+// run instead of 16 separate 4-byte stores, which took nearly as long as the 755 MB of
+// scores at T = 1024 on the 256K workload). On pages every query sees whole, a wave's four token tiles
+// run as independent MFMA chains with no masking.
 constexpr int kQueryChunk = 64;    // queries staged in LDS at a time (17 KiB with padding)
 constexpr int kQStride = kIdxTokenBytes / 16 + 1;   // 16-byte vectors per staged query
 
-__global__ __launch_bounds__(kMqWaves * 64) void index_score_mq_kernel(
+// Scores of the page held in key (A layout, see above) for the nq queries of the chunk in
+// s_q, 16 queries per step. FULL: every query sees all 64 tokens of the page, so no token or
+// block is masked; the four token tiles' MFMA chains are independent and interleave. Page
+// maxima: STAGE folds each query's into pm_slot (this wave's column of the chunk's LDS words,
+// row stride WAVES); otherwise the lanes of a query combine theirs and one writes it to
+// page_max.
+template <int WAVES, bool STAGE, bool FULL>
+__device__ __forceinline__ void score_query_tiles(const i32x4 (&key)[4][4], const i32x4* s_q, int m0, int nq,
+                                                  int T, int L0, int p, int i16, int g4, int b, int max_blocks,
+                                                  int max_pages, int32_t* __restrict__ scores, int* pm_slot,
+                                                  int32_t* __restrict__ page_max) {
+  const int blk0 = p * kBlocksPerPage + 4 * g4;   // this lane's first block of the page
+  for (int qt = 0; qt < nq; qt += 16) {
+    const int m = m0 + qt + i16;                   // this lane's query
+    i32x4 qv[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[s] = s_q[(qt + i16) * kQStride + 4 * s + g4];
+    i32x4 acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(key[tt][s], qv[s], acc[tt], 0, 0, 0);
+    int32_t* row = scores + ((size_t)b * T + m) * max_blocks;
+    int sc[4];   // blocks 4*g4 + tt of the page for query m
+    int pmax;
+    if (FULL) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) sc[tt] = (acc[tt][0] + acc[tt][1]) + (acc[tt][2] + acc[tt][3]);
+      pmax = max(max(sc[0], sc[1]), max(sc[2], sc[3]));
+      if (m < T) *reinterpret_cast<i32x4*>(row + blk0) = i32x4{sc[0], sc[1], sc[2], sc[3]};
+    } else {
+      const int Lm = L0 + m;
+      const int nblk = m < T && Lm > 0 ? (Lm + kTokensPerBlock - 1) / kTokensPerBlock : 0;
+      pmax = (int)0x80000000;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int pos = p * kPageSize + 16 * g4 + 4 * tt;   // first token of the block
+        sc[tt] = (pos < Lm ? acc[tt][0] : 0) + (pos + 1 < Lm ? acc[tt][1] : 0) + (pos + 2 < Lm ? acc[tt][2] : 0) +
+                 (pos + 3 < Lm ? acc[tt][3] : 0);
+        if (blk0 + tt < nblk) pmax = max(pmax, sc[tt]);
+      }
+      if (blk0 + 3 < nblk) {
+        *reinterpret_cast<i32x4*>(row + blk0) = i32x4{sc[0], sc[1], sc[2], sc[3]};
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          if (blk0 + tt < nblk) row[blk0 + tt] = sc[tt];
+      }
+    }
+    if (STAGE) {
+      if (pm_slot && m < T) atomicMax(pm_slot + (qt + i16) * WAVES, pmax);
+    } else if (page_max) {
+      pmax = max(pmax, __shfl_xor(pmax, 16, 64));
+      pmax = max(pmax, __shfl_xor(pmax, 32, 64));
+      if (g4 == 0 && m < T) page_max[((size_t)b * T + m) * max_pages + p] = pmax;
+    }
+  }
+}
+
+template <int WAVES, bool STAGE>
+__global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 waves per SIMD
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ idx_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages,
     int max_blocks, int T, int32_t* __restrict__ scores, int32_t* __restrict__ page_max) {
   // Query m of the chunk at s_q[m * kQStride ..]: 16 vectors plus one of padding, so the 16
   // queries a wave reads at once start in different banks.
   __shared__ i32x4 s_q[kQueryChunk * kQStride];
-  static_assert((kQueryChunk * kIdxTokenBytes / 16) % (kMqWaves * 64) == 0, "whole vectors per thread");
+  // STAGE: page maxima of a chunk, word q * WAVES + w = query q of the chunk, page w of the
+  // workgroup; two buffers, so that one chunk's words are written out while the next fills.
+  __shared__ int s_pm[STAGE ? 2 : 1][STAGE ? kQueryChunk * WAVES : 1];
+  static_assert((kQueryChunk * kIdxTokenBytes / 16) % (WAVES * 64) == 0, "whole vectors per thread");
+  static_assert(kQueryChunk % 64 == 0, "whole page-maximum words per thread");
   const int b = blockIdx.y;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g4 = lane >> 4;
-  const int p = blockIdx.x * kMqWaves + wave;
+  const int p = __builtin_amdgcn_readfirstlane(blockIdx.x * WAVES + wave);   // wave-uniform
   // The page id is wave-uniform: a scalar load (its own counter, so the keys wait for it
   // and not for the query loads) at a clamped index, in bounds whatever the length, issued
   // together with the length's load (the empty asm keeps it ahead of the exit test).
@@ -49,19 +121,19 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_mq_kernel(
   const int L = lens[b];
   asm volatile("" ::"s"(page), "s"(L));
   const int npages = (L + kPageSize - 1) / kPageSize;
-  if (blockIdx.x * kMqWaves >= npages) return;   // the same for the whole workgroup
+  if (blockIdx.x * WAVES >= npages) return;   // the same for the whole workgroup
   const bool active = p < npages;                 // idle waves still join the barriers
   const int valid = L - p * kPageSize;
   // The first query chunk is loaded before the keys, so its latency overlaps theirs; it is
   // written to LDS once it arrives (the key loads stay in flight).
   constexpr int kQVecs = kQueryChunk * kIdxTokenBytes / 16;   // 16-byte vectors per chunk
-  constexpr int kQPer = kQVecs / (kMqWaves * 64);
+  constexpr int kQPer = kQVecs / (WAVES * 64);
   const int8_t* qrow0 = q_idx + (size_t)b * T * kIdxTokenBytes;
   const int nq0 = min(kQueryChunk, T);
   i32x4 q0[kQPer];
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
-    const int x = threadIdx.x + kMqWaves * 64 * j;
+    const int x = threadIdx.x + WAVES * 64 * j;
     const int lim = nq0 * kIdxTokenBytes / 16;      // loaded without a branch (clamped index)
     const i32x4 v = reinterpret_cast<const i32x4*>(qrow0)[min(x, lim - 1)];
     q0[j] = x < lim ? v : i32x4{0, 0, 0, 0};
@@ -79,62 +151,56 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_mq_kernel(
                                  : i32x4{0, 0, 0, 0};
       }
   }
+  constexpr int kPmPer = kQueryChunk / 64;         // page-maximum words per thread and chunk
+  if (STAGE) {
+#pragma unroll
+    for (int j = 0; j < kPmPer; ++j)
+      s_pm[0][threadIdx.x + WAVES * 64 * j] = s_pm[STAGE][threadIdx.x + WAVES * 64 * j] = (int)0x80000000;
+  }
+  // Writes out the page maxima of the chunk starting at query c0 (buffer buf) and clears them.
+  auto flush_page_max = [&](int buf, int c0) {
+#pragma unroll
+    for (int j = 0; j < kPmPer; ++j) {
+      const int w = threadIdx.x + WAVES * 64 * j;
+      const int m = c0 + w / WAVES, pg = blockIdx.x * WAVES + w % WAVES;
+      if (m < T && pg < npages) page_max[((size_t)b * T + m) * max_pages + pg] = s_pm[buf][w];
+      s_pm[buf][w] = (int)0x80000000;
+    }
+  };
   const int L0 = L - T + 1;                        // query 0 sees tokens < L0
-  const bool causal = active && p * kPageSize + kPageSize > L0;
+  // A page every query sees whole (the usual case) takes a branch-free path; the page holding
+  // the end of the context or reaching into the new tokens masks per token and per block.
+  const bool full = active && (p + 1) * kPageSize <= L0;
   for (int m0 = 0; m0 < T; m0 += kQueryChunk) {
     const int nq = min(kQueryChunk, T - m0);
     if (m0 == 0) {
 #pragma unroll
       for (int j = 0; j < kQPer; ++j) {
-        const int x = threadIdx.x + kMqWaves * 64 * j;
+        const int x = threadIdx.x + WAVES * 64 * j;
         s_q[(x >> 4) * kQStride + (x & 15)] = q0[j];
       }
     } else {
       __syncthreads();                             // the previous chunk is no longer read
-      for (int x = threadIdx.x; x < kQVecs; x += kMqWaves * 64)
+      if (STAGE && page_max) flush_page_max(((m0 / kQueryChunk) - 1) & 1, m0 - kQueryChunk);
+      for (int x = threadIdx.x; x < kQVecs; x += WAVES * 64)
         s_q[(x >> 4) * kQStride + (x & 15)] =
             x < nq * kIdxTokenBytes / 16 ? reinterpret_cast<const i32x4*>(qrow0 + (size_t)m0 * kIdxTokenBytes)[x]
                                          : i32x4{0, 0, 0, 0};
     }
     __syncthreads();
     if (!active) continue;
-    for (int qt = 0; qt < nq; qt += 16) {
-      const int m = m0 + qt + i16;                 // this lane's query
-      i32x4 qv[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qv[s] = s_q[(qt + i16) * kQStride + 4 * s + g4];
-      const int Lm = L0 + m;
-      const int nblk = m < T && Lm > 0 ? (Lm + kTokensPerBlock - 1) / kTokensPerBlock : 0;
-      int pmax = (int)0x80000000;
-      int sc[4];   // blocks 4*g4 + tt of the page for query m
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        i32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(key[tt][s], qv[s], acc, 0, 0, 0);
-        const int pos = p * kPageSize + 16 * g4 + 4 * tt;   // first token of the block
-        if (causal)
-          sc[tt] = (pos < Lm ? acc[0] : 0) + (pos + 1 < Lm ? acc[1] : 0) + (pos + 2 < Lm ? acc[2] : 0) +
-                   (pos + 3 < Lm ? acc[3] : 0);
-        else
-          sc[tt] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        if (p * kBlocksPerPage + 4 * g4 + tt < nblk) pmax = max(pmax, sc[tt]);
-      }
-      const int blk0 = p * kBlocksPerPage + 4 * g4;
-      int32_t* row = scores + ((size_t)b * T + m) * max_blocks;
-      if (blk0 + 3 < nblk) {
-        *reinterpret_cast<i32x4*>(row + blk0) = i32x4{sc[0], sc[1], sc[2], sc[3]};
-      } else {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          if (blk0 + tt < nblk) row[blk0 + tt] = sc[tt];
-      }
-      if (page_max) {
-        pmax = max(pmax, __shfl_xor(pmax, 16, 64));
-        pmax = max(pmax, __shfl_xor(pmax, 32, 64));
-        if (g4 == 0 && m < T) page_max[((size_t)b * T + m) * max_pages + p] = pmax;
-      }
-    }
+    int* pm_slot = STAGE && page_max ? &s_pm[(m0 / kQueryChunk) & STAGE][STAGE ? wave : 0] : nullptr;
+    if (full)
+      score_query_tiles<WAVES, STAGE, true>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
+                                            pm_slot, page_max);
+    else
+      score_query_tiles<WAVES, STAGE, false>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
+                                             pm_slot, page_max);
+  }
+  if (STAGE && page_max) {
+    const int last = (T - 1) / kQueryChunk;        // the last chunk's maxima
+    __syncthreads();
+    flush_page_max(last & 1, last * kQueryChunk);
   }
 }
 
@@ -142,9 +208,15 @@ hipError_t launch_index_score_mq(const int8_t* q_idx, const int8_t* idx_cache, c
                                  const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                                  int32_t* page_max, int T, hipStream_t stream) {
   if (T < 1 || T > kMaxQueries) return hipErrorInvalidValue;
-  const unsigned gm = (unsigned)((max_pages + kMqWaves - 1) / kMqWaves);
-  hipLaunchKernelGGL(index_score_mq_kernel, dim3(gm, B), dim3(kMqWaves * 64), 0, stream, q_idx, idx_cache,
-                     page_table, lens, max_pages, max_blocks, T, scores, page_max);
+  if (T <= kQueryChunk) {
+    constexpr int W = 8;
+    hipLaunchKernelGGL((index_score_mq_kernel<W, false>), dim3((unsigned)((max_pages + W - 1) / W), B), dim3(W * 64),
+                       0, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, T, scores, page_max);
+  } else {
+    constexpr int W = 16;
+    hipLaunchKernelGGL((index_score_mq_kernel<W, true>), dim3((unsigned)((max_pages + W - 1) / W), B), dim3(W * 64),
+                       0, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, T, scores, page_max);
+  }
   return hipGetLastError();
 }
 
