@@ -278,7 +278,9 @@ size_t qsa_decode_multi_workspace_size(int B, int T, int Hq, int Hkv, int max_bl
 /* The multi-token decode's indexer scan on its own: scores (and, if page_max is not NULL,
  * per-page maxima [B*T, max_pages_per_seq]) of all T draft tokens of every request, from one
  * read of the indexer keys. q_idx [B, T, n_idx_heads, idx_dim]; block_scores [B*T, max_blocks];
- * row b*T + t holds draft token t's scores for blocks < ceil((L_b - T + 1 + t) / 4). Checks as
+ * row b*T + t holds draft token t's scores for blocks < ceil((L_b - T + 1 + t) / 4). Page
+ * maxima row b*T + t is written for the pages p < ceil(L_b/64) only: the largest of the
+ * token's scores there, INT32_MIN on a page where it has none. Checks as
  * qsa_index_score, plus 1 <= T <= 4096, B*T <= 65535, max_blocks % 4 == 0 and block_scores
  * 16-byte aligned. */
 qsa_status_t qsa_index_score_multi(const int8_t* q_idx, const int8_t* idx_cache,

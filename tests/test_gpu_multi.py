@@ -53,6 +53,40 @@ def test_multi_scan_alone_matches_chain():
             assert torch.equal(s[b * 3 + t, :n], plan.scores[b * 3 + t, :n]), (b, t)
 
 
+@pytest.mark.parametrize("T,lens", [(3, (3, 70, 2049)), (5, (70, 2049, 5000)), (64, (130, 5000)),
+                                    (65, (70, 300, 5000)), (130, (70, 2049, 9000)), (300, (301, 4000))])
+def test_scan_scores_and_page_maxima(T, lens):
+    """The multi-token scan alone, every token: scores against the oracle bit for bit, and
+    the page maxima, written for each page of the request's context as the largest score of
+    the token's visible blocks there (INT_MIN where it sees none) and nowhere past those pages.
+    T <= 4, up to 64 and above 64 are the scan's three forms; above 64 the maxima are folded in
+    LDS and written per 64-query chunk (T = 130, 300: a last partial chunk; the 70-token
+    request at T = 130: its first 60 tokens see nothing)."""
+    x = make_inputs(Workload("scan_pm", len(lens), ("list",) + tuple(lens), 32, 4, 2), 77 + T, "cuda")
+    _, qi = draft_queries(x, T, 77 + T)
+    say(f"[scan page maxima T={T}] lens={lens}")
+    mp = x.page_table.shape[1]
+    sentinel = 123456789
+    pm = torch.full((len(lens) * T, mp), sentinel, dtype=torch.int32, device="cuda")
+    s = qsa.index_score_multi(qi, x.idx_cache, x.page_table, x.context_lens, page_max=pm)
+    torch.cuda.synchronize()
+    s, pm, qn = s.cpu().numpy(), pm.cpu().numpy(), qi.cpu().numpy()
+    a = oracle_arrays(x)
+    for b, L in enumerate(lens):
+        npg = (L + 63) // 64
+        for t in range(T):
+            r = b * T + t
+            ref = oracle.index_scores(qn[b, t], a["idx_cache"], a["page_table"][b], oracle.draft_length(L, T, t))
+            assert np.array_equal(s[r, :len(ref)], ref), f"scores b{b} t{t}"
+            want = np.full(npg, np.iinfo(np.int32).min, dtype=np.int64)
+            for p in range(npg):
+                blk = ref[16 * p:16 * p + 16]
+                if len(blk):
+                    want[p] = blk.max()
+            assert np.array_equal(pm[r, :npg], want), f"page maxima b{b} t{t}"
+            assert np.all(pm[r, npg:] == sentinel), f"page maxima past the context b{b} t{t}"
+
+
 def test_one_draft_token_equals_decode():
     x = make_inputs(Workload("draft1", len(LENS), ("list",) + LENS, 32, 4, 3), 52, "cuda")
     q, qi = draft_queries(x, 1, 52)
