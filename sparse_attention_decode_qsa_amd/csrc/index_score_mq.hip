@@ -18,10 +18,13 @@ namespace qsa {
 // r = 4*g4 + v holds token 16*g4 + 4*tt + v, so the lane's rows are block 4*g4 + tt, the
 // block score is the sum of its four values, and over the four tiles the lane holds the four
 // consecutive blocks 4*g4 .. 4*g4+3 (one 16-byte store per lane; a query's 16 blocks of the
-// page are 64 contiguous bytes). Grid (page groups, B), one page per wave: the wave keeps its
-// page's 64 keys in registers in the A layout (16 loads of 16 bytes; lane i16 of tile tt:
-// token 16*(i16/4) + 4*tt + i16%4, bytes 64*s + 16*g4 .. +15) and runs every 16-query tile of
-// the request against them, so the keys are read once. The queries go through LDS in chunks
+// page are 64 contiguous bytes). Grid (page groups, B), one page per wave: the wave reads its
+// page's 64 keys with 16 loads of 1 KiB each (four whole token rows per load), passes them
+// once through its own LDS area into the A layout (lane i16 of tile tt, k-step s: token
+// 16*(i16/4) + 4*tt + i16%4, bytes 64*s + 16*g4 .. +15), keeps them in registers and runs
+// every 16-query tile of the request against them, so the keys are read once. Loading the A
+// layout directly would make every load 16 pieces of 64 bytes, 256 bytes apart; on this GPU
+// that made the scan 17-19% slower at up to 64 queries. The queries go through LDS in chunks
 // of kQueryChunk, loaded once per workgroup (the first chunk's loads are issued before the
 // keys', and the page id comes by a scalar load, so neither waits on the other). Causal
 // masking (query m sees tokens < L_b - T + 1 + m) is applied only on pages that reach into
@@ -108,6 +111,10 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
   // STAGE: page maxima of a chunk, word q * WAVES + w = query q of the chunk, page w of the
   // workgroup; two buffers, so that one chunk's words are written out while the next fills.
   __shared__ int s_pm[STAGE ? 2 : 1][STAGE ? kQueryChunk * WAVES : 1];
+  // Each wave's staging area for one token tile of its keys: 16 rows x 16 vectors, vector c of
+  // row r at r * 16 + (c ^ r), so that the 16 rows a lane group writes or reads at once fall
+  // in different banks.
+  __shared__ i32x4 s_k[WAVES][16 * 16];
   static_assert((kQueryChunk * kIdxTokenBytes / 16) % (WAVES * 64) == 0, "whole vectors per thread");
   static_assert(kQueryChunk % 64 == 0, "whole page-maximum words per thread");
   const int b = blockIdx.y;
@@ -138,18 +145,34 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
     const i32x4 v = reinterpret_cast<const i32x4*>(qrow0)[min(x, lim - 1)];
     q0[j] = x < lim ? v : i32x4{0, 0, 0, 0};
   }
+  // The page's keys, read contiguously: load j brings tokens 4j .. 4j+3 (1 KiB; lane l holds
+  // token 4j + l/16, bytes 16*(l%16) .. +15), and reaches the A layout through this wave's LDS
+  // area.
   i32x4 key[4][4];
+  i32x4 raw[16];
   if (active) {
-    const int8_t* base = idx_cache + (size_t)page * kIdxPageBytes + 16 * g4;
+    const int8_t* base = idx_cache + (size_t)page * kIdxPageBytes + 16 * lane;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int j = 0; j < 16; ++j)
+      raw[j] = 4 * j + (lane >> 4) < valid
+                   ? __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + j * 1024))
+                   : i32x4{0, 0, 0, 0};
+    // Token tile tt, MFMA row r = 4q + v: token 16q + 4tt + v, which load 4q + tt holds in lane
+    // 16v + c (vector c). Written to the wave's area, read back in the A layout (lane (i16, g4)
+    // of k-step s: row i16, vector 4s + g4). One wave's LDS operations run in order, so the
+    // next tile's writes follow this tile's reads.
+    i32x4* area = s_k[wave];
+    const int rw = lane >> 4, cw = lane & 15;   // write side: row within the group, vector
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int tok = 16 * (i16 >> 2) + 4 * tt + (i16 & 3);
-        key[tt][s] = tok < valid ? __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(
-                                       base + tok * kIdxTokenBytes + 64 * s))
-                                 : i32x4{0, 0, 0, 0};
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * q + rw;
+        area[r * 16 + (cw ^ r)] = raw[4 * q + tt];
       }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) key[tt][ks] = area[i16 * 16 + ((4 * ks + g4) ^ i16)];
+    }
   }
   constexpr int kPmPer = kQueryChunk / 64;         // page-maximum words per thread and chunk
   if (STAGE) {
