@@ -78,7 +78,7 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xFFFFu) | (hi16 << 16); }
 
 struct Tile {
-  bf16x8 k[4];   // K operand: token i16, dims 32s + 8*q4 .. +7
+  bf16x8 k[4];   // K rows as loaded: token 4*q4 + v, dims 8*i16 .. +7 (reshaped before use)
   u16x8 v[4];    // V rows: token 4*q4 + v, dims 8*i16 .. +7
   bool tv[4];    // token 4*q4 + v exists
   bool sv[4];    // (pair kernel) ... and is kept by the lane's column's new token
@@ -87,7 +87,8 @@ struct Tile {
 // Tile of 4 kept blocks starting at share slot bbase (share slots [0, nslot)); block ids and
 // the physical rows of their first tokens (page * 64 + row, below 2^32 for any cache that fits
 // in memory) come from LDS. kg and vg point at the lane's 16 bytes of row 0 of the caches
-// (KV head g; dims 8*q4 for K, 8*i16 for V), rs is the row stride in elements. A token past
+// (KV head g, dims 8*i16), rs is the row stride in elements: K and V are read alike, 256
+// contiguous bytes per token row and 4 rows per load. A token past
 // the share or at or past L (a poisoned or unrelated row) is not read: its lane loads the
 // row of the tile's first token instead (always present, so finite), and the token is marked
 // absent, which gives it a score of -inf and so a weight of exactly 0. Every lane loads, with
@@ -98,20 +99,15 @@ __device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const i
                                           const int* s_mask, int L, int Lc, int tk, const uint16_t* kg,
                                           const uint16_t* vg, uint32_t rs, int i16, int q4) {
   const uint32_t safe = s_ptok[bbase];   // token 0 of the tile's first block
-  {
-    const int slot = bbase + (i16 >> 2), cs = min(slot, nslot - 1);
-    const bool ok = slot < nslot && 4 * s_sel[cs] + (i16 & 3) < L;
-    const uint16_t* krow = kg + (size_t)(ok ? s_ptok[cs] + (i16 & 3) : safe) * rs;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) T.k[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
-  }
   const int slot = bbase + q4, cs = min(slot, nslot - 1);
   const int blk = slot < nslot ? s_sel[cs] : -1;
   const uint32_t row0 = s_ptok[cs];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     T.tv[v] = blk >= 0 && 4 * blk + v < L;
-    T.v[v] = *reinterpret_cast<const u16x8*>(vg + (size_t)(T.tv[v] ? row0 + v : safe) * rs);
+    const size_t row = (size_t)(T.tv[v] ? row0 + v : safe) * rs;
+    T.k[v] = *reinterpret_cast<const bf16x8*>(kg + row);
+    T.v[v] = *reinterpret_cast<const u16x8*>(vg + row);
   }
   if (PAIR) {
     const bool own = blk >= 0 && ((s_mask[cs] >> tk) & 1);
@@ -120,13 +116,30 @@ __device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const i
   }
 }
 
+// The tile's K rows into the MFMA A layout (lane (i16, q4) of k-step s: token i16, dims
+// 32s + 8*q4 .. +7) through the wave's 4 KiB LDS area: vector c (dims 8c .. 8c+7) of tile row
+// r (token 4*(r/4) + r%4 of the tile) at r * 16 + (c ^ r), so that the 16 rows a lane group
+// writes or reads at once fall in different banks. One wave's LDS operations run in order, so
+// a later tile's writes follow this tile's reads.
+__device__ __forceinline__ void k_operands(const Tile& T, bf16x8* area, int i16, int q4, bf16x8 (&ka)[4]) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * q4 + v;
+    area[r * 16 + (i16 ^ r)] = T.k[v];
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) ka[s] = area[i16 * 16 + ((4 * s + q4) ^ i16)];
+}
+
 // One tile into the wave's online softmax state (m_run, l_run in base-2 units; acc = O^T).
 template <bool PAIR>
 __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, float scale_log2, float& m_run,
-                                            float& l_run, f32x4* acc) {
+                                            float& l_run, f32x4* acc, bf16x8* karea, int i16, int q4) {
+  bf16x8 ka[4];
+  k_operands(T, karea, i16, q4, ka);
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.k[s], qa[s], sc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qa[s], sc, 0, 0, 0);
 
   float sv[4];
 #pragma unroll
@@ -175,12 +188,15 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
 // no duplication.
 template <bool PAIR>
 __device__ __forceinline__ void attend_two(const Tile& A, const Tile& B, const bf16x8* qa, float scale_log2,
-                                           float& m_run, float& l_run, f32x4* acc) {
+                                           float& m_run, float& l_run, f32x4* acc, bf16x8* karea, int i16, int q4) {
+  bf16x8 ka[4], kb[4];
+  k_operands(A, karea, i16, q4, ka);
+  k_operands(B, karea, i16, q4, kb);
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[s], qa[s], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(B.k[s], qa[s], sb, 0, 0, 0);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qa[s], sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[s], qa[s], sb, 0, 0, 0);
   }
   float sv[8];
 #pragma unroll
@@ -262,6 +278,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
   __shared__ float s_m[kAttnWaves][kMaxGroup];
   __shared__ float s_l[kAttnWaves][kMaxGroup];
   __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim + 4];
+  __shared__ bf16x8 s_kr[kAttnWaves][16 * 16];   // each wave's K reshaping area (k_operands)
 
   const int npages = (L + kPageSize - 1) / kPageSize;
   const int S = (npages + P - 1) / P;
@@ -321,7 +338,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
   }
   __syncthreads();
 
-  const uint16_t* kg = kc + (size_t)g * kHeadDim + 8 * q4;
+  const uint16_t* kg = kc + (size_t)g * kHeadDim + 8 * i16;
   const uint16_t* vg = vc + (size_t)g * kHeadDim + 8 * i16;
   const uint32_t rs = (uint32_t)Hkv * kHeadDim;
   float m_run = -INFINITY, l_run = 0.f;
@@ -339,8 +356,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int m = 0; m < kTilesInFlight; m += 2) {
       const int ti = r0 + kAttnWaves * m;
-      if (ti + kAttnWaves < nt) attend_two<false>(T[m], T[m + 1], qa, scale_log2, m_run, l_run, acc);
-      else if (ti < nt) attend_tile<false>(T[m], qa, scale_log2, m_run, l_run, acc);
+      if (ti + kAttnWaves < nt) attend_two<false>(T[m], T[m + 1], qa, scale_log2, m_run, l_run, acc, s_kr[wave], i16, q4);
+      else if (ti < nt) attend_tile<false>(T[m], qa, scale_log2, m_run, l_run, acc, s_kr[wave], i16, q4);
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -463,6 +480,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
   __shared__ float s_m[kAttnWaves][kMaxGroup];
   __shared__ float s_l[kAttnWaves][kMaxGroup];
   __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim + 4];
+  __shared__ bf16x8 s_kr[kAttnWaves][16 * 16];   // each wave's K reshaping area (k_operands)
 
   int jr[2][2];
   uint32_t pr[2][2];
@@ -575,7 +593,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) qa[s] = bf16x8{};
   }
-  const uint16_t* kg = kc + (size_t)g * kHeadDim + 8 * q4;
+  const uint16_t* kg = kc + (size_t)g * kHeadDim + 8 * i16;
   const uint16_t* vg = vc + (size_t)g * kHeadDim + 8 * i16;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[8];
@@ -592,8 +610,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
 #pragma unroll
     for (int mm = 0; mm < kTilesInFlight; mm += 2) {
       const int ti = r0 + wph * mm;
-      if (ti + wph < nt) attend_two<true>(Ts[mm], Ts[mm + 1], qa, scale_log2, m_run, l_run, acc);
-      else if (ti < nt) attend_tile<true>(Ts[mm], qa, scale_log2, m_run, l_run, acc);
+      if (ti + wph < nt) attend_two<true>(Ts[mm], Ts[mm + 1], qa, scale_log2, m_run, l_run, acc, s_kr[wave], i16, q4);
+      else if (ti < nt) attend_tile<true>(Ts[mm], qa, scale_log2, m_run, l_run, acc, s_kr[wave], i16, q4);
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
