@@ -271,6 +271,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
     if args.graph:
+        for r in range(sets):              # every set run eagerly once (the warm-up may cover fewer)
+            step(r)
+        torch.cuda.synchronize()
         ref = [(p.sel.clone(), p.out.clone()) for p in plans]
         graphs = []
         for r in range(sets):
