@@ -215,8 +215,8 @@ qsa_status_t qsa_decode(const void* q, const int8_t* q_idx, const int8_t* idx_ca
 
 /*
  * qsa_time_next_scan - measurement hook. The next launch of an indexer scan kernel made by
- * this thread (through qsa_index_score, qsa_decode, qsa_decode_noalloc, qsa_decode_multi
- * with T <= 4, or the side-cache scan of qsa_index_score_pooled, qsa_decode_pooled,
+ * this thread (through qsa_index_score, qsa_decode, qsa_decode_noalloc, qsa_decode_multi,
+ * qsa_index_score_multi, or the side-cache scan of qsa_index_score_pooled, qsa_decode_pooled,
  * qsa_decode_multi_pooled and qsa_decode_step_pooled) records start_event when the kernel begins executing and stop_event when it
  * ends (both hipEvent_t created with timing enabled, either may be NULL), so the kernel's own
  * duration can be read with hipEventElapsedTime, inside a chain, without marker packets
@@ -256,8 +256,9 @@ qsa_status_t qsa_decode_noalloc(const void* q, const int8_t* q_idx, const int8_t
 /*
  * qsa_decode_multi - multi-token decode: T new tokens per request, 1 <= T <= 4096, B*T <= 65535
  * (draft tokens of speculative decoding with a multi-token-prediction head, T <= 4, or a
- * prefill chunk). For T <= 4 the scan uses int8 dot products per query; for larger T it runs
- * as an int8 matrix product of the T queries with every page's keys on the matrix cores. From
+ * prefill chunk). The scan runs as an int8 matrix product of the T queries with every page's
+ * keys on the matrix cores, except for T = 1 and, on batches of fewer than 4,096 pages, for
+ * T <= 4, where it uses int8 dot products per query; the scores are the same integers. From
  * T = 16 on, at Hq = 8*Hkv, neighbouring new tokens share attention workgroups that read the
  * union of their kept blocks once; the results are defined exactly as below either way.
  *

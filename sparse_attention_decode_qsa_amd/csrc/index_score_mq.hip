@@ -6,6 +6,8 @@
 // query. With T new tokens per request (a prefill chunk), new token t is scored like a
 // single decode query at length L_b - (T-1-t) (it sees itself and the tokens before it),
 // into scores row b*T + t; the block score is the same integer as for one query.
+#include <hip/hip_ext.h>
+
 #include "qsa_device.h"
 
 namespace qsa {
@@ -36,6 +38,11 @@ namespace qsa {
 // run instead of 16 separate 4-byte stores, which took nearly as long as the 755 MB of
 // scores at T = 1024 on the 256K workload). On pages every query sees whole, a wave's four token tiles
 // run as independent MFMA chains with no masking.
+hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
+                              const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
+                              int32_t* page_max, int T, hipStream_t stream);   // index_score.hip
+void take_scan_events(hipEvent_t* start, hipEvent_t* stop);                   // index_score.hip
+constexpr long long kMqMinPages = 4096;   // batches from this many pages take the MFMA scan from T = 2
 constexpr int kQueryChunk = 64;    // queries staged in LDS at a time (17 KiB with padding)
 constexpr int kQStride = kIdxTokenBytes / 16 + 1;   // 16-byte vectors per staged query
 
@@ -227,20 +234,58 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
   }
 }
 
+namespace {
+template <int W, bool STAGE>
+void launch_mq_w(hipStream_t stream, hipEvent_t e0, hipEvent_t e1, const int8_t* q_idx, const int8_t* idx_cache,
+                 const int32_t* page_table, const int32_t* lens, int B, int max_pages, int max_blocks, int T,
+                 int32_t* scores, int32_t* page_max) {
+  const dim3 grid((unsigned)((max_pages + W - 1) / W), B);
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL((index_score_mq_kernel<W, STAGE>), grid, dim3(W * 64), 0, stream, e0, e1, 0, q_idx,
+                          idx_cache, page_table, lens, max_pages, max_blocks, T, scores, page_max);
+  else
+    hipLaunchKernelGGL((index_score_mq_kernel<W, STAGE>), grid, dim3(W * 64), 0, stream, q_idx, idx_cache,
+                       page_table, lens, max_pages, max_blocks, T, scores, page_max);
+}
+}  // namespace
+
+// start and stop, when not null, are recorded at the kernel's own start and end.
+hipError_t launch_index_score_mq(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
+                                 const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
+                                 int32_t* page_max, int T, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (T < 1 || T > kMaxQueries) return hipErrorInvalidValue;
+  if (T <= kQueryChunk)
+    launch_mq_w<8, false>(stream, start, stop, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, T,
+                          scores, page_max);
+  else
+    launch_mq_w<16, true>(stream, start, stop, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, T,
+                          scores, page_max);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_score_mq(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
                                  const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                                  int32_t* page_max, int T, hipStream_t stream) {
-  if (T < 1 || T > kMaxQueries) return hipErrorInvalidValue;
-  if (T <= kQueryChunk) {
-    constexpr int W = 8;
-    hipLaunchKernelGGL((index_score_mq_kernel<W, false>), dim3((unsigned)((max_pages + W - 1) / W), B), dim3(W * 64),
-                       0, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, T, scores, page_max);
-  } else {
-    constexpr int W = 16;
-    hipLaunchKernelGGL((index_score_mq_kernel<W, true>), dim3((unsigned)((max_pages + W - 1) / W), B), dim3(W * 64),
-                       0, stream, q_idx, idx_cache, page_table, lens, max_pages, max_blocks, T, scores, page_max);
-  }
-  return hipGetLastError();
+  return launch_index_score_mq(q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, scores, page_max, T,
+                               stream, nullptr, nullptr);
+}
+
+// The scan of T queries per request. One query, and 2 to 4 queries on small batches, go to the
+// int8 dot-product scan (index_score.hip), whose smaller workgroup forms spread a few pages
+// over many CUs; from 2 queries on a batch of 4,096 pages or more goes to the MFMA scan, which
+// reads the keys as whole 1 KiB pieces and takes its dot products off the vector ALUs (at the
+// 256K workload, 2 / 3 / 4 queries: 34.9 / 36.4 / 38.7 us with dot products, 32.9 / 33.3 /
+// 33.5 us on MFMA). A qsa_time_next_scan request is honoured by either.
+hipError_t launch_multi_scan(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
+                             const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
+                             int32_t* page_max, int T, hipStream_t stream) {
+  if (T == 1 || (T <= 4 && (long long)B * max_pages < kMqMinPages))
+    return launch_index_score(q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, scores, page_max, T,
+                              stream);
+  hipEvent_t e0, e1;
+  take_scan_events(&e0, &e1);
+  return launch_index_score_mq(q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, scores, page_max, T,
+                               stream, e0, e1);
 }
 
 }  // namespace qsa

@@ -13,6 +13,8 @@ static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES
 namespace qsa {
 hipError_t launch_index_score(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int,
                               int, int32_t*, int32_t*, int, hipStream_t);   // ..., T, stream
+hipError_t launch_multi_scan(const int8_t*, const int8_t*, const int32_t*, const int32_t*, int, int, int,
+                             int32_t*, int32_t*, int, hipStream_t);         // ..., T, stream
 void set_scan_events(hipEvent_t start, hipEvent_t stop);
 size_t topk_workspace_bytes(int B, int max_blocks);
 constexpr int kMaxSelBlocks = 262144;
@@ -131,7 +133,7 @@ qsa_status_t qsa_time_next_scan(void* start_event, void* stop_event) {
   return QSA_OK;
 }
 
-int qsa_version(void) { return 210; }   // 0.2.1: multi-token decode over the side cache
+int qsa_version(void) { return 220; }   // 0.2.2: the MFMA scan for 2-4 draft tokens on large batches
 
 qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
                              const int32_t* context_lens, int B, int n_idx_heads, int idx_dim,
@@ -259,8 +261,8 @@ qsa_status_t decode_chain(const void* q, const int8_t* q_idx, const int8_t* idx_
                                                     step ? step->idx_new : nullptr, step ? step->write : nullptr,
                                                     step ? step->k_cache : nullptr, step ? step->v_cache : nullptr,
                                                     step ? step->idx_cache : nullptr, Hkv, s, T, idx_cache)
-                        : launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
-                                             max_blocks, block_scores, page_max, T, s);
+                        : launch_multi_scan(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
+                                            max_blocks, block_scores, page_max, T, s);
   if (e == hipSuccess)
     e = launch_topk_select(block_scores, context_lens, page_max, BT, max_blocks, max_pages_per_seq, k,
                            sel_blocks, sel_count, T, s);
@@ -364,8 +366,8 @@ qsa_status_t qsa_index_score_multi(const int8_t* q_idx, const int8_t* idx_cache,
                                 max_pages_per_seq, max_blocks, block_scores);
   if (st != QSA_OK || B == 0) return st;
   if (max_blocks % 4 != 0 || misaligned(block_scores)) return QSA_ERR_SHAPE;   // 16-byte score stores
-  return hip_status(launch_index_score(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
-                                       max_blocks, block_scores, page_max, T, (hipStream_t)stream));
+  return hip_status(launch_multi_scan(q_idx, idx_cache, page_table, context_lens, B, max_pages_per_seq,
+                                      max_blocks, block_scores, page_max, T, (hipStream_t)stream));
 }
 
 size_t qsa_decode_multi_workspace_size(int B, int T, int Hq, int Hkv, int max_blocks, int k, int P) {

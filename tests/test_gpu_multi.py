@@ -87,6 +87,33 @@ def test_scan_scores_and_page_maxima(T, lens):
             assert np.all(pm[r, npg:] == sentinel), f"page maxima past the context b{b} t{t}"
 
 
+@pytest.mark.parametrize("T", [2, 4, 64])
+def test_time_next_scan_multi(T):
+    """qsa_time_next_scan with qsa_decode_multi on a batch of more than 4,096 pages (the MFMA scan
+    from T = 2 on): the next call's scan records a positive duration below the whole calls', the
+    hook is used once, and the results are unchanged."""
+    lens = (140000, 130000)
+    x = make_inputs(Workload("timed_multi", 2, ("list",) + lens, 32, 4, 4), 58 + T, "cuda")
+    assert x.batch * x.page_table.shape[1] >= 4096
+    q, qi = draft_queries(x, T, 58 + T)
+    plan, _ = _run(x, q, qi, 4)
+    ref = [t.clone() for t in (plan.scores, plan.sel, plan.out)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    ev[2].record()
+    qsa.time_next_scan(ev[0], ev[1])
+    plan.run()
+    plan.run()
+    ev[3].record()
+    torch.cuda.synchronize()
+    scan_ms, all_ms = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    assert 0.0 < scan_ms < all_ms, (scan_ms, all_ms)
+    for u, v in zip(ref, (plan.scores, plan.sel, plan.out)):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
 def test_one_draft_token_equals_decode():
     x = make_inputs(Workload("draft1", len(LENS), ("list",) + LENS, 32, 4, 3), 52, "cuda")
     q, qi = draft_queries(x, 1, 52)
