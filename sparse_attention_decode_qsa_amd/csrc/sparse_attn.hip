@@ -89,30 +89,35 @@ struct Tile {
 // in memory) come from LDS. kg and vg point at the lane's 16 bytes of row 0 of the caches
 // (KV head g, dims 8*i16), rs is the row stride in elements: K and V are read alike, 256
 // contiguous bytes per token row and 4 rows per load. A token past
-// the share or at or past L (a poisoned or unrelated row) is not read: its lane loads the
-// row of the tile's first token instead (always present, so finite), and the token is marked
-// absent, which gives it a score of -inf and so a weight of exactly 0. Every lane loads, with
+// the share or at or past L (a poisoned or unrelated row) is not read: its lane loads row 0
+// of its block instead (past the share, of the share's last block; always present, so
+// finite), and the token is marked absent, which gives it a score of -inf and so a weight
+// of exactly 0. Every lane loads, with
 // no branch. PAIR: the lane's column belongs to new token tk of a pair, of length Lc <= L,
 // which keeps a block of the share when bit tk of its s_mask entry is set.
 template <bool PAIR>
 __device__ __forceinline__ void load_tile(Tile& T, int bbase, int nslot, const int* s_sel, const uint32_t* s_ptok,
                                           const int* s_mask, int L, int Lc, int tk, const uint16_t* kg,
                                           const uint16_t* vg, uint32_t rs, int i16, int q4) {
-  const uint32_t safe = s_ptok[bbase];   // token 0 of the tile's first block
   const int slot = bbase + q4, cs = min(slot, nslot - 1);
   const int blk = slot < nslot ? s_sel[cs] : -1;
-  const uint32_t row0 = s_ptok[cs];
+  // Row 0 of the lane's block (of the share's last block past the share) always exists below
+  // L; a token that is absent reads it again. One 64-bit product per tile, then 32-bit steps.
+  const int nv = blk >= 0 ? L - 4 * blk : 0;     // the block's tokens below L (if > 3, all 4)
+  const size_t off0 = (size_t)s_ptok[cs] * (2u * rs);
+  const char* kp = reinterpret_cast<const char*>(kg) + off0;
+  const char* vp = reinterpret_cast<const char*>(vg) + off0;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    T.tv[v] = blk >= 0 && 4 * blk + v < L;
-    const size_t row = (size_t)(T.tv[v] ? row0 + v : safe) * rs;
-    T.k[v] = *reinterpret_cast<const bf16x8*>(kg + row);
-    T.v[v] = *reinterpret_cast<const u16x8*>(vg + row);
+    T.tv[v] = v < nv;
+    const uint32_t d = T.tv[v] ? v * 2u * rs : 0u;
+    T.k[v] = *reinterpret_cast<const bf16x8*>(kp + d);
+    T.v[v] = *reinterpret_cast<const u16x8*>(vp + d);
   }
   if (PAIR) {
-    const bool own = blk >= 0 && ((s_mask[cs] >> tk) & 1);
+    const int nc = (blk >= 0 && ((s_mask[cs] >> tk) & 1)) ? Lc - 4 * blk : 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) T.sv[v] = own && 4 * blk + v < Lc;
+    for (int v = 0; v < 4; ++v) T.sv[v] = v < nc;
   }
 }
 
