@@ -136,6 +136,8 @@ __device__ __forceinline__ void k_operands(const Tile& T, bf16x8* area, int i16,
   for (int s = 0; s < 4; ++s) ka[s] = area[i16 * 16 + ((4 * s + q4) ^ i16)];
 }
 
+constexpr float kRescaleSlack = 8.f;   // log2 of the largest weight summed against a stale maximum
+
 // One tile into the wave's online softmax state (m_run, l_run in base-2 units; acc = O^T).
 template <bool PAIR>
 __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, float scale_log2, float& m_run,
@@ -152,10 +154,12 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
   float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float m_new = fmaxf(m_run, mt);
-  // The state is rescaled only when some lane's maximum moved (a wave-uniform branch):
-  // otherwise the factor is exp2(0) = 1 exactly and the multiplications would change no bit.
-  if (__ballot(m_new != m_run)) {
+  // The reference maximum moves only when some lane's tile maximum exceeds it by more than
+  // kRescaleSlack (a wave-uniform branch); until then weights up to 2^kRescaleSlack are summed
+  // against the old reference, which the final division by l_run cancels (l_run and acc share
+  // it), so the state is rescaled about once per share instead of whenever a maximum moves.
+  if (__ballot(mt > m_run + kRescaleSlack)) {
+    const float m_new = fmaxf(m_run, mt);
     const float alpha = exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
     l_run *= alpha;
 #pragma unroll
@@ -163,7 +167,7 @@ __device__ __forceinline__ void attend_tile(const Tile& T, const bf16x8* qa, flo
     m_run = m_new;
   }
   const float m_use = m_run == -INFINITY ? 0.f : m_run;
-  // p = 2^(s - m) <= 1 on v_exp_f32; P enters the PV product as a bf16 pair (hi = bf16(p),
+  // p = 2^(s - m) <= 2^kRescaleSlack on v_exp_f32; P enters the PV product as a bf16 pair (hi = bf16(p),
   // lo = bf16(p - hi)), so the weights keep ~16 bits.
   float pv[4];
 #pragma unroll
@@ -212,8 +216,8 @@ __device__ __forceinline__ void attend_two(const Tile& A, const Tile& B, const b
   float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float m_new = fmaxf(m_run, mt);
-  if (__ballot(m_new != m_run)) {   // as in attend_tile
+  if (__ballot(mt > m_run + kRescaleSlack)) {   // as in attend_tile
+    const float m_new = fmaxf(m_run, mt);
     const float alpha = exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
     l_run *= alpha;
 #pragma unroll
