@@ -50,6 +50,9 @@ namespace qsa {
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kTilesInFlight = 4;        // tiles whose loads a wave issues before computing
+constexpr int kPairTilesInFlight = 2;    // the same in the pair kernel (3 waves per SIMD)
+constexpr int kPairAreaBytes = std::max(std::max(2 * 2 * kMaxK * 4, kAttnWaves * kMaxGroup * (kHeadDim + 4) * 4),
+                                        kAttnWaves * 16 * 16 * 16);
 constexpr int kAttnTargetGroups = 512;   // two workgroups per CU
 constexpr int kMaxSplit = 32;            // shares per slice (tiny batches: one request, few heads)
 constexpr int kPairMinTokens = 16;       // chunks of at least this many new tokens use the pair kernel
@@ -448,8 +451,10 @@ __device__ __forceinline__ int lower_bound_lds(const int* a, int n, int v) {
 // kernel's, per virtual request. The union, its rows and masks are built once for the hpw KV
 // heads (1, 2 or 4): 4/hpw waves per head split the tiles and merge through LDS, or with one
 // wave per head the wave writes its head's partial from its registers. Grid
-// (C * (Hkv/hpw) * ceil(T/2), P, B_req).
-__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
+// (C * (Hkv/hpw) * ceil(T/2), P, B_req). Three workgroups per CU (three waves per SIMD): a
+// wave loads kPairTilesInFlight tiles ahead, and one LDS area serves the union build, the K
+// reshaping and the final merge in turn.
+__global__ __launch_bounds__(kAttnThreads, 3) void sparse_attn_pair_kernel(   // 3 waves per SIMD
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int Hq, int Hkv,
@@ -481,15 +486,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
 
   __shared__ int s_cnt[kAttnWaves][2][2];
   __shared__ int s_tmp[kAttnWaves];
-  __shared__ int s_run[2][kMaxK];       // each token's kept ids inside its slice p
-  __shared__ uint32_t s_runp[2][kMaxK]; // and the physical rows of their first tokens
   __shared__ int s_sel[2 * kMaxK];      // the share's part of the union of the two runs
   __shared__ uint32_t s_ptok[2 * kMaxK];
   __shared__ int s_mask[2 * kMaxK];     // bit i: token i keeps the block
   __shared__ float s_m[kAttnWaves][kMaxGroup];
   __shared__ float s_l[kAttnWaves][kMaxGroup];
-  __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim + 4];
-  __shared__ bf16x8 s_kr[kAttnWaves][16 * 16];   // each wave's K reshaping area (k_operands)
+  // One area for three uses that a barrier separates: each token's run while the union is
+  // built, the waves' K reshaping areas in the tile loop, the wave partials in the final
+  // merge. Sharing it keeps the workgroup at 47 KB of LDS, so three fit on a CU.
+  __shared__ __attribute__((aligned(16))) unsigned char s_area[kPairAreaBytes];
+  int (*s_run)[kMaxK] = reinterpret_cast<int (*)[kMaxK]>(s_area);            // kept ids in slice p
+  uint32_t (*s_runp)[kMaxK] = reinterpret_cast<uint32_t (*)[kMaxK]>(s_area + 2 * kMaxK * 4);  // their rows
+  bf16x8 (*s_kr)[16 * 16] = reinterpret_cast<bf16x8 (*)[16 * 16]>(s_area);
+  float (*s_o)[kMaxGroup][kHeadDim + 4] = reinterpret_cast<float (*)[kMaxGroup][kHeadDim + 4]>(s_area);
 
   int jr[2][2];
   uint32_t pr[2][2];
@@ -608,16 +617,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
   f32x4 acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r0 = sub; r0 < nt; r0 += wph * kTilesInFlight) {
-    Tile Ts[kTilesInFlight];
+  for (int r0 = sub; r0 < nt; r0 += wph * kPairTilesInFlight) {
+    Tile Ts[kPairTilesInFlight];
 #pragma unroll
-    for (int mm = 0; mm < kTilesInFlight; ++mm) {
+    for (int mm = 0; mm < kPairTilesInFlight; ++mm) {
       const int ti = r0 + wph * mm;
       if (ti < nt)
         load_tile<true>(Ts[mm], 4 * ti, nslot, s_sel, s_ptok, s_mask, Lmax, Lc, tk, kg, vg, rs, i16, q4);
     }
 #pragma unroll
-    for (int mm = 0; mm < kTilesInFlight; mm += 2) {
+    for (int mm = 0; mm < kPairTilesInFlight; mm += 2) {
       const int ti = r0 + wph * mm;
       if (ti + wph < nt) attend_two<true>(Ts[mm], Ts[mm + 1], qa, scale_log2, m_run, l_run, acc, s_kr[wave], i16, q4);
       else if (ti < nt) attend_tile<true>(Ts[mm], qa, scale_log2, m_run, l_run, acc, s_kr[wave], i16, q4);
@@ -646,7 +655,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_pair_kernel(
     }
     return;
   }
-  // Several waves per head: their partials merge through LDS, as in the single-token kernel.
+  // Several waves per head: their partials merge through LDS, as in the single-token kernel,
+  // once every wave is done with its reshaping area (the same LDS).
+  __syncthreads();
   if (q4 == 0) { s_m[wave][i16] = m_run; s_l[wave][i16] = l_tot; }
 #pragma unroll
   for (int u = 0; u < 8; ++u)
