@@ -23,24 +23,28 @@
 // the K/V rows are the ids and the page-table entries. The share's ids and the physical rows
 // of their blocks' first tokens go to LDS; tiles are dealt round-robin to the waves;
 // a wave issues the loads of up to kTilesInFlight tiles before it computes on the first,
-// and keeps an online softmax over its tiles. The 4 wave partials are merged in one LDS
-// round, each thread finishing 8 output dims of one query head.
+// and keeps an online softmax over its tiles, two at a time where it has two. The 4 wave
+// partials are merged in one LDS round, each thread finishing 8 output dims of one query head.
 //
 // Per wave and tile (lane = 16*q4 + i16):
-//   S = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 dims of K, loaded straight
-//   from the paged cache (lane: token i16, dims 32s + 8*q4 .. +7), B = 32 dims x 16
-//   query heads of the KV head's group (rows past the group are zero). The result gives
-//   lane (q4, i16) the scores of tokens 4*q4 .. 4*q4+3 (= kept block q4 of the tile) for
+//   K and V rows are loaded alike, 16 bytes per lane (lane: token 4*q4 + v of the tile, dims
+//   8*i16 .. +7), so each load reads four whole 256-byte token rows.
+//   S = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 dims of K, reshaped from the
+//   loaded rows through the wave's LDS area (lane: token i16, dims 32s + 8*q4 .. +7), B = 32
+//   dims x 16 query heads of the KV head's group (rows past the group are zero). The result
+//   gives lane (q4, i16) the scores of tokens 4*q4 .. 4*q4+3 (= kept block q4 of the tile) for
 //   query head i16.
-//   O^T += V^T P on v_mfma_f32_16x16x32_bf16 with k = 32 slots = the lane's 4 tokens
-//   twice: P enters as a bf16 pair (hi, lo = p - hi), so the weights keep ~16 bits;
-//   V rows are loaded 16 bytes per lane (lane: token 4*q4+v, dims 8*i16 .. +7) and
-//   MFMA tile u (u = 0..7) takes dim 8*i16 + u as its row i16. A lane then ends up with
+//   O^T += V^T P on v_mfma_f32_16x16x32_bf16, MFMA tile u (u = 0..7) taking dim 8*i16 + u as
+//   its row i16, so the V rows need no transpose; the 32 k-slots are the lane's 8 tokens of
+//   two tiles (or its 4 tokens twice), and P enters as a bf16 pair (hi, lo = p - hi), two
+//   products with the same V operand, so the weights keep ~16 bits. A lane then ends up with
 //   query head i16 and dims 32*q4 .. 32*q4+31 of the output, contiguous.
-//   The dot products are exact bf16 products accumulated in fp32; softmax in fp32
-//   (base-2 exponent with the scale folded in).
-// Masked tokens (past the share or past L_b) are never loaded: their K and V registers
-// stay zero and their scores are -inf, so NaN rows cannot leak in.
+//   The dot products are exact bf16 products accumulated in fp32; softmax in fp32 (base-2
+//   exponent with the scale folded in, the reference maximum moved only when a maximum grows
+//   by more than 2^8).
+// Absent tokens (past the share or at or past L_b) are not read: their lanes read row 0 of
+// their own block again (present and finite), and their scores are -inf, so their weights
+// are exactly 0 and no NaN row of a poisoned page can leak in.
 #include <algorithm>
 
 #include "qsa_device.h"
