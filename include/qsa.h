@@ -18,6 +18,8 @@
  * (or qsa_decode, which runs the four on one stream). The indexer's side cache of pooled keys
  * (qsa_pool_build, qsa_cache_append, qsa_index_score_pooled, qsa_decode_pooled,
  * qsa_decode_multi_pooled) gives the same chain with a scan that reads half the bytes.
+ * Several new tokens per request (draft tokens of speculative decoding, prefill chunks) run
+ * through qsa_decode_multi and qsa_index_score_multi, each token decoded at its own length.
  *
  * Conventions for every entry point
  *   Memory     every pointer is device memory of the current HIP device, unless noted.
@@ -51,7 +53,8 @@
  *              kernel reads was written earlier in the same call, so a workspace needs no
  *              initialisation and keeps nothing between calls. Calls that share a
  *              workspace must not overlap in time.
- *   Threads    stateless and re-entrant apart from the thread-local qsa_last_hip_error.
+ *   Threads    stateless and re-entrant apart from the thread-local qsa_last_hip_error and
+ *              the thread-local request of qsa_time_next_scan.
  */
 #ifndef QSA_H_
 #define QSA_H_
