@@ -97,7 +97,7 @@ __device__ __forceinline__ void score_query_tiles(const i32x4 (&key)[4][4], cons
           if (blk0 + tt < nblk) row[blk0 + tt] = sc[tt];
       }
     }
-    if (STAGE) {
+    if constexpr (STAGE) {
       if (pm_slot && m < T) atomicMax(pm_slot + (qt + i16) * WAVES, pmax);
     } else if (page_max) {
       pmax = max(pmax, __shfl_xor(pmax, 16, 64));
@@ -182,19 +182,21 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
     }
   }
   constexpr int kPmPer = kQueryChunk / 64;         // page-maximum words per thread and chunk
-  if (STAGE) {
+  if constexpr (STAGE) {
 #pragma unroll
     for (int j = 0; j < kPmPer; ++j)
-      s_pm[0][threadIdx.x + WAVES * 64 * j] = s_pm[STAGE][threadIdx.x + WAVES * 64 * j] = (int)0x80000000;
+      s_pm[0][threadIdx.x + WAVES * 64 * j] = s_pm[1][threadIdx.x + WAVES * 64 * j] = (int)0x80000000;
   }
   // Writes out the page maxima of the chunk starting at query c0 (buffer buf) and clears them.
   auto flush_page_max = [&](int buf, int c0) {
+    if constexpr (STAGE) {
 #pragma unroll
-    for (int j = 0; j < kPmPer; ++j) {
-      const int w = threadIdx.x + WAVES * 64 * j;
-      const int m = c0 + w / WAVES, pg = blockIdx.x * WAVES + w % WAVES;
-      if (m < T && pg < npages) page_max[((size_t)b * T + m) * max_pages + pg] = s_pm[buf][w];
-      s_pm[buf][w] = (int)0x80000000;
+      for (int j = 0; j < kPmPer; ++j) {
+        const int w = threadIdx.x + WAVES * 64 * j;
+        const int m = c0 + w / WAVES, pg = blockIdx.x * WAVES + w % WAVES;
+        if (m < T && pg < npages) page_max[((size_t)b * T + m) * max_pages + pg] = s_pm[buf][w];
+        s_pm[buf][w] = (int)0x80000000;
+      }
     }
   };
   const int L0 = L - T + 1;                        // query 0 sees tokens < L0
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
       }
     } else {
       __syncthreads();                             // the previous chunk is no longer read
-      if (STAGE && page_max) flush_page_max(((m0 / kQueryChunk) - 1) & 1, m0 - kQueryChunk);
+      if (page_max) flush_page_max(((m0 / kQueryChunk) - 1) & 1, m0 - kQueryChunk);   // a no-op unless STAGE
       for (int x = threadIdx.x; x < kQVecs; x += WAVES * 64)
         s_q[(x >> 4) * kQStride + (x & 15)] =
             x < nq * kIdxTokenBytes / 16 ? reinterpret_cast<const i32x4*>(qrow0 + (size_t)m0 * kIdxTokenBytes)[x]
@@ -219,7 +221,10 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
     }
     __syncthreads();
     if (!active) continue;
-    int* pm_slot = STAGE && page_max ? &s_pm[(m0 / kQueryChunk) & STAGE][STAGE ? wave : 0] : nullptr;
+    int* pm_slot = nullptr;
+    if constexpr (STAGE) {
+      if (page_max) pm_slot = &s_pm[(m0 / kQueryChunk) & 1][wave];
+    }
     if (full)
       score_query_tiles<WAVES, STAGE, true>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
                                             pm_slot, page_max);
@@ -227,10 +232,12 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
       score_query_tiles<WAVES, STAGE, false>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
                                              pm_slot, page_max);
   }
-  if (STAGE && page_max) {
-    const int last = (T - 1) / kQueryChunk;        // the last chunk's maxima
-    __syncthreads();
-    flush_page_max(last & 1, last * kQueryChunk);
+  if constexpr (STAGE) {
+    if (page_max) {
+      const int last = (T - 1) / kQueryChunk;      // the last chunk's maxima
+      __syncthreads();
+      flush_page_max(last & 1, last * kQueryChunk);
+    }
   }
 }
 
