@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from sparse_attention_decode_qsa_amd import qsa
-from sparse_attention_decode_qsa_amd.inputs import PAGE_SIZE, WORKLOADS, Workload, make_inputs
+from sparse_attention_decode_qsa_amd.inputs import PAGE_SIZE, WORKLOADS, Workload, draft_queries, make_inputs
 from tests.helpers import ATOL, RTOL, oracle_decode, tolerance_report
 
 pytestmark = pytest.mark.gpu
@@ -296,6 +296,34 @@ def test_repeat_is_bitwise_and_workspace_is_reusable():
              lse=plan.out_lse.cpu().numpy())
     for b, r in enumerate(refs):
         check_request(g, b, r, x.lengths[b], what="plan")
+
+
+def test_concurrent_calls_on_two_streams():
+    """Calls only enqueue work on the stream they are given and keep no state between calls:
+    a single-token plan and a multi-token plan, each with its own workspace, run repeatedly
+    and interleaved on two side streams give exactly the results of one call each on the
+    default stream."""
+    x = make_inputs(W("streams_a", (70000, 3000, 20000), P=4), 21, "cuda")
+    y = make_inputs(W("streams_b", (40000, 9000), P=2), 22, "cuda")
+    qy, qiy = draft_queries(y, 20, 22)
+    a = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 4)
+    m = qsa.MultiDecodePlan(qy, qiy, y.idx_cache, y.k_cache, y.v_cache, y.page_table, y.context_lens, 2)
+    a.run()
+    m.run()
+    torch.cuda.synchronize()
+    ra = [t.clone() for t in (a.scores, a.sel, a.out, a.out_lse)]
+    rm = [t.clone() for t in (m.scores, m.sel, m.out, m.out_lse)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            a.run()
+        with torch.cuda.stream(s2):
+            m.run()
+    torch.cuda.synchronize()
+    for u, v in zip(ra, (a.scores, a.sel, a.out, a.out_lse)):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+    for u, v in zip(rm, (m.scores, m.sel, m.out, m.out_lse)):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
 
 
 # ----------------------------------------------- full-size workloads, every request
