@@ -1,10 +1,12 @@
 /* A standalone C user of libqsa: builds a small paged batch on the host, copies it to the
- * device with the HIP runtime, runs qsa_decode on the null stream and writes inputs and
- * results as raw little-endian files into the directory given as argv[1]:
+ * device with the HIP runtime, runs qsa_decode and then qsa_decode_multi (TD = 3 new tokens per
+ * request, the last three positions of each context) on the null stream and writes inputs
+ * and results as raw little-endian files into the directory given as argv[1]:
  *   meta.txt    B Hq Hkv P NP max_pages max_blocks k, then the B lengths
  *   q.bin (bf16 bits), q_idx.bin, idx_cache.bin, k_cache.bin, v_cache.bin (bf16 bits),
  *   page_table.bin, scores.bin, sel.bin, sel_count.bin, partial_out.bin, partial_lse.bin,
- *   out.bin, out_lse.bin
+ *   out.bin, out_lse.bin; for the multi-token call m_q.bin, m_q_idx.bin, m_scores.bin,
+ *   m_sel.bin, m_sel_count.bin, m_out.bin (rows b*TD + t)
  * Rows of a request's last page past its length hold NaN K/V and indexer keys of 127. */
 #include <math.h>
 #include <stdint.h>
@@ -23,6 +25,7 @@
 #define D 128
 #define PAGE 64
 #define KMAX 512
+#define TD 3
 
 static const int lens[B] = {9000, 700, 2049};
 
@@ -154,8 +157,8 @@ int main(int argc, char** argv) {
 
   const char* dir = argv[1];
   char meta[256];
-  snprintf(meta, sizeof meta, "%d %d %d %d %d %d %d %d %d %d %d\n", B, HQ, HKV, P, NP, max_pages, max_blocks, KMAX,
-           lens[0], lens[1], lens[2]);
+  snprintf(meta, sizeof meta, "%d %d %d %d %d %d %d %d %d %d %d %d\n", B, HQ, HKV, P, NP, max_pages, max_blocks, KMAX,
+           TD, lens[0], lens[1], lens[2]);
   if (dump(dir, "meta.txt", meta, strlen(meta)) || dump(dir, "q.bin", q, 2 * nq) || dump(dir, "q_idx.bin", qi, nqi) ||
       dump(dir, "idx_cache.bin", idx, nidx) || dump(dir, "k_cache.bin", kc, 2 * nkv) ||
       dump(dir, "v_cache.bin", vc, 2 * nkv) || dump(dir, "page_table.bin", pt, 4 * (size_t)B * max_pages) ||
@@ -163,6 +166,45 @@ int main(int argc, char** argv) {
       dump(dir, "sel_count.bin", cnt, 4 * B) || dump(dir, "partial_out.bin", po, 4 * (size_t)B * P * HQ * D) ||
       dump(dir, "partial_lse.bin", pl, 4 * (size_t)B * P * HQ) || dump(dir, "out.bin", out, 4 * (size_t)B * HQ * D) ||
       dump(dir, "out_lse.bin", lse, 4 * (size_t)B * HQ))
+    return 3;
+  /* multi-token decode: TD new tokens per request, its own queries, workspace and outputs */
+  const size_t mq = (size_t)B * TD * HQ * D, mqi = (size_t)B * TD * 256, BT = (size_t)B * TD;
+  uint16_t* q2 = malloc(2 * mq);
+  int8_t* qi2 = malloc(mqi);
+  for (size_t i = 0; i < mq; ++i) q2[i] = to_bf16(uniform());
+  for (size_t i = 0; i < mqi; ++i) qi2[i] = int8v();
+  void *d_q2, *d_qi2, *d_s2, *d_sel2, *d_cnt2, *d_po2, *d_pl2, *d_out2, *d_ws2 = NULL;
+  const size_t ws2 = qsa_decode_multi_workspace_size(B, TD, HQ, HKV, max_blocks, KMAX, P);
+  HIP_OK(hipMalloc(&d_q2, 2 * mq));
+  HIP_OK(hipMalloc(&d_qi2, mqi));
+  HIP_OK(hipMalloc(&d_s2, 4 * BT * max_blocks));
+  HIP_OK(hipMalloc(&d_sel2, 4 * BT * KMAX));
+  HIP_OK(hipMalloc(&d_cnt2, 4 * BT));
+  HIP_OK(hipMalloc(&d_po2, 4 * BT * P * HQ * D));
+  HIP_OK(hipMalloc(&d_pl2, 4 * BT * P * HQ));
+  HIP_OK(hipMalloc(&d_out2, 4 * BT * HQ * D));
+  if (ws2) HIP_OK(hipMalloc(&d_ws2, ws2));
+  HIP_OK(hipMemcpy(d_q2, q2, 2 * mq, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_qi2, qi2, mqi, hipMemcpyHostToDevice));
+  st = qsa_decode_multi(d_q2, d_qi2, d_idx, d_k, d_v, d_pt, d_len, B, TD, HQ, HKV, D, 4, 64, PAGE, max_pages,
+                        max_blocks, KMAX, P, scale, d_s2, d_sel2, d_cnt2, d_po2, d_pl2, d_out2, NULL, d_ws2, ws2,
+                        NULL);
+  if (st != QSA_OK) {
+    fprintf(stderr, "qsa_decode_multi: %s (hip %d)\n", qsa_status_string(st), qsa_last_hip_error());
+    return 1;
+  }
+  HIP_OK(hipDeviceSynchronize());
+  int32_t* s2 = malloc(4 * BT * max_blocks);
+  int32_t* sel2 = malloc(4 * BT * KMAX);
+  int32_t* cnt2 = malloc(4 * BT);
+  float* out2 = malloc(4 * BT * HQ * D);
+  HIP_OK(hipMemcpy(s2, d_s2, 4 * BT * max_blocks, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(sel2, d_sel2, 4 * BT * KMAX, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(cnt2, d_cnt2, 4 * BT, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(out2, d_out2, 4 * BT * HQ * D, hipMemcpyDeviceToHost));
+  if (dump(dir, "m_q.bin", q2, 2 * mq) || dump(dir, "m_q_idx.bin", qi2, mqi) ||
+      dump(dir, "m_scores.bin", s2, 4 * BT * max_blocks) || dump(dir, "m_sel.bin", sel2, 4 * BT * KMAX) ||
+      dump(dir, "m_sel_count.bin", cnt2, 4 * BT) || dump(dir, "m_out.bin", out2, 4 * BT * HQ * D))
     return 3;
   printf("ok %s\n", qsa_status_string(st));
   return 0;

@@ -1,6 +1,6 @@
 """A C program, not Python, drives the library: tests/c/decode_from_c.c allocates with the HIP
-runtime, fills a small paged batch on the host, calls qsa_decode and dumps inputs and
-results. The CPU test checks that it compiles and links with gcc against include/qsa.h; the
+runtime, fills a small paged batch on the host, calls qsa_decode and qsa_decode_multi and
+dumps inputs and results. The CPU test checks that it compiles and links with gcc against include/qsa.h; the
 GPU test runs it and compares every result with the oracle on the inputs it wrote."""
 import os
 import shutil
@@ -54,8 +54,8 @@ def test_c_program_decode_matches_oracle(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip() == "ok ok"
     meta = [int(v) for v in (out_dir / "meta.txt").read_text().split()]
-    B, Hq, Hkv, P, NP, max_pages, max_blocks, k = meta[:8]
-    lens = meta[8:8 + B]
+    B, Hq, Hkv, P, NP, max_pages, max_blocks, k, TD = meta[:9]
+    lens = meta[9:9 + B]
     D, page = 128, 64
     d = str(out_dir)
     q = _load(d, "q.bin", np.uint16, (B, Hq, D))
@@ -89,4 +89,22 @@ def test_c_program_decode_matches_oracle(tmp_path):
             ok, ma, mr = tolerance_report(got[fin], want[fin], ATOL, RTOL)
             assert ok, f"{name} outside tolerance (b={b}, max abs {ma:.3g}, max rel {mr:.3g})"
         print(f"request {b} L={L}: kept {K} blocks, parity ok", flush=True)
+    # the multi-token call: TD new tokens per request, each decoded at its own length
+    mq = _load(d, "m_q.bin", np.uint16, (B, TD, Hq, D))
+    mqi = _load(d, "m_q_idx.bin", np.int8, (B, TD, 4, 64))
+    ms = _load(d, "m_scores.bin", np.int32, (B * TD, max_blocks))
+    msel = _load(d, "m_sel.bin", np.int32, (B * TD, k))
+    mcnt = _load(d, "m_sel_count.bin", np.int32, (B * TD,))
+    mout = _load(d, "m_out.bin", np.float32, (B * TD, Hq, D))
+    refs = oracle.decode_multi(mq, mqi, idx, kc, vc, pt, lens, TD, P, float(scale), k)
+    for b, L in enumerate(lens):
+        for t in range(TD):
+            r, ref = b * TD + t, refs[b * TD + t]
+            Lt = oracle.draft_length(L, TD, t)
+            assert np.array_equal(ms[r, :(Lt + 3) // 4], ref["scores"]), f"multi scores (b={b}, t={t})"
+            K = len(ref["kept"])
+            assert mcnt[r] == K and np.array_equal(msel[r, :K], ref["kept"]) and np.all(msel[r, K:] == -1)
+            ok, ma, mr = tolerance_report(mout[r], ref["out"], ATOL, RTOL)
+            assert ok, f"multi out outside tolerance (b={b}, t={t}, max abs {ma:.3g}, max rel {mr:.3g})"
+    print(f"multi-token call ({TD} tokens per request): parity ok", flush=True)
     sys.stdout.flush()
