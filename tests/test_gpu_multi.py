@@ -327,3 +327,26 @@ def test_prefill_chunk_max_tokens():
                                     a["v_cache"], a["page_table"][0], Lt, 4, x.scale)
         check_request(g, t, ref, Lt, what=f"chunk_max t{t}")
     _check_scores_and_selection(g, qi, a, 0, L, T, range(0, T, 31))
+
+
+def test_most_virtual_requests():
+    """The most virtual requests the multi-token entry points take, B*T = 65,535 (17 requests
+    of 3,855 new tokens, so grid dimensions and per-request offsets are at their limit). New
+    token t of request b sees 6 + 13b + t tokens: early tokens keep every block, later ones
+    select 512 of up to 1,017. Sampled tokens of three requests (the dense boundary among them)
+    against the oracle in full; every 61st token's scores and selection of the last request."""
+    B, T = 17, 3855
+    lens = tuple(T + 5 + 13 * b for b in range(B))
+    x = make_inputs(Workload("bt_max", B, ("list",) + lens, 8, 1, 2), 58, "cuda")
+    q, qi = draft_queries(x, T, 58)
+    say(f"[B*T = {B * T}] lens {lens[0]}..{lens[-1]}")
+    plan, g = _run(x, q, qi, 2)
+    a = oracle_arrays(x)
+    for b in (0, 8, 16):
+        tb = 2042 - 13 * b                      # sees exactly 2,048 tokens
+        for t in (0, 1, tb, tb + 1, T - 2, T - 1):
+            Lt = oracle.draft_length(lens[b], T, t)
+            ref = oracle.decode_request(bf16_bits(q[b, t]), qi[b, t].cpu().numpy(), a["idx_cache"], a["k_cache"],
+                                        a["v_cache"], a["page_table"][b], Lt, 2, x.scale)
+            check_request(g, b * T + t, ref, Lt, what=f"bt_max b{b} t{t}")
+    _check_scores_and_selection(g, qi, a, 16, lens[16], T, range(0, T, 61))
