@@ -6,6 +6,7 @@ absolute error of 2e-3 and a maximum relative error of 1e-2 (over |oracle| >= 1e
 Small batches and the full-size workloads are checked request by request against the
 oracle.
 """
+import dataclasses
 import math
 import random
 import sys
@@ -16,7 +17,8 @@ import torch
 
 import oracle
 from sparse_attention_decode_qsa_amd import qsa
-from sparse_attention_decode_qsa_amd.inputs import PAGE_SIZE, WORKLOADS, Workload, draft_queries, make_inputs
+from sparse_attention_decode_qsa_amd.inputs import (PAGE_SIZE, WORKLOADS, Workload, draft_queries, make_inputs,
+                                                    request_subset)
 from tests.helpers import ATOL, RTOL, oracle_decode, tolerance_report
 
 pytestmark = pytest.mark.gpu
@@ -351,6 +353,36 @@ def _full(name):
     say(f"[{name}] all {x.batch} requests match; out max abs err {worst_abs:.3g}, max rel err {worst_rel:.3g}; "
         f"oracle {time.time() - t0:.1f} s")
     return x, g
+
+
+def test_most_requests():
+    """The most requests qsa_decode takes, B = 65,535 (the selection's grid width and the other
+    kernels' grid heights at that count), of 0 to 129 tokens each, so every block is kept:
+    every request's count, ids and finiteness; about 250 sampled requests, empty ones and the
+    last ones among them, against the oracle in full."""
+    B = 65535
+    rng = np.random.default_rng(5)
+    lens = tuple(int(v) for v in rng.integers(0, 130, B))
+    c = make_inputs(W("b_max", lens, 8, 1, 2), 59, "cpu")   # drawn on the host, then copied
+    x = dataclasses.replace(c, **{f: getattr(c, f).cuda() for f in
+                                  ("q", "q_idx", "idx_cache", "k_cache", "v_cache", "page_table", "context_lens")})
+    say(f"[b_max] {B} requests of 0..129 tokens")
+    plan = qsa.DecodePlan(x.q, x.q_idx, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, 2)
+    plan.run()
+    torch.cuda.synchronize()
+    g = dict(scores=plan.scores.cpu().numpy(), sel=plan.sel.cpu().numpy(), cnt=plan.sel_count.cpu().numpy(),
+             po=plan.partial_out.cpu().numpy(), pl=plan.partial_lse.cpu().numpy(), out=plan.out.cpu().numpy(),
+             lse=plan.out_lse.cpu().numpy())
+    check_properties(x, g)
+    for b, L in enumerate(lens):                 # every block kept, in order
+        n = (L + 3) // 4
+        assert np.array_equal(g["sel"][b, :n], np.arange(n)), f"request {b}"
+    empties = [b for b, L in enumerate(lens) if L == 0][:3]
+    rows = sorted(set(rng.choice(B, 250, replace=False).tolist() + empties + [0, B - 2, B - 1]))
+    refs = oracle_decode(oracle, request_subset(c, rows))
+    for i, b in enumerate(rows):
+        check_request({key: v[b:b + 1] for key, v in g.items()}, 0, refs[i], lens[b], what=f"b_max {b}")
+    say(f"[b_max] {len(rows)} sampled requests match")
 
 
 def test_full_w2_planted_selection_everywhere():
