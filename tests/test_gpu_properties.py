@@ -11,7 +11,8 @@ request's last page hold poison (NaN K/V, indexer keys 127) that must not reach 
 Multi-token decode: up to 3 requests, T from 1 to 8 or 16 to 40 new tokens, independent or
 correlated indexer queries. Wider shapes: up to 6
 requests of up to 80,000 tokens, group sizes 16, 3 and 1, up to 64 slices, k below 512 and
-page tables with spare capacity.
+page tables with spare capacity. Side cache: the fused decode step (cache writes in the
+scan) and draft tokens scored from the side cache, up to 4 requests of up to 20,000 tokens.
 """
 import numpy as np
 import pytest
@@ -24,6 +25,8 @@ from sparse_attention_decode_qsa_amd import qsa
 from sparse_attention_decode_qsa_amd.inputs import Workload, bf16_bits, draft_queries, make_inputs
 from tests.helpers import oracle_arrays, oracle_decode
 from tests.test_gpu_multi import _run as run_multi
+from tests.test_gpu_side_cache import _stripped as stripped_caches
+from tests.test_gpu_side_cache import _valid_entries as side_entries
 from tests.test_gpu_parity import check_request, run_chain, say
 
 pytestmark = pytest.mark.gpu
@@ -98,3 +101,66 @@ def test_chain_matches_oracle_on_wider_shapes(lens, gqa, P, k, alphabet, extra_p
     refs = oracle_decode(oracle, x, P=P, k=k)
     for b, r in enumerate(refs):
         check_request(g, b, r, x.lengths[b], k, what="prop wide")
+
+
+@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(lens=st.lists(st.one_of(st.integers(0, 300), st.integers(0, 20000)), min_size=1, max_size=4),
+       gqa=st.sampled_from(GQA), P=st.integers(1, 8), alphabet=st.sampled_from(ALPHABETS),
+       seed=st.integers(0, 2**16))
+def test_side_cache_step_matches_oracle_on_random_shapes(lens, gqa, P, alphabet, seed):
+    """The decode step over the side cache (qsa_decode_step_pooled: the new token's K, V and
+    indexer rows and its block's side-cache entry written inside the scan, then selection,
+    attention and merge) on caches one token short of the generator's: the caches it leaves are
+    the generator's bit for bit, every side-cache entry is the oracle's pooled key, and every
+    request's results are the oracle's decode at full length."""
+    hq, hkv = gqa
+    w = Workload("props", len(lens), ("list",) + tuple(lens), hq, hkv, P, alphabet=alphabet)
+    x = make_inputs(w, seed, "cuda")
+    say(f"[prop side step] lens={lens} Hq/Hkv={hq}/{hkv} P={P} alphabet={alphabet} seed={seed}")
+    k, v, idx, side, k_new, v_new, i_new = stripped_caches(x, seed)
+    plan = qsa.StepPlan(k_new, v_new, i_new, x.q, x.q_idx, idx, k, v, x.page_table, x.context_lens, side, P)
+    plan.run()
+    torch.cuda.synchronize()
+    assert torch.equal(k.view(torch.int16), x.k_cache.view(torch.int16))
+    assert torch.equal(v.view(torch.int16), x.v_cache.view(torch.int16))
+    assert torch.equal(idx, x.idx_cache)
+    a = oracle_arrays(x)
+    got, want = side_entries(side.cpu().numpy(), a)
+    assert np.array_equal(got, want)
+    g = dict(scores=plan.scores.cpu().numpy(), sel=plan.sel.cpu().numpy(), cnt=plan.sel_count.cpu().numpy(),
+             po=plan.partial_out.cpu().numpy(), pl=plan.partial_lse.cpu().numpy(), out=plan.out.cpu().numpy(),
+             lse=plan.out_lse.cpu().numpy())
+    refs = oracle_decode(oracle, x, P=P)
+    for b, r in enumerate(refs):
+        check_request(g, b, r, x.lengths[b], what="prop side step")
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(lens=st.lists(st.one_of(st.integers(0, 300), st.integers(0, 20000)), min_size=1, max_size=4),
+       T=st.integers(2, 4), gqa=st.sampled_from(GQA), P=st.integers(1, 4), alphabet=st.sampled_from(ALPHABETS),
+       seed=st.integers(0, 2**16))
+def test_side_cache_drafts_match_oracle_on_random_shapes(lens, T, gqa, P, alphabet, seed):
+    """Draft tokens scored from the side cache (qsa_decode_multi_pooled; the pages holding
+    draft positions from the int8 rows): every (request, draft token) against the oracle."""
+    hq, hkv = gqa
+    w = Workload("propd", len(lens), ("list",) + tuple(lens), hq, hkv, P, alphabet=alphabet)
+    x = make_inputs(w, seed, "cuda")
+    q, qi = draft_queries(x, T, seed)
+    say(f"[prop side drafts] lens={lens} T={T} Hq/Hkv={hq}/{hkv} P={P} alphabet={alphabet} seed={seed}")
+    side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens)
+    plan = qsa.MultiDecodePlan(q, qi, x.idx_cache, x.k_cache, x.v_cache, x.page_table, x.context_lens, P,
+                               pooled=side)
+    plan.run()
+    torch.cuda.synchronize()
+    g = dict(scores=plan.scores.cpu().numpy(), sel=plan.sel.cpu().numpy(), cnt=plan.sel_count.cpu().numpy(),
+             po=plan.partial_out.cpu().numpy(), pl=plan.partial_lse.cpu().numpy(), out=plan.out.cpu().numpy(),
+             lse=plan.out_lse.cpu().numpy())
+    a = oracle_arrays(x)
+    refs = oracle.decode_multi(bf16_bits(q), qi.cpu().numpy(), a["idx_cache"], a["k_cache"], a["v_cache"],
+                               a["page_table"], a["lengths"], T, P, x.scale)
+    for b, L in enumerate(lens):
+        for t in range(T):
+            r = b * T + t
+            check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"prop side T{T} b{b} t{t}")
