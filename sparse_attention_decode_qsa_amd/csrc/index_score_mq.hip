@@ -38,13 +38,32 @@ namespace qsa {
 // run instead of 16 separate 4-byte stores, which took nearly as long as the 755 MB of
 // scores at T = 1024 on the 256K workload). On pages every query sees whole, a wave's four token tiles
 // run as independent MFMA chains with no masking.
+//
+// From 5 to 64 queries the score rows go out as nontemporal stores: the selection reads them
+// only on its candidate pages, and kept out of L2 and the MALL they leave that room to the
+// attention's K/V rows (whole calls at the 256K workload: 8 queries 81.8 -> 80.9 us, 16
+// queries 111.8 -> 108.0 us, 32 queries 162.2 -> 157.0 us, 64 queries 245.9 -> 240.5 us).
+// With 2 to 4 draft queries they made the scan and the call slower (four queries 67.3 ->
+// 69.0 us per call). Above 64 queries the effect changed sign from one GPU to the next (1,024
+// correlated queries: -10 to +50 us per call of about 900 us; under a kernel trace the
+// selection gained 19 us and the attention lost 7 us), so the 16-wave form stores plainly too.
 hipError_t launch_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
                               const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                               int32_t* page_max, int T, hipStream_t stream);   // index_score.hip
 void take_scan_events(hipEvent_t* start, hipEvent_t* stop);                   // index_score.hip
 constexpr long long kMqMinPages = 4096;   // batches from this many pages take the MFMA scan from T = 2
+constexpr int kMaxDraftQueries = 4;   // up to here score rows are stored plainly (see store_scores)
 constexpr int kQueryChunk = 64;    // queries staged in LDS at a time (17 KiB with padding)
 constexpr int kQStride = kIdxTokenBytes / 16 + 1;   // 16-byte vectors per staged query
+
+// One lane's 16-byte run of four block scores. NTS: a nontemporal store, so the score rows
+// of a chunk (which the selection reads only on its candidate pages) do not take L2 and MALL
+// space from the attention's K/V rows.
+template <bool NTS>
+__device__ __forceinline__ void store_scores(int32_t* dst, i32x4 v) {
+  if constexpr (NTS) __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(dst));
+  else *reinterpret_cast<i32x4*>(dst) = v;
+}
 
 // Scores of the page held in key (A layout, see above) for the nq queries of the chunk in
 // s_q, 16 queries per step. FULL: every query sees all 64 tokens of the page, so no token or
@@ -52,7 +71,7 @@ constexpr int kQStride = kIdxTokenBytes / 16 + 1;   // 16-byte vectors per stage
 // maxima: STAGE folds each query's into pm_slot (this wave's column of the chunk's LDS words,
 // row stride WAVES); otherwise the lanes of a query combine theirs and one writes it to
 // page_max.
-template <int WAVES, bool STAGE, bool FULL>
+template <int WAVES, bool STAGE, bool FULL, bool NTS>
 __device__ __forceinline__ void score_query_tiles(const i32x4 (&key)[4][4], const i32x4* s_q, int m0, int nq,
                                                   int T, int L0, int p, int i16, int g4, int b, int max_blocks,
                                                   int max_pages, int32_t* __restrict__ scores, int* pm_slot,
@@ -77,7 +96,7 @@ __device__ __forceinline__ void score_query_tiles(const i32x4 (&key)[4][4], cons
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) sc[tt] = (acc[tt][0] + acc[tt][1]) + (acc[tt][2] + acc[tt][3]);
       pmax = max(max(sc[0], sc[1]), max(sc[2], sc[3]));
-      if (m < T) *reinterpret_cast<i32x4*>(row + blk0) = i32x4{sc[0], sc[1], sc[2], sc[3]};
+      if (m < T) store_scores<NTS>(row + blk0, i32x4{sc[0], sc[1], sc[2], sc[3]});
     } else {
       const int Lm = L0 + m;
       const int nblk = m < T && Lm > 0 ? (Lm + kTokensPerBlock - 1) / kTokensPerBlock : 0;
@@ -90,7 +109,7 @@ __device__ __forceinline__ void score_query_tiles(const i32x4 (&key)[4][4], cons
         if (blk0 + tt < nblk) pmax = max(pmax, sc[tt]);
       }
       if (blk0 + 3 < nblk) {
-        *reinterpret_cast<i32x4*>(row + blk0) = i32x4{sc[0], sc[1], sc[2], sc[3]};
+        store_scores<NTS>(row + blk0, i32x4{sc[0], sc[1], sc[2], sc[3]});
       } else {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
@@ -107,7 +126,7 @@ __device__ __forceinline__ void score_query_tiles(const i32x4 (&key)[4][4], cons
   }
 }
 
-template <int WAVES, bool STAGE>
+template <int WAVES, bool STAGE, bool NTS>
 __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 waves per SIMD
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ idx_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ lens, int max_pages,
@@ -226,10 +245,10 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
       if (page_max) pm_slot = &s_pm[(m0 / kQueryChunk) & 1][wave];
     }
     if (full)
-      score_query_tiles<WAVES, STAGE, true>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
+      score_query_tiles<WAVES, STAGE, true, NTS>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
                                             pm_slot, page_max);
     else
-      score_query_tiles<WAVES, STAGE, false>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
+      score_query_tiles<WAVES, STAGE, false, NTS>(key, s_q, m0, nq, T, L0, p, i16, g4, b, max_blocks, max_pages, scores,
                                              pm_slot, page_max);
   }
   if constexpr (STAGE) {
@@ -242,16 +261,16 @@ __global__ __launch_bounds__(WAVES * 64, 4) void index_score_mq_kernel(   // 4 w
 }
 
 namespace {
-template <int W, bool STAGE>
+template <int W, bool STAGE, bool NTS>
 void launch_mq_w(hipStream_t stream, hipEvent_t e0, hipEvent_t e1, const int8_t* q_idx, const int8_t* idx_cache,
                  const int32_t* page_table, const int32_t* lens, int B, int max_pages, int max_blocks, int T,
                  int32_t* scores, int32_t* page_max) {
   const dim3 grid((unsigned)((max_pages + W - 1) / W), B);
   if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL((index_score_mq_kernel<W, STAGE>), grid, dim3(W * 64), 0, stream, e0, e1, 0, q_idx,
+    hipExtLaunchKernelGGL((index_score_mq_kernel<W, STAGE, NTS>), grid, dim3(W * 64), 0, stream, e0, e1, 0, q_idx,
                           idx_cache, page_table, lens, max_pages, max_blocks, T, scores, page_max);
   else
-    hipLaunchKernelGGL((index_score_mq_kernel<W, STAGE>), grid, dim3(W * 64), 0, stream, q_idx, idx_cache,
+    hipLaunchKernelGGL((index_score_mq_kernel<W, STAGE, NTS>), grid, dim3(W * 64), 0, stream, q_idx, idx_cache,
                        page_table, lens, max_pages, max_blocks, T, scores, page_max);
 }
 }  // namespace
@@ -261,12 +280,15 @@ hipError_t launch_index_score_mq(const int8_t* q_idx, const int8_t* idx_cache, c
                                  const int32_t* lens, int B, int max_pages, int max_blocks, int32_t* scores,
                                  int32_t* page_max, int T, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (T < 1 || T > kMaxQueries) return hipErrorInvalidValue;
-  if (T <= kQueryChunk)
-    launch_mq_w<8, false>(stream, start, stop, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, T,
-                          scores, page_max);
+  if (T <= kMaxDraftQueries)
+    launch_mq_w<8, false, false>(stream, start, stop, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks,
+                                 T, scores, page_max);
+  else if (T <= kQueryChunk)
+    launch_mq_w<8, false, true>(stream, start, stop, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks,
+                                T, scores, page_max);
   else
-    launch_mq_w<16, true>(stream, start, stop, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks, T,
-                          scores, page_max);
+    launch_mq_w<16, true, false>(stream, start, stop, q_idx, idx_cache, page_table, lens, B, max_pages, max_blocks,
+                                 T, scores, page_max);
   return hipGetLastError();
 }
 

@@ -133,7 +133,7 @@ qsa_status_t qsa_time_next_scan(void* start_event, void* stop_event) {
   return QSA_OK;
 }
 
-int qsa_version(void) { return 220; }   // 0.2.2: the MFMA scan for 2-4 draft tokens on large batches
+int qsa_version(void) { return 230; }   // 0.2.3: nontemporal score stores in chunks of 5-64 new tokens
 
 qsa_status_t qsa_index_score(const int8_t* q_idx, const int8_t* idx_cache, const int32_t* page_table,
                              const int32_t* context_lens, int B, int n_idx_heads, int idx_dim,
