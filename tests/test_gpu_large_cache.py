@@ -1,8 +1,8 @@
 """Caches above 2^31 elements.
 
 The requests' pages are placed at the top of indexer and K/V caches of more than 2^31
-elements each (the K and V caches hold 4.3 GB of bf16 apiece), so every K/V address the
-kernels form lies past element 2^31 and every page id is above 65,535. The pages below are
+elements each (the K and V caches hold 4.5 GB of bf16 apiece), so every K/V address the
+kernels form lies past element 2^31 and every page id is at least 65,600. The pages below are
 filled with NaN (K/V) and the largest indexer value, so a read of a page the request does not
 own would show in the scores, the selection or the outputs. The results are compared with the
 oracle run on the same requests held in a compact cache.
@@ -97,3 +97,32 @@ def test_multi_token_on_caches_above_2g_elements(lifted, T):
             r = b * T + t
             check_request(g, r, refs[r], oracle.draft_length(L, T, t), what=f"large cache T{T} b{b} t{t}")
     say(f"[large cache T={T}] every (request, token) matches the oracle")
+
+
+def test_side_cache_step_on_caches_above_2g_elements(lifted):
+    """The side-cache decode step (qsa_decode_step_pooled) on the lifted caches: each request's
+    last row removed and the side cache built one token short, then the step writes the row
+    back (main and side cache, past element 2^31) and decodes over the pooled keys. The caches
+    must come back bit for bit and every request must match the oracle."""
+    from tests.test_gpu_side_cache import _stripped
+    c, x = lifted
+    k, v, idx, side, k_new, v_new, i_new = _stripped(x, seed=7)
+    step = qsa.StepPlan(k_new, v_new, i_new, x.q, x.q_idx, idx, k, v, x.page_table, x.context_lens, side, 4)
+    step.run()
+    full_side = qsa.pool_build(x.idx_cache, x.page_table, x.context_lens)
+    torch.cuda.synchronize()
+    for name, u, w in (("k", k, x.k_cache), ("v", v, x.v_cache), ("idx", idx, x.idx_cache)):
+        assert torch.equal(u.view(torch.int8), w.view(torch.int8)), name
+    pt = x.page_table.cpu().numpy()
+    for b, L in enumerate(LENS):                 # the side cache of every page of every request
+        for p in range((L + PAGE_SIZE - 1) // PAGE_SIZE):
+            nb = min(PAGE_SIZE, L - p * PAGE_SIZE + 3) // 4
+            pg = int(pt[b][p])
+            assert torch.equal(side[pg, :nb], full_side[pg, :nb]), (b, p)
+    g = dict(scores=step.scores.cpu().numpy(), sel=step.sel.cpu().numpy(), cnt=step.sel_count.cpu().numpy(),
+             po=step.partial_out.cpu().numpy(), pl=step.partial_lse.cpu().numpy(), out=step.out.cpu().numpy(),
+             lse=step.out_lse.cpu().numpy())
+    refs = oracle_decode(oracle, c)
+    for b, r in enumerate(refs):
+        check_request(g, b, r, LENS[b], what="large cache side-cache step")
+    say("[large cache] side-cache step: caches restored, every request matches the oracle")
