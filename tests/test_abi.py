@@ -312,3 +312,14 @@ def test_decode_noalloc_host_checks():
     # the w4 and 128-request shapes fit
     assert L.qsa_decode_workspace_size(4, 32, 4, 65536, 512, 4) <= qsa.NOALLOC_SCRATCH_BYTES
     assert L.qsa_decode_workspace_size(128, 32, 4, 65536, 512, 4) <= qsa.NOALLOC_SCRATCH_BYTES
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises: there is no fallback path."""
+    from sparse_attention_decode_qsa_amd import qsa
+    monkeypatch.setattr(qsa, "LIB_PATH", str(tmp_path / "libqsa.so"))
+    monkeypatch.setattr(qsa, "_lib", None)
+    with pytest.raises(ImportError, match="missing"):
+        qsa.lib()
+    with pytest.raises(ImportError):
+        qsa.decode_workspace_size(4, 32, 4, 65536, 512, 4)
