@@ -76,10 +76,11 @@ def test_decode_on_caches_above_2g_elements(lifted):
     say(f"[large cache] qsa_decode and the four calls match the oracle on all {len(LENS)} requests")
 
 
-@pytest.mark.parametrize("T", [4, 16])
+@pytest.mark.parametrize("T", [4, 16, 65])
 def test_multi_token_on_caches_above_2g_elements(lifted, T):
-    """Draft tokens (T = 4, dot-product or MFMA scan) and a prefill chunk (T = 16, the MFMA scan
-    and the pair attention kernel) on the lifted caches."""
+    """Draft tokens (T = 4, dot-product or MFMA scan) and prefill chunks (T = 16: the MFMA scan
+    and the pair attention kernel; T = 65: the scan's form for more than 64 queries) on the
+    lifted caches."""
     c, x = lifted
     q, qi = draft_queries(c, T, 71 + T)
     plan = qsa.MultiDecodePlan(q.cuda(), qi.cuda(), x.idx_cache, x.k_cache, x.v_cache, x.page_table,
